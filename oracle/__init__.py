@@ -1,0 +1,14 @@
+"""Plain float64 CPU oracle of the speculative-sampling verifier.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the benchmark's CPU-baseline leg, never by the
+HIP library or its binding. It shares no code with them.
+"""
+from .verify import (FLAG_EMPTY_RESIDUAL, FLAG_ID_RANGE, FLAG_NONFINITE, FLAG_Q_ZERO, FATAL, accept_test,
+                     accept_test_exact, inverse_cdf,
+                     log_softmax_at, residual, softmax, verify_dense, verify_onehot, verify_sparse, verify_windows,
+                     widen)
+
+__all__ = ["FLAG_EMPTY_RESIDUAL", "FLAG_ID_RANGE", "FLAG_NONFINITE", "FLAG_Q_ZERO", "FATAL", "accept_test",
+           "accept_test_exact",
+           "inverse_cdf", "log_softmax_at", "residual", "softmax", "verify_dense", "verify_onehot", "verify_sparse",
+           "verify_windows", "widen"]
