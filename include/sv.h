@@ -1,0 +1,178 @@
+/*
+ * sv.h -- C ABI of the batched speculative-sampling verifier for AMD Instinct MI355X (gfx950).
+ *
+ * The rule (Leviathan et al., as restated on the page "Uno: the draft model was already inside the target model",
+ * section "What 'lossless' actually has to mean"): a drafted token x, proposed from q, is accepted when a uniform
+ * u satisfies u < min(1, p(x)/q(x)); the block is cut at the first rejection (DFlash/DFlash2 guide, section 4.4),
+ * where one replacement token is drawn from max(p - q, 0) renormalised; when every draft is accepted, one bonus
+ * token is drawn from the target's next distribution (same guide, section 2: tokens per cycle in [1, gamma + 1]).
+ * Dense calls form p = softmax(z_target / T) and q = softmax(z_draft / T) (same guide, section 9 Q3: temperature on
+ * both sides before the ratio).
+ *
+ * Conventions shared by every entry point
+ * - Every array argument is a DEVICE pointer owned by the caller. The library allocates nothing, keeps no state
+ *   between calls and may be called from several host threads on different streams.
+ * - Work is enqueued on `stream` (a hipStream_t, or NULL for the null stream) of the current device; outputs are
+ *   valid once that stream has reached the enqueued work. No call synchronises the host.
+ * - The return value is 0 (SV_OK) or a negative SV_ERR_* code. Argument errors are detected on the host BEFORE any
+ *   HIP call, so nothing has been enqueued when one is returned. SV_ERR_HIP means a launch failed.
+ * - Data faults inside the tensors do not fail the call; they are reported per sequence in `flags` (SV_FLAG_*).
+ *   A sequence with SV_FLAG_NONFINITE or SV_FLAG_ID_RANGE is not verified: n_accepted = -1, out_token = -1,
+ *   accept = 0 for all its rows, p_draft / q_draft (or p_spec / q_spec / correction_probs) = NaN.
+ * - The index of a draw is the smallest i whose inclusive running sum of the draw's weights exceeds t = u * (total
+ *   weight), in vocabulary order (dense) or in the given support-slot order (sparse); if rounding leaves no such i,
+ *   the last index with positive weight is taken. An empty residual (zero total) draws from p instead and sets
+ *   SV_FLAG_EMPTY_RESIDUAL.
+ * - The accept test is strict (u == min(1, ratio) rejects), as in the engine routine printed on the Uno page.
+ */
+#ifndef SV_H
+#define SV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------------------------------------------- */
+#define SV_OK             0
+#define SV_ERR_NULL      (-1)   /* a required pointer is NULL                                                     */
+#define SV_ERR_SHAPE     (-2)   /* B, gamma, V, k or a stride out of range, or a size product overflows          */
+#define SV_ERR_DTYPE     (-3)   /* dtype is not SV_F32 or SV_BF16                                                 */
+#define SV_ERR_TEMP      (-4)   /* temperature is not finite or is <= 0                                           */
+#define SV_ERR_ALIGN     (-5)   /* a pointer is not aligned to its element size (workspace: to 256 bytes)        */
+#define SV_ERR_WORKSPACE (-6)   /* workspace smaller than sv_workspace_bytes() or NULL while bytes are needed     */
+#define SV_ERR_HIP       (-7)   /* a kernel launch failed                                                         */
+#define SV_ERR_ARG       (-8)   /* any other invalid argument (bonus not 0/1, unknown kind)                       */
+
+/* ---- logit element types ------------------------------------------------------------------------------------ */
+#define SV_F32  0
+#define SV_BF16 1
+
+/* ---- workspace kinds ---------------------------------------------------------------------------------------- */
+#define SV_KIND_DENSE  0
+#define SV_KIND_ONEHOT 1
+#define SV_KIND_SPARSE 2
+
+/* ---- per-sequence flags ------------------------------------------------------------------------------------- */
+#define SV_FLAG_NONFINITE      1u  /* NaN or +inf logit (or a row all -inf) in a row that was read; for sparse, a
+                                      NaN, infinite or negative probability. Fatal for the sequence, except in the
+                                      bonus row, where it only voids the bonus token (out_token = -1).           */
+#define SV_FLAG_ID_RANGE       2u  /* a draft / spec id outside [0, V) (sparse: outside [0, vocab_size) when given,
+                                      for spec and support ids), `order` not a permutation of [0, gamma), or
+                                      start outside [0, gamma]. Fatal for the sequence.                          */
+#define SV_FLAG_EMPTY_RESIDUAL 4u  /* the residual had zero mass and the draw used p instead. Informational.      */
+#define SV_FLAG_Q_ZERO         8u  /* q was exactly 0 at a verified draft (ratio 0, rejected). Informational.     */
+
+/* ---- limits ------------------------------------------------------------------------------------------------- */
+#define SV_MAX_GAMMA 1024        /* drafted positions per sequence                                                */
+#define SV_MAX_K     256         /* support size of a sparse row (kp, kq)                                          */
+
+/*
+ * Bytes of device workspace a call of `kind` needs for B sequences of gamma drafts over V_or_k (V for dense and
+ * one-hot, the p-support size kp for sparse). Depends only on these arguments. Returns 0 when no workspace is
+ * needed and (size_t)-1 for arguments the calls would reject. The workspace is scratch: its contents need not be
+ * initialised and are meaningless afterwards; it must not be shared by calls that may run concurrently.
+ */
+size_t sv_workspace_bytes(int kind, int64_t B, int32_t gamma, int64_t V_or_k);
+
+/* Static text for a status code. */
+const char* sv_status_string(int status);
+
+/*
+ * Profiling hook (no counterpart on the pages; it lets a caller time the HBM-bound pass on its own). When both
+ * events are non-NULL, the next sv_verify_dense or sv_verify_onehot_draft call made on this host thread records
+ * `start_event` just before its row-statistics kernel and `stop_event` just after it, on that call's stream, and
+ * then forgets them; hipEventElapsedTime(start, stop) is that kernel's duration. The events (hipEvent_t) are created
+ * and owned by the caller. Passing two NULLs clears a pending request. Returns SV_OK, or SV_ERR_NULL when exactly
+ * one event is NULL. The request is per host thread, so concurrent callers on other threads are unaffected.
+ */
+int sv_profile_next_stats(void* start_event, void* stop_event);
+
+/*
+ * Dense verification: p and q from full logit rows.
+ *
+ * target_logits  [B][gamma + bonus][V] of `dtype`; element (b, r, i) at target_logits[b*t_seq + r*t_row + i].
+ *                Row gamma is read only for a bonus draw. Rows of slots before `start` are not read.
+ * draft_logits   [B][gamma][V] of `dtype`, at draft_logits[b*d_seq + r*d_row + i].
+ * dtype          SV_F32 or SV_BF16 (both tensors). Pointers aligned to the element size; rows need no further
+ *                alignment (strides are in elements and must be >= 1; V is contiguous).
+ * B, gamma, V    1 <= B <= 2^31-1, 1 <= gamma <= SV_MAX_GAMMA, 1 <= V <= 2^31-1.
+ * draft_ids      [B][gamma] int32, the drafted token of each storage row.
+ * u_accept       [B][gamma] float uniforms in [0, 1) for the accept tests, by storage row.
+ * u_sample       [B][gamma + 1] float uniforms in [0, 1): a residual draw at slot k reads u_sample[b][order[k]],
+ *                the bonus draw reads u_sample[b][gamma].
+ * temperature    T > 0, finite: p = softmax(z_target / T), q = softmax(z_draft / T).
+ * bonus          1: draw a bonus token from target row gamma when every verified slot is accepted; 0: no bonus
+ *                (out_token = -1 then), and the target needs only gamma rows.
+ * start          [B] int32 or NULL (= all 0). Slots start[b] .. gamma-1 are verified. On return start[b] is set to
+ *                min(gamma, k + 1), k = the first rejected slot (gamma if none), so that consecutive calls chain
+ *                verification rounds over one window (Self-Speculative Masked Diffusions, 关键设计 2 and 4). A
+ *                sequence with start[b] == gamma is finished: nothing is read, n = 0, out_token = -1, start kept.
+ * order          [B][gamma] int32 or NULL (= identity): slot s verifies storage row order[b][s].
+ * accept         [B][gamma] uint8 or NULL: the raw test of every verified row (0 for rows before start).
+ * n_accepted     [B] int32 (required): accepted drafts from start up to the first rejection.
+ * out_token      [B] int32 (required): the residual or bonus token, or -1.
+ * p_draft/q_draft [B][gamma] float or NULL: p(x) and q(x) at each verified row (0 elsewhere).
+ * flags          [B] uint32 or NULL.
+ * workspace      >= sv_workspace_bytes(SV_KIND_DENSE, B, gamma, V) bytes of device memory, 256-byte aligned.
+ */
+int sv_verify_dense(const void* target_logits, int64_t t_seq, int64_t t_row,
+                    const void* draft_logits, int64_t d_seq, int64_t d_row,
+                    int dtype, int64_t B, int32_t gamma, int64_t V,
+                    const int32_t* draft_ids, const float* u_accept, const float* u_sample,
+                    float temperature, int32_t bonus,
+                    int32_t* start, const int32_t* order,
+                    uint8_t* accept, int32_t* n_accepted, int32_t* out_token,
+                    float* p_draft, float* q_draft, uint32_t* flags,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Greedy-draft verification (the last paragraph of the Uno page's section "What 'lossless' actually has to mean":
+ * a greedy drafter makes q one-hot, and the rule must be applied to that q): q = e_d at the draft id d, so the
+ * test is u < p(d) and the residual is p with d removed, renormalised. No draft logits exist and only target rows
+ * are read. Arguments as for sv_verify_dense without the draft tensor and q_draft.
+ * workspace >= sv_workspace_bytes(SV_KIND_ONEHOT, B, gamma, V).
+ */
+int sv_verify_onehot_draft(const void* target_logits, int64_t t_seq, int64_t t_row,
+                           int dtype, int64_t B, int32_t gamma, int64_t V,
+                           const int32_t* draft_ids, const float* u_accept, const float* u_sample,
+                           float temperature, int32_t bonus,
+                           int32_t* start, const int32_t* order,
+                           uint8_t* accept, int32_t* n_accepted, int32_t* out_token,
+                           float* p_draft, uint32_t* flags,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Sparse verification on top-k supports, following the engine routine printed on the Uno page (section "What
+ * 'lossless' actually has to mean"): p_spec and q_spec are the support probabilities whose id equals the drafted
+ * id (summed in slot order); accept iff q_spec > 0 and u < min(1, p_spec / q_spec), evaluated exactly as
+ * u * q_spec < p_spec in float64; the correction distribution on p's support is max(p_i - q_on_p_i, 0) renormalised,
+ * with q_on_p_i the q probability of p's i-th id. Probabilities are used as given (no renormalisation of p or q).
+ * All arithmetic is float64 in slot order, so every output equals the float64 evaluation of these definitions.
+ *
+ * p_ids, p_probs  [B][gamma + bonus][kp] int32 / float, contiguous (row gamma only read for a bonus draw).
+ * q_ids, q_probs  [B][gamma][kq] int32 / float, contiguous.
+ * kp, kq          1 .. SV_MAX_K.
+ * vocab_size      > 0: spec and support ids outside [0, vocab_size) flag SV_FLAG_ID_RANGE; 0: ids unchecked.
+ * spec_ids        [B][gamma] int32 drafted ids; u_accept [B][gamma]; u_sample [B][gamma + 1] (column k for a
+ *                 residual draw at slot k, column gamma for the bonus).
+ * accept          [B][gamma] uint8 or NULL; n_accepted, out_token [B] int32 (required).
+ * correction_probs [B][gamma][kp] float or NULL: the draw distribution of each row (p's fallback when empty).
+ * p_spec, q_spec  [B][gamma] float or NULL.  flags [B] uint32 or NULL.
+ * workspace       unused (sv_workspace_bytes returns 0); may be NULL.
+ */
+int sv_verify_sparse(const int32_t* p_ids, const float* p_probs,
+                     const int32_t* q_ids, const float* q_probs,
+                     int64_t B, int32_t gamma, int32_t kp, int32_t kq, int64_t vocab_size,
+                     const int32_t* spec_ids, const float* u_accept, const float* u_sample, int32_t bonus,
+                     uint8_t* accept, int32_t* n_accepted, int32_t* out_token,
+                     float* correction_probs, float* p_spec, float* q_spec, uint32_t* flags,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SV_H */

@@ -1,0 +1,188 @@
+// Exported C entry points of the verifier library: argument validation on the host (before any HIP call),
+// workspace sizing and launch sequencing. The kernels live in sv_dense.hip and sv_sparse.hip.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <limits>
+
+#include "sv.h"
+#include "sv_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxI32 = std::numeric_limits<int32_t>::max();
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Checks shared by the dense and one-hot calls. Returns SV_OK or an error code.
+int check_dense_common(const void* tgt, int64_t t_seq, int64_t t_row, int dtype, int64_t B, int32_t gamma, int64_t V,
+                       const int32_t* ids, const float* ua, const float* us, float temperature, int32_t bonus,
+                       int32_t* start, const int32_t* order, uint8_t* accept, int32_t* n_acc, int32_t* token,
+                       float* p_draft, uint32_t* flags) {
+  if (!tgt || !ids || !ua || !us || !n_acc || !token) return SV_ERR_NULL;
+  if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
+  if (B < 1 || B > kMaxI32 || gamma < 1 || gamma > SV_MAX_GAMMA || V < 1 || V > kMaxI32) return SV_ERR_SHAPE;
+  if (t_seq < 1 || t_row < 1) return SV_ERR_SHAPE;
+  if (bonus != 0 && bonus != 1) return SV_ERR_ARG;
+  if (!std::isfinite(temperature) || !(temperature > 0.f)) return SV_ERR_TEMP;
+  // the largest element offset must fit in int64 (and the per-sequence work in the grid)
+  const double last = double(B - 1) * double(t_seq) + double(gamma + bonus - 1) * double(t_row) + double(V);
+  if (last > 9.0e18) return SV_ERR_SHAPE;
+  const size_t es = dtype == SV_BF16 ? 2 : 4;
+  if (!aligned(tgt, es)) return SV_ERR_ALIGN;
+  if (!aligned(ids, 4) || !aligned(ua, 4) || !aligned(us, 4) || !aligned(n_acc, 4) || !aligned(token, 4) ||
+      (start && !aligned(start, 4)) || (order && !aligned(order, 4)) || (p_draft && !aligned(p_draft, 4)) ||
+      (flags && !aligned(flags, 4)))
+    return SV_ERR_ALIGN;
+  (void)accept;
+  return SV_OK;
+}
+
+// Grids of the plan must fit the launch limits.
+int check_grid(const sv::DensePlan& p) {
+  if (double(p.ntens) * double(p.B) * double(p.G) * double(p.nseg1) > double(kMaxI32)) return SV_ERR_SHAPE;
+  if (double(p.B) * double(p.nseg2) > double(kMaxI32)) return SV_ERR_SHAPE;
+  return SV_OK;
+}
+
+// Events for the next dense / one-hot call on this host thread (see sv_profile_next_stats).
+thread_local void* t_ev_start = nullptr;
+thread_local void* t_ev_stop = nullptr;
+
+void take_events(sv::DenseArgs& a) {
+  a.ev_start = t_ev_start;
+  a.ev_stop = t_ev_stop;
+  t_ev_start = t_ev_stop = nullptr;
+}
+
+int check_workspace(void* ws, size_t bytes, size_t need) {
+  if (need == 0) return SV_OK;
+  if (!ws) return SV_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return SV_ERR_ALIGN;
+  if (bytes < need) return SV_ERR_WORKSPACE;
+  return SV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sv_workspace_bytes(int kind, int64_t B, int32_t gamma, int64_t V_or_k) {
+  const size_t bad = static_cast<size_t>(-1);
+  if (B < 1 || B > kMaxI32 || gamma < 1 || gamma > SV_MAX_GAMMA || V_or_k < 1) return bad;
+  switch (kind) {
+    case SV_KIND_DENSE:
+    case SV_KIND_ONEHOT:
+      if (V_or_k > kMaxI32) return bad;
+      return sv::make_dense_plan(B, gamma, V_or_k, kind == SV_KIND_DENSE ? 2 : 1).total;
+    case SV_KIND_SPARSE:
+      if (V_or_k > SV_MAX_K) return bad;
+      return 0;
+    default:
+      return bad;
+  }
+}
+
+int sv_profile_next_stats(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr)) return SV_ERR_NULL;
+  t_ev_start = start_event;
+  t_ev_stop = stop_event;
+  return SV_OK;
+}
+
+const char* sv_status_string(int status) {
+  switch (status) {
+    case SV_OK: return "ok";
+    case SV_ERR_NULL: return "a required pointer is NULL";
+    case SV_ERR_SHAPE: return "shape or stride out of range";
+    case SV_ERR_DTYPE: return "unsupported dtype";
+    case SV_ERR_TEMP: return "temperature must be finite and > 0";
+    case SV_ERR_ALIGN: return "misaligned pointer";
+    case SV_ERR_WORKSPACE: return "workspace missing or too small";
+    case SV_ERR_HIP: return "HIP launch failed";
+    case SV_ERR_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+int sv_verify_dense(const void* target_logits, int64_t t_seq, int64_t t_row,
+                    const void* draft_logits, int64_t d_seq, int64_t d_row,
+                    int dtype, int64_t B, int32_t gamma, int64_t V,
+                    const int32_t* draft_ids, const float* u_accept, const float* u_sample,
+                    float temperature, int32_t bonus,
+                    int32_t* start, const int32_t* order,
+                    uint8_t* accept, int32_t* n_accepted, int32_t* out_token,
+                    float* p_draft, float* q_draft, uint32_t* flags,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dense_common(target_logits, t_seq, t_row, dtype, B, gamma, V, draft_ids, u_accept, u_sample,
+                              temperature, bonus, start, order, accept, n_accepted, out_token, p_draft, flags);
+  if (st != SV_OK) return st;
+  if (!draft_logits) return SV_ERR_NULL;
+  if (d_seq < 1 || d_row < 1) return SV_ERR_SHAPE;
+  if (double(B - 1) * double(d_seq) + double(gamma - 1) * double(d_row) + double(V) > 9.0e18) return SV_ERR_SHAPE;
+  if (!aligned(draft_logits, dtype == SV_BF16 ? 2 : 4)) return SV_ERR_ALIGN;
+  if (q_draft && !aligned(q_draft, 4)) return SV_ERR_ALIGN;
+  const sv::DensePlan plan = sv::make_dense_plan(B, gamma, V, 2);
+  st = check_grid(plan);
+  if (st != SV_OK) return st;
+  st = check_workspace(workspace, workspace_bytes, plan.total);
+  if (st != SV_OK) return st;
+
+  sv::DenseArgs a{target_logits, t_seq, t_row, draft_logits, d_seq, d_row, dtype, draft_ids, u_accept, u_sample,
+                  temperature, bonus, start, order, accept, n_accepted, out_token, p_draft, q_draft, flags,
+                  static_cast<char*>(workspace)};
+  take_events(a);
+  return sv::launch_dense(plan, a, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+int sv_verify_onehot_draft(const void* target_logits, int64_t t_seq, int64_t t_row,
+                           int dtype, int64_t B, int32_t gamma, int64_t V,
+                           const int32_t* draft_ids, const float* u_accept, const float* u_sample,
+                           float temperature, int32_t bonus,
+                           int32_t* start, const int32_t* order,
+                           uint8_t* accept, int32_t* n_accepted, int32_t* out_token,
+                           float* p_draft, uint32_t* flags,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dense_common(target_logits, t_seq, t_row, dtype, B, gamma, V, draft_ids, u_accept, u_sample,
+                              temperature, bonus, start, order, accept, n_accepted, out_token, p_draft, flags);
+  if (st != SV_OK) return st;
+  const sv::DensePlan plan = sv::make_dense_plan(B, gamma, V, 1);
+  st = check_grid(plan);
+  if (st != SV_OK) return st;
+  st = check_workspace(workspace, workspace_bytes, plan.total);
+  if (st != SV_OK) return st;
+  sv::DenseArgs a{target_logits, t_seq, t_row, nullptr, 0, 0, dtype, draft_ids, u_accept, u_sample,
+                  temperature, bonus, start, order, accept, n_accepted, out_token, p_draft, nullptr, flags,
+                  static_cast<char*>(workspace)};
+  take_events(a);
+  return sv::launch_dense(plan, a, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+int sv_verify_sparse(const int32_t* p_ids, const float* p_probs,
+                     const int32_t* q_ids, const float* q_probs,
+                     int64_t B, int32_t gamma, int32_t kp, int32_t kq, int64_t vocab_size,
+                     const int32_t* spec_ids, const float* u_accept, const float* u_sample, int32_t bonus,
+                     uint8_t* accept, int32_t* n_accepted, int32_t* out_token,
+                     float* correction_probs, float* p_spec, float* q_spec, uint32_t* flags,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!p_ids || !p_probs || !q_ids || !q_probs || !spec_ids || !u_accept || !u_sample || !n_accepted || !out_token)
+    return SV_ERR_NULL;
+  if (B < 1 || B > kMaxI32 || gamma < 1 || gamma > SV_MAX_GAMMA || kp < 1 || kp > SV_MAX_K || kq < 1 ||
+      kq > SV_MAX_K || vocab_size < 0 || vocab_size > kMaxI32)
+    return SV_ERR_SHAPE;
+  if (bonus != 0 && bonus != 1) return SV_ERR_ARG;
+  if (double(B) * double(gamma + 1) * double(kp > kq ? kp : kq) > 9.0e18) return SV_ERR_SHAPE;
+  const void* ptrs[] = {p_ids, p_probs, q_ids, q_probs, spec_ids, u_accept, u_sample, n_accepted, out_token,
+                        correction_probs, p_spec, q_spec, flags};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, 4)) return SV_ERR_ALIGN;
+  sv::SparseArgs a{p_ids, p_probs, q_ids, q_probs, B, gamma, kp, kq, vocab_size, spec_ids, u_accept, u_sample, bonus,
+                   accept, n_accepted, out_token, correction_probs, p_spec, q_spec, flags};
+  return sv::launch_sparse(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Internal declarations shared by the host entry points and the kernel launchers of the verifier library.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+namespace sv {
+
+// Kinds of draw a sequence needs after the accept/first-reject scan.
+enum JobKind : int32_t {
+  JOB_NONE = 0,      // nothing to draw (finished, fatal, or no bonus)
+  JOB_RESID = 1,     // residual max(p - q, 0) at a rejected row, q from draft logits
+  JOB_ONEHOT = 2,    // residual p with the draft id removed (q one-hot)
+  JOB_BONUS = 3,     // bonus draw from p of target row gamma
+};
+
+// One record per sequence, written by the scan kernel and read by the draw kernels.
+struct alignas(32) Job {
+  int32_t kind;      // JobKind
+  int32_t row;       // storage row of the draw (gamma for the bonus)
+  int32_t d;         // draft id at that row (one-hot residual)
+  int32_t pad0;
+  float u;           // the uniform of the draw
+  float m_t;         // exact max of the target row (from the statistics pass; unused for the bonus)
+  float m_d;         // exact max of the draft row
+  float pad1;
+};
+
+// Sizes and workspace layout of one dense / one-hot call. Depends only on (B, gamma, V, number of tensors).
+struct DensePlan {
+  int64_t B = 0;
+  int32_t G = 0;
+  int64_t V = 0;
+  int32_t ntens = 0;     // 2: target + draft; 1: target only (one-hot)
+  int32_t nseg1 = 1;     // segments per row in the statistics pass
+  int32_t nseg2 = 1;     // segments per row in the float64 draw passes
+  size_t off_part1 = 0;  // float2 (max, sum) per (tensor, b, row, seg1)
+  size_t off_jobs = 0;   // Job per b
+  size_t off_part2a = 0; // double4 (m_t, S_t, m_d, S_d) per (b, seg2)
+  size_t off_part2b = 0; // double2 (residual mass, p mass) per (b, seg2)
+  size_t total = 0;
+};
+
+DensePlan make_dense_plan(int64_t B, int32_t G, int64_t V, int32_t ntens);
+
+struct DenseArgs {
+  const void* tgt; int64_t t_seq, t_row;
+  const void* dft; int64_t d_seq, d_row;     // dft == nullptr: one-hot drafts
+  int dtype;
+  const int32_t* ids; const float* ua; const float* us;
+  float temperature; int32_t bonus;
+  int32_t* start; const int32_t* order;
+  uint8_t* accept; int32_t* n_acc; int32_t* token;
+  float* p_draft; float* q_draft; uint32_t* flags;
+  char* ws;
+  void* ev_start = nullptr;   // optional hipEvent_t recorded around the row-statistics kernel
+  void* ev_stop = nullptr;
+};
+
+hipError_t launch_dense(const DensePlan& plan, const DenseArgs& a, hipStream_t stream);
+
+struct SparseArgs {
+  const int32_t* p_ids; const float* p_probs;
+  const int32_t* q_ids; const float* q_probs;
+  int64_t B; int32_t G; int32_t kp; int32_t kq; int64_t vocab;
+  const int32_t* spec; const float* ua; const float* us; int32_t bonus;
+  uint8_t* accept; int32_t* n_acc; int32_t* token;
+  float* corr; float* p_spec; float* q_spec; uint32_t* flags;
+};
+
+hipError_t launch_sparse(const SparseArgs& a, hipStream_t stream);
+
+}  // namespace sv

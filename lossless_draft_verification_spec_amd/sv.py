@@ -1,0 +1,228 @@
+"""Python binding of the verifier's C ABI (``include/sv.h``), over ctypes.
+
+Argument marshalling only: tensors are checked for device, dtype and layout, outputs and the workspace are allocated
+with torch on the input's device, and the C entry point of the same name is called on the current torch stream.
+Every step of the verification runs in the HIP library; there is no fallback. Importing this module raises if the
+library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsv.so")
+
+SV_OK = 0
+SV_F32, SV_BF16 = 0, 1
+SV_KIND_DENSE, SV_KIND_ONEHOT, SV_KIND_SPARSE = 0, 1, 2
+SV_FLAG_NONFINITE, SV_FLAG_ID_RANGE, SV_FLAG_EMPTY_RESIDUAL, SV_FLAG_Q_ZERO = 1, 2, 4, 8
+SV_MAX_GAMMA, SV_MAX_K = 1024, 256
+
+EXPORTS = ("sv_workspace_bytes", "sv_status_string", "sv_profile_next_stats", "sv_verify_dense",
+           "sv_verify_onehot_draft", "sv_verify_sparse")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m lossless_draft_verification_spec_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I64, I32, SZ, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+    lib.sv_workspace_bytes.argtypes = [ctypes.c_int, I64, I32, I64]
+    lib.sv_workspace_bytes.restype = SZ
+    lib.sv_status_string.argtypes = [ctypes.c_int]
+    lib.sv_status_string.restype = ctypes.c_char_p
+    lib.sv_profile_next_stats.argtypes = [P, P]
+    lib.sv_profile_next_stats.restype = ctypes.c_int
+    lib.sv_verify_dense.argtypes = [P, I64, I64, P, I64, I64, ctypes.c_int, I64, I32, I64, P, P, P, F, I32, P, P,
+                                    P, P, P, P, P, P, P, SZ, P]
+    lib.sv_verify_dense.restype = ctypes.c_int
+    lib.sv_verify_onehot_draft.argtypes = [P, I64, I64, ctypes.c_int, I64, I32, I64, P, P, P, F, I32, P, P,
+                                           P, P, P, P, P, P, SZ, P]
+    lib.sv_verify_onehot_draft.restype = ctypes.c_int
+    lib.sv_verify_sparse.argtypes = [P, P, P, P, I64, I32, I32, I32, I64, P, P, P, I32, P, P, P, P, P, P, P, P, SZ, P]
+    lib.sv_verify_sparse.restype = ctypes.c_int
+    return lib
+
+
+LIB = _load()
+
+
+class SVError(RuntimeError):
+    def __init__(self, status: int):
+        super().__init__(f"sv status {status}: {sv_status_string(status)}")
+        self.status = status
+
+
+def sv_workspace_bytes(kind: int, B: int, gamma: int, V_or_k: int) -> int:
+    return int(LIB.sv_workspace_bytes(kind, B, gamma, V_or_k))
+
+
+def sv_status_string(status: int) -> str:
+    return LIB.sv_status_string(status).decode()
+
+
+def sv_profile_next_stats(start_event, stop_event) -> None:
+    """Time the next dense / one-hot call's row-statistics kernel with two caller-owned hipEvent_t handles."""
+    st = LIB.sv_profile_next_stats(start_event, stop_event)
+    if st != SV_OK:
+        raise SVError(st)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, dtype, shape, device):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _logits_layout(t, name, rows, B, device):
+    if t.device != device or t.dim() != 3 or t.shape[0] != B or t.shape[1] < rows:
+        raise ValueError(f"{name}: expected a [B={B}, >={rows}, V] tensor on {device}")
+    if t.stride(2) != 1 and t.shape[2] > 1:
+        raise ValueError(f"{name}: the vocabulary axis must be contiguous")
+    # a size-1 axis may carry any stride (numpy's newaxis gives 0); it is never stepped, so pass 1
+    seq = t.stride(0) if t.shape[0] > 1 else 1
+    row = t.stride(1) if t.shape[1] > 1 else 1
+    return seq, row
+
+
+def workspace(kind: int, B: int, gamma: int, V_or_k: int, device) -> torch.Tensor | None:
+    n = sv_workspace_bytes(kind, B, gamma, V_or_k)
+    if n == (1 << 64) - 1:
+        raise SVError(-2)
+    if n == 0:
+        return None
+    ws = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    return ws[off:off + n]
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return SV_F32
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _outputs(B, G, device, out, names):
+    out = {} if out is None else out
+    spec = {"accept": ((B, G), torch.uint8), "n_accepted": ((B,), torch.int32), "out_token": ((B,), torch.int32),
+            "p_draft": ((B, G), torch.float32), "q_draft": ((B, G), torch.float32), "flags": ((B,), torch.int32)}
+    for n in names:
+        if n not in out:
+            shape, dt = spec[n]
+            out[n] = torch.empty(shape, dtype=dt, device=device)
+    return out
+
+
+def sv_verify_dense(target, draft, draft_ids, u_accept, u_sample, temperature, bonus=1, start=None, order=None, *,
+                    out=None, ws=None, stream=None, outputs=("accept", "n_accepted", "out_token", "p_draft",
+                                                            "q_draft", "flags")):
+    """Dense verification (see ``sv_verify_dense`` in include/sv.h). target [B, gamma+bonus, V], draft [B, gamma, V]
+    (float32 or bfloat16, vocabulary axis contiguous); draft_ids int32 [B, gamma]; u_accept float32 [B, gamma];
+    u_sample float32 [B, gamma + 1]; start int32 [B] (updated in place) or None; order int32 [B, gamma] or None.
+    Returns a dict of output tensors (flags as int32 holding the uint32 bits)."""
+    B, G = draft_ids.shape
+    dev = target.device
+    V = target.shape[-1]
+    t_seq, t_row = _logits_layout(target, "target", G + bonus, B, dev)
+    d_seq, d_row = _logits_layout(draft, "draft", G, B, dev)
+    if draft.dtype != target.dtype or draft.shape[-1] != V:
+        raise ValueError("draft must match target in dtype and vocabulary size")
+    _need(draft_ids, "draft_ids", torch.int32, (B, G), dev)
+    _need(u_accept, "u_accept", torch.float32, (B, G), dev)
+    _need(u_sample, "u_sample", torch.float32, (B, G + 1), dev)
+    if start is not None:
+        _need(start, "start", torch.int32, (B,), dev)
+    if order is not None:
+        _need(order, "order", torch.int32, (B, G), dev)
+    o = _outputs(B, G, dev, out, outputs)
+    if ws is None:
+        ws = workspace(SV_KIND_DENSE, B, G, V, dev)
+    st = LIB.sv_verify_dense(_ptr(target), t_seq, t_row, _ptr(draft), d_seq, d_row, _dtype_code(target), B, G, V,
+                             _ptr(draft_ids), _ptr(u_accept), _ptr(u_sample), float(temperature), int(bonus),
+                             _ptr(start), _ptr(order), _ptr(o.get("accept")), _ptr(o["n_accepted"]),
+                             _ptr(o["out_token"]), _ptr(o.get("p_draft")), _ptr(o.get("q_draft")), _ptr(o.get("flags")),
+                             _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    if st != SV_OK:
+        raise SVError(st)
+    return o
+
+
+def sv_verify_onehot_draft(target, draft_ids, u_accept, u_sample, temperature, bonus=1, start=None, order=None, *,
+                           out=None, ws=None, stream=None,
+                           outputs=("accept", "n_accepted", "out_token", "p_draft", "flags")):
+    """Greedy-draft verification (see ``sv_verify_onehot_draft`` in include/sv.h): q is one-hot at each draft id."""
+    B, G = draft_ids.shape
+    dev = target.device
+    V = target.shape[-1]
+    t_seq, t_row = _logits_layout(target, "target", G + bonus, B, dev)
+    _need(draft_ids, "draft_ids", torch.int32, (B, G), dev)
+    _need(u_accept, "u_accept", torch.float32, (B, G), dev)
+    _need(u_sample, "u_sample", torch.float32, (B, G + 1), dev)
+    if start is not None:
+        _need(start, "start", torch.int32, (B,), dev)
+    if order is not None:
+        _need(order, "order", torch.int32, (B, G), dev)
+    o = _outputs(B, G, dev, out, outputs)
+    if ws is None:
+        ws = workspace(SV_KIND_ONEHOT, B, G, V, dev)
+    st = LIB.sv_verify_onehot_draft(_ptr(target), t_seq, t_row, _dtype_code(target), B, G, V, _ptr(draft_ids),
+                                    _ptr(u_accept), _ptr(u_sample), float(temperature), int(bonus), _ptr(start),
+                                    _ptr(order), _ptr(o.get("accept")), _ptr(o["n_accepted"]), _ptr(o["out_token"]),
+                                    _ptr(o.get("p_draft")), _ptr(o.get("flags")), _ptr(ws),
+                                    0 if ws is None else ws.numel(), _stream(stream))
+    if st != SV_OK:
+        raise SVError(st)
+    return o
+
+
+def sv_verify_sparse(p_ids, p_probs, q_ids, q_probs, spec_ids, u_accept, u_sample, bonus=1, vocab_size=0, *,
+                     out=None, stream=None,
+                     outputs=("accept", "n_accepted", "out_token", "correction_probs", "p_spec", "q_spec", "flags")):
+    """Sparse top-k verification (see ``sv_verify_sparse`` in include/sv.h). p_ids/p_probs [B, gamma+bonus, kp],
+    q_ids/q_probs [B, gamma, kq] (int32 / float32, contiguous); spec_ids int32 [B, gamma]."""
+    B, G = spec_ids.shape
+    dev = spec_ids.device
+    kp, kq = p_ids.shape[-1], q_ids.shape[-1]
+    _need(p_ids, "p_ids", torch.int32, (B, G + bonus, kp), dev)
+    _need(p_probs, "p_probs", torch.float32, (B, G + bonus, kp), dev)
+    _need(q_ids, "q_ids", torch.int32, (B, G, kq), dev)
+    _need(q_probs, "q_probs", torch.float32, (B, G, kq), dev)
+    _need(spec_ids, "spec_ids", torch.int32, (B, G), dev)
+    _need(u_accept, "u_accept", torch.float32, (B, G), dev)
+    _need(u_sample, "u_sample", torch.float32, (B, G + 1), dev)
+    o = {} if out is None else out
+    spec = {"accept": ((B, G), torch.uint8), "n_accepted": ((B,), torch.int32), "out_token": ((B,), torch.int32),
+            "correction_probs": ((B, G, kp), torch.float32), "p_spec": ((B, G), torch.float32),
+            "q_spec": ((B, G), torch.float32), "flags": ((B,), torch.int32)}
+    for n in outputs:
+        if n not in o:
+            o[n] = torch.empty(spec[n][0], dtype=spec[n][1], device=dev)
+    st = LIB.sv_verify_sparse(_ptr(p_ids), _ptr(p_probs), _ptr(q_ids), _ptr(q_probs), B, G, kp, kq, int(vocab_size),
+                              _ptr(spec_ids), _ptr(u_accept), _ptr(u_sample), int(bonus), _ptr(o.get("accept")),
+                              _ptr(o["n_accepted"]), _ptr(o["out_token"]), _ptr(o.get("correction_probs")),
+                              _ptr(o.get("p_spec")), _ptr(o.get("q_spec")), _ptr(o.get("flags")), None, 0,
+                              _stream(stream))
+    if st != SV_OK:
+        raise SVError(st)
+    return o

@@ -1,0 +1,139 @@
+"""Helpers for the GPU parity tests: move seeded inputs to the device, run the HIP path through the C ABI, and
+compare with the oracle.
+
+Decision parity (accept flags, accepted lengths, drawn tokens) must be exact except where the oracle's decision
+margin is below 1e-5 (|u - min(1, ratio)| for a flag, the distance of t to the nearer CDF boundary over the total
+mass for a draw). Every disagreement must sit at such a margin, and disagreeing positions (a flag, or a token where
+the accepted lengths agree) must stay under 1e-4 of the verified positions. Probabilities agree to 1e-5 relative
+for float32 logits and 2e-3 relative for bfloat16 logits (absolute 1e-30 in the denormal range).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+
+MARGIN = 1e-5
+MAX_DISAGREE_FRACTION = 1e-4
+RTOL = {"f32": 1e-5, "bf16": 2e-3}
+ATOL = 1e-30
+
+
+def dev():
+    return torch.device("cuda", 0)
+
+
+def t_logits(x, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x)).view(torch.bfloat16).to(dev())
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev())
+
+
+def t_(x, dt):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dt).to(dev())
+
+
+def host(out):
+    res = {}
+    for k, v in out.items():
+        a = v.cpu().numpy()
+        if k == "flags":
+            a = a.astype(np.uint32)
+        res[k] = a
+    return res
+
+
+def run_dense(case, *, start=None, order=None, target=None, draft=None, u_accept=None, u_sample=None):
+    from lossless_draft_verification_spec_amd import sv
+    tgt = t_logits(case["target"], case["dtype"]) if target is None else target
+    dft = t_logits(case["draft"], case["dtype"]) if draft is None else draft
+    st = None if start is None else t_(start, torch.int32)
+    od = None if order is None else t_(order, torch.int32)
+    ua = t_(case["u_accept"] if u_accept is None else u_accept, torch.float32)
+    us = t_(case["u_sample"] if u_sample is None else u_sample, torch.float32)
+    out = sv.sv_verify_dense(tgt, dft, t_(case["draft_ids"], torch.int32), ua, us, case["temperature"],
+                             bonus=case["bonus"], start=st, order=od)
+    torch.cuda.synchronize()
+    res = host(out)
+    if st is not None:
+        res["start_out"] = st.cpu().numpy()
+    return res
+
+
+def run_onehot(case, *, start=None, order=None, target=None):
+    from lossless_draft_verification_spec_amd import sv
+    tgt = t_logits(case["target"], case["dtype"]) if target is None else target
+    st = None if start is None else t_(start, torch.int32)
+    od = None if order is None else t_(order, torch.int32)
+    out = sv.sv_verify_onehot_draft(tgt, t_(case["draft_ids"], torch.int32), t_(case["u_accept"], torch.float32),
+                                    t_(case["u_sample"], torch.float32), case["temperature"], bonus=case["bonus"],
+                                    start=st, order=od)
+    torch.cuda.synchronize()
+    res = host(out)
+    if st is not None:
+        res["start_out"] = st.cpu().numpy()
+    return res
+
+
+def run_sparse(case, vocab_size=0):
+    from lossless_draft_verification_spec_amd import sv
+    out = sv.sv_verify_sparse(t_(case["p_ids"], torch.int32), t_(case["p_probs"], torch.float32),
+                              t_(case["q_ids"], torch.int32), t_(case["q_probs"], torch.float32),
+                              t_(case["spec_ids"], torch.int32), t_(case["u_accept"], torch.float32),
+                              t_(case["u_sample"], torch.float32), bonus=case["bonus"], vocab_size=vocab_size)
+    torch.cuda.synchronize()
+    return host(out)
+
+
+def oracle_dense(case, *, start=None, order=None, seqs=None, onehot=False):
+    sl = slice(None) if seqs is None else seqs
+    kw = dict(bonus=case["bonus"], dtype=case["dtype"],
+              start=None if start is None else np.asarray(start)[sl],
+              order=None if order is None else np.asarray(order)[sl])
+    if onehot:
+        return oracle.verify_onehot(case["target"][sl], case["draft_ids"][sl], case["u_accept"][sl],
+                                    case["u_sample"][sl], case["temperature"], **kw)
+    return oracle.verify_dense(case["target"][sl], case["draft"][sl], case["draft_ids"][sl], case["u_accept"][sl],
+                               case["u_sample"][sl], case["temperature"], **kw)
+
+
+def compare_decisions(g, o, label="", verified=None):
+    """Decision parity with margin accounting. Returns a summary dict; raises AssertionError on a failure."""
+    acc_g, acc_o = g["accept"].astype(bool), o["accept"].astype(bool)
+    dis_acc = acc_g != acc_o
+    if dis_acc.any():
+        m = o["margin_accept"][dis_acc]
+        assert np.all(m < MARGIN), f"{label}: accept flags disagree at margins {m[m >= MARGIN][:5]}"
+    n_dis = g["n_accepted"] != o["n_accepted"]
+    if n_dis.any():
+        # a different accepted length must come from a flag disagreement (already margin-checked) in that sequence
+        assert np.all(dis_acc[n_dis].any(axis=-1)), f"{label}: n differs without a flag disagreement"
+    tok_dis = (~n_dis) & (g["out_token"] != o["out_token"])
+    if tok_dis.any():
+        m = o["margin_cdf"][tok_dis]
+        assert np.all(m < MARGIN), (f"{label}: tokens disagree at margins {m[m >= MARGIN][:5]} "
+                                    f"(gpu {g['out_token'][tok_dis][:5]} oracle {o['out_token'][tok_dis][:5]})")
+    fl_g, fl_o = g["flags"].astype(np.uint32), o["flags"].astype(np.uint32)
+    same = ~n_dis & ~tok_dis
+    assert np.array_equal(fl_g[same], fl_o[same]), f"{label}: flags {fl_g[same][fl_g[same] != fl_o[same]][:5]}"
+    if "start_out" in g:
+        assert np.array_equal(g["start_out"][~n_dis], o["start_out"][~n_dis]), f"{label}: start"
+    n_pos = int(np.isfinite(o["margin_accept"]).sum()) if verified is None else int(verified)
+    bad = int(dis_acc.sum() + tok_dis.sum())
+    assert bad <= MAX_DISAGREE_FRACTION * max(n_pos, 1), f"{label}: {bad} disagreeing positions of {n_pos}"
+    near_acc = int((o["margin_accept"] < MARGIN).sum())
+    near_cdf = int((o["margin_cdf"] < MARGIN).sum())
+    return dict(positions=n_pos, disagreements=bad, near_ties_accept=near_acc, near_ties_cdf=near_cdf)
+
+
+def compare_probs(g, o, key, dtype, label="", key_o=None):
+    a = g[key].astype(np.float64)
+    b = o[key if key_o is None else key_o].astype(np.float64)
+    nan_a, nan_b = np.isnan(a), np.isnan(b)
+    assert np.array_equal(nan_a, nan_b), f"{label}: NaN pattern of {key} differs"
+    ok = ~nan_b
+    err = np.abs(a[ok] - b[ok])
+    lim = RTOL[dtype] * np.abs(b[ok]) + ATOL
+    assert np.all(err <= lim), f"{label}: {key} max rel err {np.max(err / np.maximum(np.abs(b[ok]), 1e-300)):.3g}"
+    return float(np.max(err / np.maximum(np.abs(b[ok]), 1e-300))) if ok.any() else 0.0
