@@ -222,7 +222,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--only", default=None, help="time only this workload (the headline is always timed)")
+    ap.add_argument("--only", default=None,
+                    help="time only this workload besides the headline ('headline': the headline alone)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy, the reference for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); sequences shard across GPUs with no "
@@ -233,6 +236,15 @@ def main():
     from lossless_draft_verification_spec_amd import sv, workloads
 
     d = torch.device("cuda", 0)
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=d)        # 1 GiB read + 1 GiB written per copy
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: 3 x 1 GiB")
+        del src, dst
+        torch.cuda.empty_cache()
     log("generating", HEADLINE)
     head = workloads.make(HEADLINE)
     r = bench_dense(head, args.steps, args.warmup, torch, sv, d)

@@ -16,8 +16,8 @@ enum JobKind : int32_t {
   JOB_BONUS = 3,     // bonus draw from p of target row gamma
 };
 
-// One record per sequence, written by the scan kernel and read by the draw kernels.
-struct alignas(32) Job {
+// One record per sequence, written by the leader workgroup of the mass pass and read by the pick.
+struct alignas(16) Job {
   int32_t kind;      // JobKind
   int32_t row;       // storage row of the draw (gamma for the bonus)
   int32_t d;         // draft id at that row (one-hot residual)
@@ -26,6 +26,9 @@ struct alignas(32) Job {
   float m_t;         // exact max of the target row (from the statistics pass; unused for the bonus)
   float m_d;         // exact max of the draft row
   float pad1;
+  double kappa;      // S_d / S_t of the row pair as estimated by the statistics pass (float32 sums)
+  int32_t new_start; // start for the next call (-1: leave unchanged), written by the pick
+  int32_t pad2;
 };
 
 // Sizes and workspace layout of one dense / one-hot call. Depends only on (B, gamma, V, number of tensors).
@@ -36,10 +39,13 @@ struct DensePlan {
   int32_t ntens = 0;     // 2: target + draft; 1: target only (one-hot)
   int32_t nseg1 = 1;     // segments per row in the statistics pass
   int32_t nseg2 = 1;     // segments per row in the float64 draw passes
+  int64_t nch = 1;       // 1024-element chunks per row in the draw passes
+  int32_t cpw = 1;       // chunks per workgroup of the draw's mass pass
   size_t off_part1 = 0;  // float2 (max, sum) per (tensor, b, row, seg1)
   size_t off_jobs = 0;   // Job per b
-  size_t off_part2a = 0; // double4 (m_t, S_t, m_d, S_d) per (b, seg2)
-  size_t off_part2b = 0; // double2 (residual mass, p mass) per (b, seg2)
+  size_t off_part2a = 0; // double4 (m_seg, S_t, m_d, S_d) per (b, seg2)
+  size_t off_chunks = 0; // chunk record per (b, chunk)
+  size_t off_masses = 0; // double per (b, chunk)
   size_t total = 0;
 };
 

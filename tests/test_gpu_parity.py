@@ -160,6 +160,21 @@ def test_dense_data_faults():
     assert g["flags"][7] & oracle.FLAG_ID_RANGE
 
 
+@pytest.mark.parametrize("V", [30_000, 600_001])
+def test_dense_near_equal_distributions(V):
+    """Draft = target + tiny noise: the residual's sign is undecided for most elements, so the draw recomputes most
+    chunks exactly (at V = 600001 more chunks than the pick's queue holds). Uniforms near 1 force rejections."""
+    B, G = 3, 2
+    case = W.dense_case(B, G, V, dtype="f32", sigma_t=2.0, sigma_d=2e-5, seed=16)
+    case["u_accept"][:] = np.float32(0.99999)
+    g = run_dense(case)
+    o = oracle_dense(case)
+    s = compare_decisions(g, o, f"near-equal V={V}")
+    compare_probs(g, o, "p_draft", "f32")
+    log(f"near-equal V={V}: {s}, n {g['n_accepted'].tolist()}")
+    assert (g["n_accepted"] < G).any()
+
+
 def test_dense_is_deterministic():
     case = W.dense_case(4, 6, 40_000, dtype="bf16", seed=15)
     a, b = run_dense(case), run_dense(case)
