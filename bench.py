@@ -215,6 +215,27 @@ def cpu_baseline(case, seconds):
                        f"numpy float64, one thread")
 
 
+def measured_traffic():
+    """HBM bytes per launch of the statistics kernel from the committed FETCH_SIZE / WRITE_SIZE counter summary,
+    or None when the kernel source has changed since the counters were taken."""
+    import hashlib
+    prof = os.path.join(ROOT, "profiles", "k_stats_dense_block_traffic.txt")
+    src = os.path.join(ROOT, "lossless_draft_verification_spec_amd", "csrc", "sv_dense.hip")
+    try:
+        rec = None
+        with open(prof) as f:
+            for ln in f:
+                if ln.startswith("TRAFFIC_JSON "):
+                    rec = json.loads(ln[len("TRAFFIC_JSON "):])
+        with open(src, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    if rec is None or rec.get("source_sha256") != sha:
+        return None
+    return int(rec["traffic_bytes"])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -277,7 +298,7 @@ def main():
         "hbm_GBps": r["hbm_GBps"], "hbm_frac_of_peak": r["hbm_frac"],
         "roofline": {"bound": "hbm", "achieved": r.get("stats_kernel_GBps"), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": (r["stats_kernel_GBps"] / HBM_PEAK_GBPS) if r.get("stats_kernel_GBps") else None,
-                     "traffic": None, "kernel": "k_stats (row statistics)",
+                     "traffic": measured_traffic(), "kernel": "k_stats (row statistics)", "traffic_unit": "B/launch",
                      "kernel_ms": r.get("stats_kernel_ms"), "kernel_bytes": r.get("stats_kernel_bytes")},
         "cpu_baseline": cpu,
         "workloads": {HEADLINE: r, **others},
