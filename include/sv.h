@@ -72,8 +72,11 @@ extern "C" {
 /*
  * Bytes of device workspace a call of `kind` needs for B sequences of gamma drafts over V_or_k (V for dense and
  * one-hot, the p-support size kp for sparse). Depends only on these arguments. Returns 0 when no workspace is
- * needed and (size_t)-1 for arguments the calls would reject. The workspace is scratch: its contents need not be
- * initialised and are meaningless afterwards; it must not be shared by calls that may run concurrently.
+ * needed and (size_t)-1 for arguments the calls would reject. The workspace holds the call's work-queue counters
+ * and scratch records. It must be zero-filled before its first use (for example allocated with torch.zeros or
+ * cleared with hipMemset once); every call leaves its counters at zero again, so the same workspace serves any
+ * number of later calls of any shape it is large enough for without being cleared again. Apart from the counters
+ * its contents are meaningless after a call. It must not be shared by calls that may run concurrently.
  */
 size_t sv_workspace_bytes(int kind, int64_t B, int32_t gamma, int64_t V_or_k);
 
@@ -81,10 +84,10 @@ size_t sv_workspace_bytes(int kind, int64_t B, int32_t gamma, int64_t V_or_k);
 const char* sv_status_string(int status);
 
 /*
- * Profiling hook (no counterpart on the pages; it lets a caller time the HBM-bound pass on its own). When both
+ * Profiling hook (no counterpart on the pages; it lets a caller time the verifier's kernel on its own). When both
  * events are non-NULL, the next sv_verify_dense or sv_verify_onehot_draft call made on this host thread records
- * `start_event` just before its row-statistics kernel and `stop_event` just after it, on that call's stream, and
- * then forgets them; hipEventElapsedTime(start, stop) is that kernel's duration. The events (hipEvent_t) are created
+ * `start_event` when its kernel starts and `stop_event` when it ends (from the dispatch itself), on that call's
+ * stream, and then forgets them; hipEventElapsedTime(start, stop) is that kernel's duration. The events (hipEvent_t) are created
  * and owned by the caller. Passing two NULLs clears a pending request. Returns SV_OK, or SV_ERR_NULL when exactly
  * one event is NULL. The request is per host thread, so concurrent callers on other threads are unaffected.
  */

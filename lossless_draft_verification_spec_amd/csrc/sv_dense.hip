@@ -6,18 +6,20 @@
 // renormalised there, or a bonus token from the next target row when every draft is accepted (same guide,
 // section 2). p and q are softmaxes of the logits divided by the temperature (same guide, section 9 Q3).
 //
-// Three launches, all on the caller's stream:
-//  1. k_stats     : one read of every verified logit row. Per (row, segment) it keeps a running max and a running
-//                   sum of exp2((z - max) * log2(e)/T) in float32, folds the threads together in float64 and writes
-//                   (max, sum, logit at the draft id). 16-byte non-temporal loads, a two-group ping-pong per thread.
-//                   This pass moves almost all the bytes; it is bound by HBM bandwidth.
-//  2. k_draw_mass : one-wave workgroups. Each first evaluates p(x), q(x) and the strict test u < min(1, p/q) for
-//                   every verified slot of its sequence and finds the first rejection from `start` along `order`
-//                   (the first workgroup of the sequence writes the per-row outputs and the draw job); it then
-//                   computes, in float64, the exact softmax normalisers and the residual mass of its chunks of the
-//                   row(s) the draw needs (at most one row pair per sequence).
-//  3. k_draw_pick : one workgroup per sequence: chunk masses, their running sum, and a search inside the one chunk
-//                   that holds t = u * (total mass).
+// One launch on the caller's stream: one 256-thread workgroup per work item, in a queue order that the hardware's
+// in-order dispatch turns into a schedule. Three kinds of item:
+//  - statistics item (one segment of one verified logit row): a running max and a running sum of
+//    exp2((z - max) * log2(e)/T) in float32, folded over the workgroup in float64, written as (max, sum, logit at the
+//    draft id). 16-byte non-temporal loads, a two-group ping-pong per thread. These items move almost all the bytes;
+//    they are bound by HBM bandwidth.
+//  - scan (one per sequence, queued about one resident round after the sequence's statistics items): evaluates p(x),
+//    q(x) and the strict test u < min(1, p/q) of every verified slot, finds the first rejection from `start` along
+//    `order`, writes the per-row outputs and publishes the sequence's draw job.
+//  - draw task (a range of 512-element chunks of the row or row pair the draw needs; queued after every statistics
+//    item): float64 residual masses of its chunks and partial softmax normalisers. The last task of a sequence to
+//    finish forms the chunk masses and their running sum, and searches the one chunk that holds t = u * (total mass).
+// Draw tasks start on the compute units that the last statistics items leave free, so the float64 draw overlaps the
+// tail of the streaming phase instead of waiting for a second launch.
 // The float64 draw exists because a token boundary of the residual CDF often lies within 1e-7 of t at these
 // vocabulary sizes; float32 sums would pick a neighbouring token far more often than the float64 reference does.
 
@@ -41,9 +43,27 @@ constexpr int kUnroll = 4;          // 16-byte vectors per thread per group
 #define SV_STATS_NT 1
 #endif
 constexpr bool kNonTemporal = SV_STATS_NT != 0;   // streaming loads that bypass cache retention
-constexpr int kStatsWpe = 4;        // waves per SIMD the statistics kernel is compiled for (more waves stream worse)
-constexpr int kStatsWgPerCu = 0;    // persistent grid cap per CU (0: one workgroup per work item)
-constexpr int kDrawBlock = 256;
+constexpr int kWpe = 4;             // waves per SIMD the kernel is compiled for (more waves stream worse)
+constexpr int kDrawBlock = 256;     // threads per workgroup, both kinds of item
+#ifndef SV_ITEM_BYTES
+#define SV_ITEM_BYTES 131072
+#endif
+constexpr int64_t kItemBytes = SV_ITEM_BYTES;   // target bytes of logits per statistics item
+#ifndef SV_TASK_CHUNKS
+#define SV_TASK_CHUNKS 16
+#endif
+constexpr int64_t kTaskChunks = SV_TASK_CHUNKS; // chunks per draw task (four per wave)
+#ifndef SV_LAG_ROUNDS
+#define SV_LAG_ROUNDS 1
+#endif
+constexpr int kLagRounds = SV_LAG_ROUNDS;       // resident rounds of statistics items between a sequence's statistics
+                                                // and its scan
+constexpr int kCtrStride = 64;                  // int32 slots between per-sequence counters (one 256-byte line each)
+#ifndef SV_SLEEP
+#define SV_SLEEP 16
+#endif
+constexpr int32_t kSpinCap = 1 << 20;           // polls before a draw task stops waiting for its job (never reached
+                                                // when the hardware dispatches as documented)
 
 struct alignas(16) Partial1 {
   float m;        // exact max of the segment's logits (raw, before the temperature)
@@ -55,6 +75,14 @@ struct alignas(16) Partial1 {
 // element access
 // ----------------------------------------------------------------------------------------------------------------
 
+// Loads through the global address space. The logit rows are always global memory; saying so keeps the loads
+// global_load instructions (not flat ones) wherever the compiler cannot see where a pointer came from.
+#define SV_GLOBAL __attribute__((address_space(1)))
+template <typename V>
+__device__ __forceinline__ V gload(const V* p) {
+  return *(const SV_GLOBAL V*)(p);
+}
+
 template <typename T> struct Vec;
 template <> struct Vec<float> {
   static constexpr int kEPV = 4;                                  // elements per 16-byte vector
@@ -62,7 +90,7 @@ template <> struct Vec<float> {
     v[0] = __uint_as_float(w.x); v[1] = __uint_as_float(w.y);
     v[2] = __uint_as_float(w.z); v[3] = __uint_as_float(w.w);
   }
-  __device__ static __forceinline__ float load1(const float* p) { return *p; }
+  __device__ static __forceinline__ float load1(const float* p) { return gload(p); }
 };
 template <> struct Vec<uint16_t> {
   static constexpr int kEPV = 8;
@@ -72,12 +100,106 @@ template <> struct Vec<uint16_t> {
     v[4] = __uint_as_float(w.z << 16); v[5] = __uint_as_float(w.z & 0xFFFF0000u);
     v[6] = __uint_as_float(w.w << 16); v[7] = __uint_as_float(w.w & 0xFFFF0000u);
   }
-  __device__ static __forceinline__ float load1(const uint16_t* p) { return __uint_as_float(uint32_t(*p) << 16); }
+  __device__ static __forceinline__ float load1(const uint16_t* p) { return __uint_as_float(uint32_t(gload(p)) << 16); }
 };
 
 __device__ __forceinline__ float ex2f(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Element i of a row of V logits, -inf for i >= V. The load address is clamped into the row and the value selected
+// afterwards, so a run of such loads issues without a branch (and a wait) per element.
+template <typename T>
+__device__ __forceinline__ float elem_or_ninf(const T* row, int64_t i, int64_t V) {
+  const float z = Vec<T>::load1(row + (i < V ? i : V - 1));
+  return i < V ? z : -INFINITY;
+}
+
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 gload4(const uint4* p) {
+  const u32x4 r = *(const SV_GLOBAL u32x4*)(p);
+  return make_uint4(r.x, r.y, r.z, r.w);
+}
+
+// ----------------------------------------------------------------------------------------------------------------
+// wave-level reductions and scans through DPP: data-parallel-primitive moves between the lanes of a row of 16 inside
+// the VALU (a few cycles each, where a cross-lane shuffle is an LDS round trip); rows are combined with readlane.
+// All 64 lanes must be active. The operation order is fixed, so results are bitwise reproducible and identical in
+// every lane.
+// ----------------------------------------------------------------------------------------------------------------
+
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror: lane i <- lane 7 - i within each 8
+constexpr int kDppMirror = 0x140;      // row_mirror: lane i <- lane 15 - i within each row
+constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;   // row_shr:n
+constexpr int kDppBcast15 = 0x142;     // row_bcast:15: lane 15 of the previous row
+constexpr int kDppBcast31 = 0x143;     // row_bcast:31: lane 31
+
+// v moved by the DPP control CTRL; lanes outside ROWS, or whose source lies outside the row, get `old`.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ int dpp_i(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWS, 0xF, false);
+}
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+  return __int_as_float(dpp_i<CTRL, ROWS>(__float_as_int(old), __float_as_int(v)));
+}
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ double dpp_d(double old, double v) {
+  return __hiloint2double(dpp_i<CTRL, ROWS>(__double2hiint(old), __double2hiint(v)),
+                          dpp_i<CTRL, ROWS>(__double2loint(old), __double2loint(v)));
+}
+__device__ __forceinline__ double readlane_d(double v, int l) {
+  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
+                          __builtin_amdgcn_readlane(__double2loint(v), l));
+}
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+  v += dpp_d<kDppXor1>(0.0, v);
+  v += dpp_d<kDppXor2>(0.0, v);
+  v += dpp_d<kDppHalfMirror>(0.0, v);
+  v += dpp_d<kDppMirror>(0.0, v);
+  return (readlane_d(v, 0) + readlane_d(v, 16)) + (readlane_d(v, 32) + readlane_d(v, 48));
+}
+
+__device__ __forceinline__ double wave_max_d(double v) {
+  v = fmax(v, dpp_d<kDppXor1>(v, v));
+  v = fmax(v, dpp_d<kDppXor2>(v, v));
+  v = fmax(v, dpp_d<kDppHalfMirror>(v, v));
+  v = fmax(v, dpp_d<kDppMirror>(v, v));
+  return fmax(fmax(readlane_d(v, 0), readlane_d(v, 16)), fmax(readlane_d(v, 32), readlane_d(v, 48)));
+}
+
+__device__ __forceinline__ float wave_max_f(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v, v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v, v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v, v));
+  v = fmaxf(v, dpp_f<kDppMirror>(v, v));
+  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
+}
+
+__device__ __forceinline__ int wave_min_i(int v) {
+  v = min(v, dpp_i<kDppXor1>(v, v));
+  v = min(v, dpp_i<kDppXor2>(v, v));
+  v = min(v, dpp_i<kDppHalfMirror>(v, v));
+  v = min(v, dpp_i<kDppMirror>(v, v));
+  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+// Inclusive running sum over the lanes in lane order (Hillis-Steele inside each row, then row carries).
+__device__ __forceinline__ double wave_incl_scan(double v) {
+  v += dpp_d<kDppShr1>(0.0, v);
+  v += dpp_d<kDppShr2>(0.0, v);
+  v += dpp_d<kDppShr4>(0.0, v);
+  v += dpp_d<kDppShr8>(0.0, v);
+  v += dpp_d<kDppBcast15, 0xA>(0.0, v);
+  v += dpp_d<kDppBcast31, 0xC>(0.0, v);
+  return v;
+}
 
 // ----------------------------------------------------------------------------------------------------------------
 // block reductions (fixed order, so results are bitwise reproducible)
@@ -85,7 +207,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 template <int BLOCK>
 __device__ __forceinline__ float block_max(float v, float* sh) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  v = wave_max_f(v);
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   __syncthreads();
   if (l == 0) sh[w] = v;
@@ -98,7 +220,7 @@ __device__ __forceinline__ float block_max(float v, float* sh) {
 
 template <int BLOCK>
 __device__ __forceinline__ double block_sum(double v, double* sh) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  v = wave_sum(v);
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   __syncthreads();
   if (l == 0) sh[w] = v;
@@ -110,18 +232,69 @@ __device__ __forceinline__ double block_sum(double v, double* sh) {
 }
 
 // ----------------------------------------------------------------------------------------------------------------
+// passing records between workgroups of one kernel
+// ----------------------------------------------------------------------------------------------------------------
+// Each XCD has its own write-back L2, so a plain store from one workgroup may not be visible to a workgroup on
+// another XCD before the kernel ends. Records handed over inside a kernel are stored and loaded at device scope
+// (written through to, and read from, the level where all XCDs agree); the writer waits for its stores to complete
+// and then counts itself on a per-sequence counter (a system-scope atomic, performed where all XCDs agree); the
+// workgroup that brings the count to its total reads the records. Nobody waits on a counter.
+template <typename V>
+__device__ __forceinline__ void st_dev(V* p, V v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename V>
+__device__ __forceinline__ V ld_dev(const V* p) {
+  return __hip_atomic_load(const_cast<V*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ctr_add(int32_t* p) {
+  return __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// ----------------------------------------------------------------------------------------------------------------
 // 1. row statistics
 // ----------------------------------------------------------------------------------------------------------------
 
-struct StatsParams {
+struct ChunkRec;
+
+// Everything one call needs, shared by both kinds of work item.
+struct DenseParams {
   const void* tgt; int64_t t_seq, t_row;
-  const void* dft; int64_t d_seq, d_row;
-  int64_t B; int32_t G; int64_t V; int32_t nseg; int32_t ntens;
-  float c;                                  // log2(e) / T, rounded to float
-  const int32_t* start; const int32_t* order;
-  const int32_t* ids;                       // [B][G] draft ids (the logit at the id is gathered with segment 0)
-  Partial1* part;                           // [ntens][B][G][nseg]
+  const void* dft; int64_t d_seq, d_row;     // dft == nullptr: one-hot drafts
+  int64_t B; int32_t G; int64_t V; int32_t nseg1; int32_t ntens; int32_t bonus;
+  float c;                                    // log2(e) / T, rounded to float (statistics items)
+  double c2;                                  // log2(e) / T in float64 (draw: weights are 2^((z - max) * c2))
+  const int32_t* ids; const float* ua; const float* us;
+  int32_t* start; const int32_t* order;
+  uint8_t* accept; int32_t* n_acc; int32_t* token; float* p_draft; float* q_draft; uint32_t* flags;
+  // work queue: per sequence n1 statistics items and ntask draw tasks; the draw tasks of sequence b follow the
+  // statistics items of sequence b + lag
+  int32_t n1; int32_t ntask; int32_t lag; int32_t n_items;
+  int64_t nch;                                // 1024-element chunks per row
+  int32_t* ready;                             // per b (stride kCtrStride): statistics items finished
+  int32_t* done;                              // per b (stride kCtrStride): draw tasks finished
+  Job* jobs;                                  // per b: the draw job
+  Partial1* part1;                            // per (tensor, b, row, segment)
+  double4* part2;            // per (b, task): reference max, sum e_t (relative to it), m_d, sum e_d
+  ChunkRec* chunks;          // per (b, chunk), see ChunkRec
+  double* masses;            // per (b, chunk): chunk masses, written by the pick when the chunks exceed one tile
 };
+
+// The parameters are read in place from the kernel-argument segment (constant address space) by every function,
+// inlined or not, instead of being copied to per-lane private memory for the functions that are not inlined.
+typedef const __attribute__((address_space(4))) DenseParams DP;
+
+// The kernel's parameters, read in place from its kernel-argument segment. Only the kernel itself may ask for that
+// segment's address; functions that are not inlined receive the reference as an argument (in vector registers) and
+// make it uniform again with uniform_params, so that their parameter reads are scalar loads.
+__device__ __forceinline__ DP& kernel_params() { return *(DP*)(__builtin_amdgcn_kernarg_segment_ptr()); }
+
+__device__ __forceinline__ DP& uniform_params(DP& p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(&p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32));
+  return *reinterpret_cast<DP*>((uint64_t(hi) << 32) | lo);
+}
 
 // Running state of one thread: max m, mc = fl(m * c), s = sum of 2^(z*c - mc).
 struct Run {
@@ -158,7 +331,7 @@ __device__ __forceinline__ void absorb(Run& st, const float* v, float c) {
 
 template <bool NT>
 __device__ __forceinline__ uint4 load_vec(const uint4* p) {
-  const u32x4* q = reinterpret_cast<const u32x4*>(p);
+  const SV_GLOBAL u32x4* q = (const SV_GLOBAL u32x4*)(p);
   u32x4 r;
   if constexpr (NT) r = __builtin_nontemporal_load(q);
   else r = *q;
@@ -167,15 +340,13 @@ __device__ __forceinline__ uint4 load_vec(const uint4* p) {
 
 // One work item: segment `seg` of one row. Returns without writing when the row's slot lies before start.
 template <typename T, int BLOCK, int U, bool NT>
-__device__ __forceinline__ void stats_item(const StatsParams& prm, int64_t item, float* sh_f, double* sh_d) {
+__device__ __forceinline__ void stats_item(DP& prm, int64_t b, int item, float* sh_f, double* sh_d) {
   using VT = Vec<T>;
   constexpr int EPV = VT::kEPV;
 
-  int64_t w = item;
-  const int seg = int(w % prm.nseg); w /= prm.nseg;
-  const int row = int(w % prm.G);    w /= prm.G;
-  const int64_t b = w % prm.B;
-  const int tens = int(w / prm.B);
+  const int seg = item % prm.nseg1;
+  const int row = (item / prm.nseg1) % prm.G;
+  const int tens = item / (prm.nseg1 * prm.G);
 
   if (prm.start) {                                   // rows of slots before start are not read
     const int st = prm.start[b];
@@ -202,13 +373,13 @@ __device__ __forceinline__ void stats_item(const StatsParams& prm, int64_t item,
   int64_t head = int64_t(((16u - (addr & 15u)) & 15u) / sizeof(T));
   if (head > V) head = V;
   const int64_t nvec = (V - head) / EPV;
-  const int64_t v0 = nvec * seg / prm.nseg, v1 = nvec * (seg + 1) / prm.nseg;
+  const int64_t v0 = nvec * seg / prm.nseg1, v1 = nvec * (seg + 1) / prm.nseg1;
 
   Run st{-INFINITY, -INFINITY, 0.f};
   if (seg == 0) {
     for (int64_t i = threadIdx.x; i < head; i += BLOCK) { float z = VT::load1(base + i); absorb<1>(st, &z, c); }
   }
-  if (seg == prm.nseg - 1) {
+  if (seg == prm.nseg1 - 1) {
     for (int64_t i = head + nvec * EPV + threadIdx.x; i < V; i += BLOCK) {
       float z = VT::load1(base + i);
       absorb<1>(st, &z, c);
@@ -275,29 +446,16 @@ __device__ __forceinline__ void stats_item(const StatsParams& prm, int64_t item,
     s = NAN;
   }
   s = block_sum<BLOCK>(s, sh_d);
-  if (threadIdx.x == 0) {
-    Partial1 out;
-    out.m = M;
-    out.zx = NAN;
+  if (threadIdx.x == 0) {          // read by other workgroups of this launch: device-scope stores
+    float zx = NAN;
     if (seg == 0) {
       const int x = prm.ids[b * prm.G + row];
-      if (x >= 0 && int64_t(x) < V) out.zx = VT::load1(base + x);
+      if (x >= 0 && int64_t(x) < V) zx = VT::load1(base + x);
     }
-    out.s = s;
-    prm.part[((int64_t(tens) * prm.B + b) * prm.G + row) * prm.nseg + seg] = out;
-  }
-}
-
-// Persistent over work items (row, segment): workgroup g handles items g, g + gridDim.x, ... The grid is sized by
-// the launcher to the device (WPE waves per SIMD, i.e. WPE * 4 / (BLOCK / 64) workgroups per CU).
-template <typename T, int BLOCK, int U, bool NT, int WPE>
-__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void k_stats(StatsParams prm) {
-  __shared__ float sh_f[BLOCK / 64];
-  __shared__ double sh_d[BLOCK / 64];
-  const int64_t n_items = int64_t(prm.ntens) * prm.B * prm.G * prm.nseg;
-  for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
-    stats_item<T, BLOCK, U, NT>(prm, item, sh_f, sh_d);
-    __syncthreads();
+    Partial1* out = prm.part1 + ((int64_t(tens) * prm.B + b) * prm.G + row) * prm.nseg1 + seg;
+    st_dev(&out->m, M);
+    st_dev(&out->zx, zx);
+    st_dev(&out->s, s);
   }
 }
 
@@ -305,7 +463,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(WPE, WPE)
 // 2. draw: accept tests and first-rejection scan, then the float64 draw (mass pass + pick)
 // ----------------------------------------------------------------------------------------------------------------
 //
-// The rows are cut into chunks of kChunk = 1024 consecutive elements (one wave, 16 consecutive elements per lane).
+// The rows are cut into chunks of kChunk = 512 consecutive elements (one wave, 8 consecutive elements per lane).
 // The mass pass starts, in every workgroup, with the accept tests of its sequence (from the statistics pass's
 // per-row max, sum and draft-id logit) and the scan for the first rejection; the workgroup of the sequence's first
 // segment writes the per-row outputs and the draw job. It then computes, per chunk of the draw's row(s), A = sum
@@ -316,48 +474,12 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(WPE, WPE)
 // recomputes that chunk exactly. The pick forms every chunk's mass, scans them in order, finds the chunk that
 // holds t = u * (total mass) and searches it with one wave.
 
-constexpr int kChunk = 1024;        // elements per chunk
-constexpr int kPer = 16;            // elements per lane in a chunk
+constexpr int kChunk = 512;         // elements per chunk
+constexpr int kPer = 8;             // elements per lane in a chunk
 constexpr double kBand = 3.0e-5;    // relative width of the undecided zone of the residual's sign test
-constexpr int kTile = 4096;         // chunks held in LDS at a time by the pick
+constexpr int kTile = 1024;         // chunks held in LDS at a time by the pick
+constexpr int kDrawWaves = kDrawBlock / 64;
 
-struct DenseParams {
-  const void* tgt; int64_t t_seq, t_row;
-  const void* dft; int64_t d_seq, d_row;     // dft == nullptr: one-hot drafts
-  int64_t B; int32_t G; int64_t V; int32_t nseg1; int32_t bonus;
-  float c;                                    // log2(e) / T, rounded to float (statistics pass)
-  double invT;                                // 1 / T in float64 (draw)
-  const int32_t* ids; const float* ua; const float* us;
-  int32_t* start; const int32_t* order;
-  uint8_t* accept; int32_t* n_acc; int32_t* token; float* p_draft; float* q_draft; uint32_t* flags;
-  const Partial1* part1;
-  Job* jobs;
-  int32_t nseg2; int32_t cpw; int64_t nch;
-  double4* part2a;     // per (b, seg): reference max m_seg, sum e_t (relative to m_seg), m_d, sum e_d
-  struct ChunkRec* chunks;   // per (b, chunk), see ChunkRec
-  double* masses;            // per (b, chunk): chunk masses, written by the pick when the chunks exceed one tile
-};
-
-// Combine the segment partials of one row: exact max m and S = sum 2^((z - m) * c) in float64; zx from segment 0.
-__device__ __forceinline__ void row_stats(const Partial1* p, int nseg, double c, float& m, double& S, float& zx) {
-  float mm = -INFINITY;
-  for (int i = 0; i < nseg; ++i) mm = fmaxf(mm, p[i].m);
-  double s = 0.0;
-  bool nan = false;
-  for (int i = 0; i < nseg; ++i) {
-    nan |= isnan(p[i].s);
-    if (p[i].m == mm) s += p[i].s;
-    else if (p[i].m != -INFINITY) s += p[i].s * exp2((double(p[i].m) - double(mm)) * c);
-  }
-  m = mm;
-  S = nan ? NAN : s;
-  zx = p[0].zx;
-}
-
-struct SlotEval {
-  float P, Q;
-  bool acc, qzero, bad_id, nonfinite;
-};
 
 // 2^x for a float64 x, to float32 accuracy at any magnitude: the integer part is applied exactly with ldexp, only
 // the fraction in [0, 1) goes through the hardware exp2.
@@ -368,49 +490,119 @@ __device__ __forceinline__ float exp2_split(double x) {
   return ldexpf(ex2f(float(x - n)), int(n));
 }
 
+// 2^((m - M) * c) for a segment max m <= M: exactly 1 when m == M, 0 for an empty segment, else to float32 accuracy
+// (the scan needs the row sums only to float32 accuracy; the draw forms its own float64 normalisers).
+__device__ __forceinline__ double seg_scale(float m, float M, double c) {
+  if (m == M) return 1.0;
+  if (m == -INFINITY) return 0.0;
+  return double(exp2_split((double(m) - double(M)) * c));
+}
+
+// Row statistics of a target row and (dense) its draft row from their segment partials, written by other
+// workgroups of this launch (device-scope loads): exact max m and S = sum 2^((z - m) * c) over the row. The partials
+// of both rows are requested together, four segments at a time, so rows of up to four segments cost one round trip.
+// Identical rows give identical results.
+struct RowPair {
+  float mt, zt, md, zd;   // max and logit at the draft id of the target and draft rows
+  double St, Sd;          // sums relative to the max (NaN when a segment saw NaN)
+};
+
+__device__ __forceinline__ RowPair row_pair_stats(const Partial1* pt, const Partial1* pd, int nseg, double c) {
+  constexpr int K = 4;
+  const Partial1* qd = pd ? pd : pt;             // one-hot: loads of the target row stand in, results unused
+  RowPair r;
+  r.zt = ld_dev(&pt[0].zx);
+  const float zd0 = ld_dev(&qd[0].zx);
+  r.zd = pd ? zd0 : 0.f;
+  float Mt = -INFINITY, Md = -INFINITY;
+  double St = 0.0, Sd = 0.0;
+  bool nt = false, nd = false;
+  for (int i0 = 0; i0 < nseg; i0 += K) {
+    float mt[K], md[K];
+    double st[K], sd[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {                 // clamped indices: every load is issued, none is conditional
+      const int i = min(i0 + k, nseg - 1);
+      mt[k] = ld_dev(&pt[i].m);
+      st[k] = ld_dev(&pt[i].s);
+      md[k] = ld_dev(&qd[i].m);
+      sd[k] = ld_dev(&qd[i].s);
+    }
+    float bt = Mt, bd = Md;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      if (i0 + k >= nseg) { mt[k] = md[k] = -INFINITY; st[k] = sd[k] = 0.0; }
+      bt = fmaxf(bt, mt[k]);
+      bd = fmaxf(bd, md[k]);
+    }
+    St *= seg_scale(Mt, bt, c);
+    Sd *= seg_scale(Md, bd, c);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      nt |= isnan(st[k]);
+      nd |= isnan(sd[k]);
+      St += st[k] * seg_scale(mt[k], bt, c);
+      Sd += sd[k] * seg_scale(md[k], bd, c);
+    }
+    Mt = bt;
+    Md = bd;
+  }
+  r.mt = Mt;
+  r.St = nt ? NAN : St;
+  r.md = pd ? Md : 0.f;
+  r.Sd = pd ? (nd ? NAN : Sd) : 1.0;
+  return r;
+}
+
+struct SlotEval {
+  float P, Q;
+  bool acc, qzero, bad_id, nonfinite;
+  RowPair rs;
+  int32_t x;
+  float us;               // the row's draw uniform
+};
+
+
 // p(x), q(x) and the strict test u < min(1, p/q) of storage row r. The log-probabilities are assembled in float64
 // from the row statistics; the hardware float32 log2/exp2 finish them (relative error ~1e-6 on the ratio and on
 // p(x), q(x)).
-__device__ __forceinline__ SlotEval eval_slot(const DenseParams& prm, int64_t b, int r) {
-  SlotEval e{NAN, NAN, false, false, false, false};
+__device__ __forceinline__ SlotEval eval_slot(const DP& prm, int64_t b, int r) {
+  SlotEval e;
+  e.P = e.Q = NAN;
+  e.acc = e.qzero = e.bad_id = e.nonfinite = false;
   const int G = prm.G;
   const double c = double(prm.c);
   const int x = prm.ids[b * G + r];
-  float mt, zt, md = 0.f, zd = 0.f;
-  double St, Sd = 1.0;
-  row_stats(prm.part1 + (b * G + r) * prm.nseg1, prm.nseg1, c, mt, St, zt);
-  e.nonfinite = isnan(St) || mt == INFINITY || mt == -INFINITY;
-  if (prm.dft) {
-    row_stats(prm.part1 + ((prm.B + b) * G + r) * prm.nseg1, prm.nseg1, c, md, Sd, zd);
-    e.nonfinite |= isnan(Sd) || md == INFINITY || md == -INFINITY;
-  }
+  const float u = prm.ua[b * G + r];
+  e.us = prm.us[b * (G + 1) + r];
+  e.x = x;
+  e.rs = row_pair_stats(prm.part1 + (b * G + r) * prm.nseg1,
+                        prm.dft ? prm.part1 + ((prm.B + b) * G + r) * prm.nseg1 : nullptr, prm.nseg1, c);
+  const RowPair& rs = e.rs;
+  e.nonfinite = isnan(rs.St) || rs.mt == INFINITY || rs.mt == -INFINITY;
+  if (prm.dft) e.nonfinite |= isnan(rs.Sd) || rs.md == INFINITY || rs.md == -INFINITY;
   if (x < 0 || int64_t(x) >= prm.V) {
     e.bad_id = true;
     return e;
   }
-  const double lp = (double(zt) - double(mt)) * c - double(__builtin_amdgcn_logf(float(St)));   // log2 p(x)
-  double lq = 0.0;                                                                              // one-hot: q(x) = 1
+  const double lp = (double(rs.zt) - double(rs.mt)) * c - double(__builtin_amdgcn_logf(float(rs.St)));   // log2 p(x)
+  double lq = 0.0;                                                                                       // one-hot
   if (prm.dft) {
-    e.qzero = (zd == -INFINITY);
-    lq = (double(zd) - double(md)) * c - double(__builtin_amdgcn_logf(float(Sd)));
+    e.qzero = (rs.zd == -INFINITY);
+    lq = (double(rs.zd) - double(rs.md)) * c - double(__builtin_amdgcn_logf(float(rs.Sd)));
   }
   e.P = exp2_split(lp);
   e.Q = prm.dft ? exp2_split(lq) : 1.f;
   float ratio = e.qzero ? 0.f : exp2_split(lp - lq);
   if (ratio != ratio) ratio = 0.f;
-  e.acc = prm.ua[b * G + r] < fminf(1.f, ratio);
+  e.acc = u < fminf(1.f, ratio);
   return e;
 }
 
-__device__ __forceinline__ int wave_min_i(int v) {
-  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
-  return v;
-}
-
-// Accept tests and first-rejection scan of sequence b by one wave (every wave of the sequence computes the same
-// result). The leader wave writes the per-row outputs, n_accepted, flags, out_token = -1 and the job record; the
-// new start is stored in the job and written by the pick, after every wave of this kernel has read the old one.
-__device__ Job seq_scan(const DenseParams& prm, int64_t b, bool leader, uint32_t* seen) {
+// Accept tests and first-rejection scan of sequence b by one wave (lane l takes slots start + l, start + l + 64, ...).
+// Every draw task of the sequence computes the same record; the leader also writes the per-row outputs and
+// n_accepted. out_token, flags and the new start are written once, by the sequence's last draw task.
+__device__ __forceinline__ Job seq_scan(DP& prm, int64_t b, bool leader, uint32_t* seen) {
   const int lane = threadIdx.x & 63;
   const int G = prm.G;
   const int32_t* ord = prm.order ? prm.order + b * G : nullptr;
@@ -434,13 +626,25 @@ __device__ Job seq_scan(const DenseParams& prm, int64_t b, bool leader, uint32_t
   bad = __any(bad);
   const bool done = !bad && st == G;
   int bad_id = 0, nf = 0, qz = 0, kmin = G;
-  if (!bad && !done) {
-    for (int s = st + lane; s < G; s += 64) {
-      const SlotEval e = eval_slot(prm, b, ord ? ord[s] : s);
-      bad_id |= e.bad_id;
-      nf |= e.nonfinite;
-      qz |= e.qzero;
-      if (!e.acc) kmin = min(kmin, s);
+  RowPair krs{};                                   // statistics of this lane's first rejected slot
+  int32_t kx = 0;
+  float ku = 0.f;
+  const float u_bonus = prm.us[b * (G + 1) + G];
+  // Every slot is evaluated, whatever start is, so that all loads go out together; slots before start (whose rows
+  // were not read) and every slot of a sequence with a bad order or start are then ignored.
+  for (int s = lane; s < G; s += 64) {
+    int r = ord ? ord[s] : s;
+    r = (r >= 0 && r < G) ? r : 0;                 // addresses stay in range under an invalid order
+    const SlotEval e = eval_slot(prm, b, r);
+    if (bad || done || s < st) continue;
+    bad_id |= e.bad_id;
+    nf |= e.nonfinite;
+    qz |= e.qzero;
+    if (!e.acc && kmin == G) { kmin = s; krs = e.rs; kx = e.x; ku = e.us; }
+    if (leader) {
+      if (prm.accept) prm.accept[b * G + r] = e.acc ? 1 : 0;
+      if (prm.p_draft) prm.p_draft[b * G + r] = e.P;
+      if (prm.q_draft) prm.q_draft[b * G + r] = e.Q;
     }
   }
   bad_id = __any(bad_id);
@@ -454,139 +658,73 @@ __device__ Job seq_scan(const DenseParams& prm, int64_t b, bool leader, uint32_t
   Job job{};
   job.kind = JOB_NONE;
   job.new_start = -1;
+  job.flags = flg;
   if (!fatal && !done) {
     job.new_start = min(G, k + 1);
     if (k < G) {
-      const int r = ord ? ord[k] : k;
+      const int kl = k & 63;                       // the lane that evaluated slot k
       job.kind = prm.dft ? JOB_RESID : JOB_ONEHOT;
-      job.row = r;
-      job.d = prm.ids[b * G + r];
-      job.u = prm.us[b * (G + 1) + r];
-      double S_t, S_d = 1.0;
-      float zx;
-      row_stats(prm.part1 + (b * G + r) * prm.nseg1, prm.nseg1, double(prm.c), job.m_t, S_t, zx);
-      if (prm.dft) row_stats(prm.part1 + ((prm.B + b) * G + r) * prm.nseg1, prm.nseg1, double(prm.c), job.m_d, S_d, zx);
+      job.row = ord ? ord[k] : k;
+      job.d = __builtin_amdgcn_readlane(kx, kl);
+      job.u = readlane_f(ku, kl);
+      job.m_t = readlane_f(krs.mt, kl);
+      job.m_d = readlane_f(krs.md, kl);
+      const double S_t = readlane_d(krs.St, kl), S_d = prm.dft ? readlane_d(krs.Sd, kl) : 1.0;
       job.kappa = S_d / S_t;
     } else if (prm.bonus) {
       job.kind = JOB_BONUS;
       job.row = G;
-      job.u = prm.us[b * (G + 1) + G];
+      job.u = u_bonus;
     }
   }
   if (leader) {
+    if (fatal) __builtin_amdgcn_s_waitcnt(0);       // the per-slot stores above land before they are overwritten
+    // rows not verified (before start, or every row when nothing is left), and every row of a failed sequence
     for (int s = lane; s < G; s += 64) {
+      if (!(fatal || done || s < st)) continue;
       const int r = ord && !bad ? ord[s] : s;
-      uint8_t a = 0;
-      float P = 0.f, Q = 0.f;
-      if (fatal) {
-        P = Q = NAN;
-      } else if (!done && s >= st) {
-        const SlotEval e = eval_slot(prm, b, r);
-        a = e.acc ? 1 : 0;
-        P = e.P;
-        Q = e.Q;
-      }
-      if (prm.accept) prm.accept[b * G + r] = a;
-      if (prm.p_draft) prm.p_draft[b * G + r] = P;
-      if (prm.q_draft) prm.q_draft[b * G + r] = Q;
+      const float pq = fatal ? NAN : 0.f;
+      if (prm.accept) prm.accept[b * G + r] = 0;
+      if (prm.p_draft) prm.p_draft[b * G + r] = pq;
+      if (prm.q_draft) prm.q_draft[b * G + r] = pq;
     }
-    if (lane == 0) {
-      prm.n_acc[b] = fatal ? -1 : (done ? 0 : k - st);
-      prm.token[b] = -1;
-      if (prm.flags) prm.flags[b] = flg;
-      prm.jobs[b] = job;
-    }
+    if (lane == 0) prm.n_acc[b] = fatal ? -1 : (done ? 0 : k - st);
   }
   return job;
 }
 
-// exp(x) in float64 by Tang's table-driven method (P. T. P. Tang, "Table-driven implementation of the exponential
-// function in IEEE floating-point arithmetic", ACM TOMS 15(2), 1989): x = (64 e + j) ln2/64 + r with |r| <= ln2/128,
-// exp(x) = 2^e * 2^(j/64) * (1 + expm1(r)), expm1(r) by its degree-5 Taylor polynomial (truncation < 4e-17).
-// kExp2Tab[j] = 2^(j/64) correctly rounded; each workgroup copies it to LDS for the per-lane lookups.
-__constant__ double kExp2Tab[64] = {
-    0x1.0000000000000p+0, 0x1.02c9a3e778061p+0, 0x1.059b0d3158574p+0, 0x1.0874518759bc8p+0,
-    0x1.0b5586cf9890fp+0, 0x1.0e3ec32d3d1a2p+0, 0x1.11301d0125b51p+0, 0x1.1429aaea92de0p+0,
-    0x1.172b83c7d517bp+0, 0x1.1a35beb6fcb75p+0, 0x1.1d4873168b9aap+0, 0x1.2063b88628cd6p+0,
-    0x1.2387a6e756238p+0, 0x1.26b4565e27cddp+0, 0x1.29e9df51fdee1p+0, 0x1.2d285a6e4030bp+0,
-    0x1.306fe0a31b715p+0, 0x1.33c08b26416ffp+0, 0x1.371a7373aa9cbp+0, 0x1.3a7db34e59ff7p+0,
-    0x1.3dea64c123422p+0, 0x1.4160a21f72e2ap+0, 0x1.44e086061892dp+0, 0x1.486a2b5c13cd0p+0,
-    0x1.4bfdad5362a27p+0, 0x1.4f9b2769d2ca7p+0, 0x1.5342b569d4f82p+0, 0x1.56f4736b527dap+0,
-    0x1.5ab07dd485429p+0, 0x1.5e76f15ad2148p+0, 0x1.6247eb03a5585p+0, 0x1.6623882552225p+0,
-    0x1.6a09e667f3bcdp+0, 0x1.6dfb23c651a2fp+0, 0x1.71f75e8ec5f74p+0, 0x1.75feb564267c9p+0,
-    0x1.7a11473eb0187p+0, 0x1.7e2f336cf4e62p+0, 0x1.82589994cce13p+0, 0x1.868d99b4492edp+0,
-    0x1.8ace5422aa0dbp+0, 0x1.8f1ae99157736p+0, 0x1.93737b0cdc5e5p+0, 0x1.97d829fde4e50p+0,
-    0x1.9c49182a3f090p+0, 0x1.a0c667b5de565p+0, 0x1.a5503b23e255dp+0, 0x1.a9e6b5579fdbfp+0,
-    0x1.ae89f995ad3adp+0, 0x1.b33a2b84f15fbp+0, 0x1.b7f76f2fb5e47p+0, 0x1.bcc1e904bc1d2p+0,
-    0x1.c199bdd85529cp+0, 0x1.c67f12e57d14bp+0, 0x1.cb720dcef9069p+0, 0x1.d072d4a07897cp+0,
-    0x1.d5818dcfba487p+0, 0x1.da9e603db3285p+0, 0x1.dfc97337b9b5fp+0, 0x1.e502ee78b3ff6p+0,
-    0x1.ea4afa2a490dap+0, 0x1.efa1bee615a27p+0, 0x1.f50765b6e4540p+0, 0x1.fa7c1819e90d8p+0,
-};
+// 2^y in float64, table-driven in the manner of Tang's exponential (P. T. P. Tang, ACM TOMS 15(2), 1989): y is
+// rounded to a multiple of 1/256, n = 256 k + j; 2^(j/256) comes from a 256-entry table in LDS, 2^f for the remainder
+// |f| <= 1/512 from its degree-4 Taylor polynomial (truncation below 4e-17 relative) and 2^k is applied exactly with
+// ldexp. Every workgroup that draws fills the table first (one entry per thread).
+__shared__ double s_exp2tab[256];
 
-__device__ __forceinline__ void exp_table_init(double* tab) {
-  if (threadIdx.x < 64) tab[threadIdx.x] = kExp2Tab[threadIdx.x];
-  __syncthreads();
+// The core assumes a finite y >= -1020.
+__device__ __forceinline__ double fexp_core(double y) {
+  const double kMagic = 26388279066624.0;                      // 1.5 * 2^44: its ulp is 1/256
+  const double t = y + kMagic;
+  const int n = int(__double2loint(t));                        // round(256 y), two's complement in the low bits
+  const double f = y - (t - kMagic);                           // y - n / 256, exact, |f| <= 1/512
+  double q = fma(0x1.3b2ab6fba4e77p-7, f, 0x1.c6b08d704a0c0p-5);  // ln2^4/24, ln2^3/6
+  q = fma(q, f, 0x1.ebfbdff82c58fp-3);                         // ln2^2/2
+  q = fma(q, f, 0x1.62e42fefa39efp-1);                         // ln2
+  q = fma(q, f, 1.0);
+  return ldexp(s_exp2tab[n & 255] * q, n >> 8);
 }
 
-// exp(d * invT) for d = z - max <= 0. kC = invT * 64/ln2. The nearest integer k of d * kC comes from adding
-// 1.5 * 2^52 (its low mantissa bits then hold k); r = d * invT - k * ln2/64 is formed with one rounding because
-// k * L1 is exact (L1 keeps 36 bits, |k| < 2^17). Inputs at or below -746 (after scaling), -inf and NaN are
-// evaluated on garbage and replaced at the end by 0 (NaN stays NaN).
-struct ExpArg {
-  double invT, kC;
-};
-
-// Core of the evaluation, valid for finite d with d * invT >= -745 (no special-value handling).
-__device__ __forceinline__ double fexp_core(double d, const ExpArg& ea, const double* tab) {
-  const double kMagic = 6755399441055744.0;                     // 1.5 * 2^52
-  const double y = fma(d, ea.kC, kMagic);
-  const int k = int(__double2loint(y));
-  const double kd = y - kMagic;
-  double r = fma(d, ea.invT, -kd * 0x1.62e42fefa0000p-7);
-  r = fma(-kd, 0x1.cf79abc9e3b3ap-46, r);
-  double q = fma(r, 1.0 / 120.0, 1.0 / 24.0);
-  q = fma(q, r, 1.0 / 6.0);
-  q = fma(q, r, 0.5);
-  q = fma(q, r, 1.0);
-  const double em1 = q * r;
-  const double t = tab[k & 63];
-  return ldexp(fma(t, em1, t), k >> 6);
+// Any y: below the range (y < -1074), -inf and NaN are evaluated on garbage and replaced by 0 (NaN stays NaN).
+__device__ __forceinline__ double fexp_scaled(double y) {
+  const double res = fexp_core(y >= -1074.0 ? y : 0.0);
+  return (y >= -1074.0) ? res : (y != y ? y : 0.0);
 }
 
-__device__ __forceinline__ double fexp_scaled(double d, const ExpArg& ea, const double* tab) {
-  const double kMagic = 6755399441055744.0;                     // 1.5 * 2^52
-  const double y = fma(d, ea.kC, kMagic);
-  const int k = int(__double2loint(y));
-  const double kd = y - kMagic;
-  double r = fma(d, ea.invT, -kd * 0x1.62e42fefa0000p-7);       // ln2/64, leading 36 bits (product exact)
-  r = fma(-kd, 0x1.cf79abc9e3b3ap-46, r);                       // ln2/64, remainder
-  double q = fma(r, 1.0 / 120.0, 1.0 / 24.0);
-  q = fma(q, r, 1.0 / 6.0);
-  q = fma(q, r, 0.5);
-  q = fma(q, r, 1.0);
-  const double em1 = q * r;
-  const double t = tab[k & 63];
-  const double res = ldexp(fma(t, em1, t), k >> 6);
-  const double x = d * ea.invT;
-  return (x >= -746.0) ? res : (x != x ? x : 0.0);
-}
-
-__device__ __forceinline__ double wave_sum(double v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
-__device__ __forceinline__ double wave_incl_scan(double v, int lane) {
-  for (int o = 1; o < 64; o <<= 1) {
-    const double n = __shfl_up(v, o);
-    if (lane >= o) v += n;
-  }
-  return v;
-}
+// The exponent (z - m) * log2(e) / T of an element, formed as z * c2 + nm with one rounding, nm = -(m * c2). Every
+// evaluation of an element's weight goes through here, so repeated evaluations agree bit for bit.
+__device__ __forceinline__ double xarg(float z, double c2, double nm) { return fma(double(z), c2, nm); }
 
 template <int BLOCK>
 __device__ __forceinline__ double block_max_d(double v, double* sh) {
-  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o));
+  v = wave_max_d(v);
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   __syncthreads();
   if (l == 0) sh[w] = v;
@@ -601,7 +739,7 @@ __device__ __forceinline__ double block_max_d(double v, double* sh) {
 template <int BLOCK>
 __device__ __forceinline__ double block_excl_scan(double v, double* sh, double& total) {
   const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const double incl = wave_incl_scan(v, l);
+  const double incl = wave_incl_scan(v);
   __syncthreads();
   if (l == 63) sh[w] = incl;
   __syncthreads();
@@ -615,38 +753,38 @@ __device__ __forceinline__ double block_excl_scan(double v, double* sh, double& 
   return base + incl - v;
 }
 
-// 16 consecutive logits starting at element i0 of a row, as float; -inf past the end of the row.
+// kPer consecutive logits starting at element i0 of a row, as float; -inf past the end of the row.
 template <typename T>
-__device__ __forceinline__ void load16(const T* row, int64_t i0, int64_t V, bool vec, float* z) {
+__device__ __forceinline__ void load_lane(const T* row, int64_t i0, int64_t V, bool vec, float* z) {
   if (vec && i0 + kPer <= V) {
     const uint4* p = reinterpret_cast<const uint4*>(row + i0);
     constexpr int NV = kPer / Vec<T>::kEPV;
 #pragma unroll
-    for (int k = 0; k < NV; ++k) Vec<T>::unpack(p[k], z + k * Vec<T>::kEPV);
+    for (int k = 0; k < NV; ++k) Vec<T>::unpack(gload4(p + k), z + k * Vec<T>::kEPV);
   } else {
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) z[e] = (i0 + e < V) ? Vec<T>::load1(row + i0 + e) : -INFINITY;
+    for (int e = 0; e < kPer; ++e) z[e] = elem_or_ninf<T>(row, i0 + e, V);
   }
 }
 
-// Exact draw weights of the lane's 16 elements of chunk c (relative to the common reference max mt): the residual
+// Exact draw weights of the lane's kPer elements of chunk c (relative to the common reference max mt): the residual
 // max(p_i - q_i, 0), or p_i when use_p. Compiled without contraction so repeated evaluations agree bit for bit.
 template <typename T>
 __device__ __forceinline__ void chunk_weights(const Job& job, const T* rt, const T* rd, bool vec, int64_t c, int lane,
                                               int64_t V, double mt, double inv_st, double md, double inv_sd,
-                                              double invT, bool use_p, const double* tab, double* w) {
+                                              double c2, bool use_p, double* w) {
 #pragma clang fp contract(off)
   const int64_t i0 = c * kChunk + int64_t(lane) * kPer;
   float zt[kPer], zd[kPer];
-  load16<T>(rt, i0, V, vec, zt);
+  load_lane<T>(rt, i0, V, vec, zt);
   const bool resid = job.kind == JOB_RESID && !use_p;
-  if (resid) load16<T>(rd, i0, V, vec, zd);
-  const ExpArg ea{invT, invT * 92.332482616893656};
+  if (resid) load_lane<T>(rd, i0, V, vec, zd);
+  const double nmt = -(mt * c2), nmd = -(md * c2);
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
-    const double p = fexp_scaled(double(zt[e]) - mt, ea, tab) * inv_st;
+    const double p = fexp_scaled(xarg(zt[e], c2, nmt)) * inv_st;
     double q = 0.0;
-    if (resid) q = fexp_scaled(double(zd[e]) - md, ea, tab) * inv_sd;
+    if (resid) q = fexp_scaled(xarg(zd[e], c2, nmd)) * inv_sd;
     else if (!use_p && job.kind == JOB_ONEHOT) q = (i0 + e == job.d) ? 1.0 : 0.0;
     const double r = use_p ? p : p - q;
     w[e] = r > 0.0 ? r : 0.0;
@@ -667,202 +805,290 @@ constexpr int kAmbMax = 4;
 struct alignas(16) ChunkRec {
   double A, D;
   int32_t n_amb, pad0;
-  double pad1;
+  double mref;                       // the max the exps are taken against (for a bonus row: the task's max)
   double et[kAmbMax], ed[kAmbMax];
 };
 
+__device__ __forceinline__ double4 ld_task(const double4* p) {
+  const double* d = reinterpret_cast<const double*>(p);
+  return make_double4(ld_dev(d), ld_dev(d + 1), ld_dev(d + 2), ld_dev(d + 3));
+}
+__device__ __forceinline__ void st_task(double4* p, double4 v) {
+  double* d = reinterpret_cast<double*>(p);
+  st_dev(d, v.x);
+  st_dev(d + 1, v.y);
+  st_dev(d + 2, v.z);
+  st_dev(d + 3, v.w);
+}
+
 // Elements of the lane: all finite and within exp's range of the reference max (so the guard-free core applies).
-__device__ __forceinline__ bool lane_safe(const float* z, double m, double invT) {
+__device__ __forceinline__ bool lane_safe(const float* z, double m, double c2) {
   float lo = z[0], hi = z[0];
 #pragma unroll
   for (int e = 1; e < kPer; ++e) { lo = fminf(lo, z[e]); hi = fmaxf(hi, z[e]); }
   // NaN makes both comparisons false; +inf fails the upper bound check; -inf fails the lower one
-  return (double(lo) - m) * invT >= -740.0 && double(hi) <= m && hi == hi && lo == lo;
+  return (double(lo) - m) * c2 >= -1020.0 && double(hi) <= m && hi == hi && lo == lo;
 }
 
-// One lane's 16 elements: exp of both logits, the residual's sign test and the sums.
+// One lane's kPer elements: exp of both logits, the residual's sign test and the sums. A and D are accumulated as
+// fma(e, w, .) with w = 1 where the residual is positive and 0 elsewhere.
 template <int KIND, bool SAFE>
-__device__ __forceinline__ void mass_lane(const float* zt, const float* zd, double mt, double md, int64_t i0, int32_t d,
-                                          const ExpArg& ea, const double* tab, double k_lo, double k_hi, double& st,
-                                          double& sd, double& A, double& D, uint32_t& amb) {
+__device__ __forceinline__ void mass_lane(const float* zt, const float* zd, double c2, double nmt, double nmd,
+                                          int64_t i0, int32_t d, double k_lo, double k_hi, double& st, double& sd,
+                                          double& A, double& D, uint32_t& amb) {
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
-    const double et = SAFE ? fexp_core(double(zt[e]) - mt, ea, tab) : fexp_scaled(double(zt[e]) - mt, ea, tab);
+    const double xt = xarg(zt[e], c2, nmt);
+    const double et = SAFE ? fexp_core(xt) : fexp_scaled(xt);
     st += et;
     if constexpr (KIND == JOB_RESID) {
-      const double ed = SAFE ? fexp_core(double(zd[e]) - md, ea, tab) : fexp_scaled(double(zd[e]) - md, ea, tab);
+      const double xd = xarg(zd[e], c2, nmd);
+      const double ed = SAFE ? fexp_core(xd) : fexp_scaled(xd);
       sd += ed;
       // r_e > 0 iff et * (S_d / S_t) > ed; kappa brackets S_d / S_t within kBand
       const bool pos = et * k_lo > ed;
       const bool neg = et * k_hi <= ed;
-      A += pos ? et : 0.0;
-      D += pos ? ed : 0.0;
+      const double w = pos ? 1.0 : 0.0;
+      A = fma(et, w, A);
+      D = fma(ed, w, D);
       amb |= (!(pos || neg) ? 1u : 0u) << e;
     } else if constexpr (KIND == JOB_ONEHOT) {
-      A += (i0 + e == d) ? 0.0 : et;
-    } else {
-      A += et;
+      A = fma(et, (i0 + e == d) ? 0.0 : 1.0, A);
     }
   }
 }
 
-// Chunk loop of the mass pass for one kind of draw (KIND is uniform per sequence).
-template <typename T, int KIND>
-__device__ __forceinline__ void mass_chunks(const DenseParams& prm, const Job& job, int64_t b, int64_t c0, int64_t c1,
-                                            const T* rt, const T* rd, bool vec, double mt, const double* tab,
-                                            double& st, double& sd) {
-  const int lane = threadIdx.x;
-  const int64_t V = prm.V;
-  const double md = job.m_d;
-  const ExpArg ea{prm.invT, prm.invT * 92.332482616893656};
-  const double k_lo = job.kappa * (1.0 - kBand), k_hi = job.kappa * (1.0 + kBand);
-  float zt[kPer], zd[kPer];
-  for (int64_t c = c0; c < c1; ++c) {
-    const int64_t i0 = c * kChunk + int64_t(lane) * kPer;
-    load16<T>(rt, i0, V, vec, zt);
-    if constexpr (KIND == JOB_RESID) load16<T>(rd, i0, V, vec, zd);
-    bool safe = i0 + kPer <= V && lane_safe(zt, mt, prm.invT);
-    if constexpr (KIND == JOB_RESID) safe = safe && lane_safe(zd, md, prm.invT);
-    safe = __all(safe);
-    double A = 0.0, D = 0.0;
-    uint32_t amb = 0;                                  // bit e: element e undecided
-    if (safe)
-      mass_lane<KIND, true>(zt, zd, mt, md, i0, job.d, ea, tab, k_lo, k_hi, st, sd, A, D, amb);
-    else
-      mass_lane<KIND, false>(zt, zd, mt, md, i0, job.d, ea, tab, k_lo, k_hi, st, sd, A, D, amb);
-    A = wave_sum(A);
-    if constexpr (KIND == JOB_RESID) D = wave_sum(D);
-    ChunkRec* rec = prm.chunks + b * prm.nch + c;
-    int namb = 0;
-    if constexpr (KIND == JOB_RESID) {
-      if (__any(amb != 0)) {                           // rare: list the undecided elements in element order
-        const int mine = __popc(amb);
-        int before = mine;                             // inclusive prefix over lanes
-        for (int o = 1; o < 64; o <<= 1) {
-          const int n = __shfl_up(before, o);
-          if (lane >= o) before += n;
-        }
-        namb = __shfl(before, 63);
-        int pos = before - mine;
-        for (int e = 0; e < kPer; ++e) {
-          if ((amb >> e) & 1u) {                       // recomputed exactly as in mass_lane
-            if (pos < kAmbMax) {
-              rec->et[pos] = fexp_scaled(double(zt[e]) - mt, ea, tab);
-              rec->ed[pos] = fexp_scaled(double(zd[e]) - md, ea, tab);
-            }
-            ++pos;
+// One chunk of the mass pass, its kPer elements per lane in zt (and zd): the sums, the undecided elements and the
+// chunk's record.
+template <int KIND>
+__device__ __forceinline__ void chunk_body(DP& prm, const Job& job, int64_t b, int64_t c, int64_t i0,
+                                           const float* zt, const float* zd, double mt, double md, double c2,
+                                           double nmt, double nmd, double k_lo, double k_hi, double& st, double& sd) {
+  const int lane = threadIdx.x & 63;
+  bool safe = i0 + kPer <= prm.V && lane_safe(zt, mt, c2);
+  if constexpr (KIND == JOB_RESID) safe = safe && lane_safe(zd, md, c2);
+  safe = __all(safe);
+  double A = 0.0, D = 0.0, cst = 0.0, csd = 0.0;     // this chunk's sums
+  uint32_t amb = 0;                                  // bit e: element e undecided
+  if (safe)
+    mass_lane<KIND, true>(zt, zd, c2, nmt, nmd, i0, job.d, k_lo, k_hi, cst, csd, A, D, amb);
+  else
+    mass_lane<KIND, false>(zt, zd, c2, nmt, nmd, i0, job.d, k_lo, k_hi, cst, csd, A, D, amb);
+  st += cst;
+  sd += csd;
+  if constexpr (KIND == JOB_BONUS) A = cst;          // the bonus draws from p: the chunk's whole sum
+  A = wave_sum(A);
+  if constexpr (KIND == JOB_RESID) D = wave_sum(D);
+  ChunkRec* rec = prm.chunks + b * prm.nch + c;
+  int namb = 0;
+  if constexpr (KIND == JOB_RESID) {
+    if (__any(amb != 0)) {                           // rare: list the undecided elements in element order
+      const int mine = __popc(amb);
+      int before = mine;                             // inclusive prefix over lanes
+      for (int o = 1; o < 64; o <<= 1) {
+        const int n = __shfl_up(before, o);
+        if (lane >= o) before += n;
+      }
+      namb = __shfl(before, 63);
+      int pos = before - mine;
+      for (int e = 0; e < kPer; ++e) {
+        if ((amb >> e) & 1u) {                       // recomputed exactly as in mass_lane
+          if (pos < kAmbMax) {
+            st_dev(&rec->et[pos], fexp_scaled(xarg(zt[e], c2, nmt)));
+            st_dev(&rec->ed[pos], fexp_scaled(xarg(zd[e], c2, nmd)));
           }
+          ++pos;
         }
       }
     }
-    if (lane == 0) {
-      rec->A = A;
-      rec->D = D;
-      rec->n_amb = namb;
-    }
+  }
+  if (lane == 0) {
+    st_dev(&rec->A, A);
+    st_dev(&rec->D, D);
+    st_dev(&rec->n_amb, namb);
+    st_dev(&rec->mref, mt);
   }
 }
 
-// One wave per workgroup; each workgroup handles cpw consecutive chunks of one sequence's draw row(s), after the
-// sequence's scan.
-template <typename T>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_draw_mass(DenseParams prm) {
-  __shared__ double tab[64];
-  __shared__ uint32_t seen[SV_MAX_GAMMA / 32];
-  const int seg = int(blockIdx.x % prm.nseg2);
-  const int64_t b = blockIdx.x / prm.nseg2;
-  exp_table_init(tab);
-  const Job job = seq_scan(prm, b, seg == 0, seen);
-  if (job.kind == JOB_NONE) return;
-  const int lane = threadIdx.x;
+// Chunk loop of the mass pass for one kind of draw (KIND is uniform per sequence): chunks c0, c0 + stride, ... below
+// c1. Chunks that lie wholly inside a 16-byte aligned row take the vector loop, with the next chunk's loads in flight
+// while the current one is evaluated; a partial last chunk, or a row off the 16-byte grid, takes element loads.
+template <typename T, int KIND>
+__device__ __forceinline__ void mass_chunks(DP& prm, const Job& job, int64_t b, int64_t c0, int64_t c1,
+                                            int stride, const T* rt, const T* rd, bool vec, double mt,
+                                            double& st, double& sd) {
+  constexpr int NV = kPer / Vec<T>::kEPV;
+  const int lane = threadIdx.x & 63;
   const int64_t V = prm.V;
-  const int64_t c0 = int64_t(seg) * prm.cpw, c1 = min<int64_t>(prm.nch, c0 + prm.cpw);
-  const T* rt = static_cast<const T*>(prm.tgt) + b * prm.t_seq + int64_t(job.row) * prm.t_row;
-  const bool resid = job.kind == JOB_RESID;
-  const T* rd = resid ? static_cast<const T*>(prm.dft) + b * prm.d_seq + int64_t(job.row) * prm.d_row : nullptr;
-  const bool vec = (reinterpret_cast<uintptr_t>(rt) & 15u) == 0 &&
-                   (!resid || (reinterpret_cast<uintptr_t>(rd) & 15u) == 0);
-
-  double mt = job.m_t;
-  int has_nan = 0;
-  if (job.kind == JOB_BONUS) {            // the bonus row was not in the statistics pass: this segment's max
-    float zt[kPer];
-    float m = -INFINITY;
-    for (int64_t c = c0; c < c1; ++c) {
-      load16<T>(rt, c * kChunk + int64_t(lane) * kPer, V, vec, zt);
+  const double md = job.m_d;
+  const double c2 = prm.c2;
+  const double nmt = -(mt * c2), nmd = -(md * c2);
+  const double k_lo = job.kappa * (1.0 - kBand), k_hi = job.kappa * (1.0 + kBand);
+  const int64_t step = int64_t(stride) * kChunk;
+  float zt[kPer], zd[kPer];
+  const int64_t c_vec = vec ? min<int64_t>(c1, V / kChunk) : c0;   // chunks below V / kChunk are whole
+  int64_t c = c0;
+  int64_t i0 = c0 * kChunk + int64_t(lane) * kPer;
+  if (c < c_vec) {
+    uint4 nt[NV], nd[NV];                            // the chunk in flight
+    const uint4* pt = reinterpret_cast<const uint4*>(rt + i0);
+    const uint4* pd = KIND == JOB_RESID ? reinterpret_cast<const uint4*>(rd + i0) : nullptr;
+    const int64_t vstep = step / Vec<T>::kEPV;       // in 16-byte vectors
 #pragma unroll
-      for (int e = 0; e < kPer; ++e) { m = fmaxf(m, zt[e]); has_nan |= (zt[e] != zt[e]); }
+    for (int k = 0; k < NV; ++k) nt[k] = gload4(pt + k);
+    if constexpr (KIND == JOB_RESID) {
+#pragma unroll
+      for (int k = 0; k < NV; ++k) nd[k] = gload4(pd + k);
     }
-    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    mt = m;
-    has_nan = __any(has_nan);
-  }
-  double st = 0.0, sd = 0.0;
-  if (mt == -INFINITY) {                  // a segment of -inf only (bonus row): no mass
-    for (int64_t c = c0 + lane; c < c1; c += 64) {
-      prm.chunks[b * prm.nch + c].A = 0.0;
-      prm.chunks[b * prm.nch + c].D = 0.0;
-      prm.chunks[b * prm.nch + c].n_amb = 0;
+    for (; c < c_vec; c += stride, i0 += step, pt += vstep) {
+#pragma unroll
+      for (int k = 0; k < NV; ++k) Vec<T>::unpack(nt[k], zt + k * Vec<T>::kEPV);
+      if constexpr (KIND == JOB_RESID) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) Vec<T>::unpack(nd[k], zd + k * Vec<T>::kEPV);
+      }
+      if (c + stride < c_vec) {                      // next chunk's loads overlap this chunk's arithmetic
+#pragma unroll
+        for (int k = 0; k < NV; ++k) nt[k] = gload4(pt + vstep + k);
+        if constexpr (KIND == JOB_RESID) {
+#pragma unroll
+          for (int k = 0; k < NV; ++k) nd[k] = gload4(pd + vstep + k);
+        }
+      }
+      if constexpr (KIND == JOB_RESID) pd += vstep;
+      chunk_body<KIND>(prm, job, b, c, i0, zt, zd, mt, md, c2, nmt, nmd, k_lo, k_hi, st, sd);
     }
-  } else if (job.kind == JOB_RESID) {
-    mass_chunks<T, JOB_RESID>(prm, job, b, c0, c1, rt, rd, vec, mt, tab, st, sd);
-  } else if (job.kind == JOB_ONEHOT) {
-    mass_chunks<T, JOB_ONEHOT>(prm, job, b, c0, c1, rt, rd, vec, mt, tab, st, sd);
-  } else {
-    mass_chunks<T, JOB_BONUS>(prm, job, b, c0, c1, rt, rd, vec, mt, tab, st, sd);
   }
-  st = wave_sum(st);
-  if (resid) sd = wave_sum(sd);
-  if (lane == 0) prm.part2a[b * prm.nseg2 + seg] = make_double4(mt, has_nan ? NAN : st, job.m_d, sd);
+  for (; c < c1; c += stride, i0 += step) {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) zt[e] = elem_or_ninf<T>(rt, i0 + e, V);
+    if constexpr (KIND == JOB_RESID) {
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) zd[e] = elem_or_ninf<T>(rd, i0 + e, V);
+    }
+    chunk_body<KIND>(prm, job, b, c, i0, zt, zd, mt, md, c2, nmt, nmd, k_lo, k_hi, st, sd);
+  }
 }
 
-template <typename T, int BLOCK>
-__global__ __launch_bounds__(BLOCK) void k_draw_pick(DenseParams prm) {
-  constexpr int NW = BLOCK / 64;
-  __shared__ double tab[64];
-  __shared__ double sh_d[NW];
-  __shared__ double s_mass[kTile];
-  __shared__ int s_amb[kTile];
-  __shared__ int s_namb, s_cand, s_last;
-  __shared__ double s_base;
-  const int64_t b = blockIdx.x;
-  const Job job = prm.jobs[b];
-  if (prm.start && job.new_start >= 0 && threadIdx.x == 0) prm.start[b] = job.new_start;
-  if (job.kind == JOB_NONE) return;
-  exp_table_init(tab);
+// Draw weights of the kPT consecutive elements of chunk c that thread tid holds in the search (elements
+// kPT * tid .. kPT * tid + kPT - 1), evaluated exactly as chunk_weights does. Every load is issued before the first
+// weight is formed.
+constexpr int kPT = kChunk / kDrawBlock;
+template <typename T>
+__device__ __forceinline__ void chunk_weights_t(const Job& job, const T* rt, const T* rd, int64_t c, int tid, int64_t V,
+                                                double mt, double inv_st, double md, double inv_sd, double c2,
+                                                bool use_p, double* w) {
+#pragma clang fp contract(off)
+  const int64_t i0 = c * kChunk + int64_t(tid) * kPT;
+  const bool resid = job.kind == JOB_RESID && !use_p;
+  const double nmt = -(mt * c2), nmd = -(md * c2);
+  float zt[kPT], zd[kPT];
+#pragma unroll
+  for (int e = 0; e < kPT; ++e) zt[e] = elem_or_ninf<T>(rt, i0 + e, V);
+  if (resid) {
+#pragma unroll
+    for (int e = 0; e < kPT; ++e) zd[e] = elem_or_ninf<T>(rd, i0 + e, V);
+  }
+#pragma unroll
+  for (int e = 0; e < kPT; ++e) {
+    const int64_t i = i0 + e;
+    const double p = fexp_scaled(xarg(zt[e], c2, nmt)) * inv_st;
+    double q = 0.0;
+    if (resid) {
+      q = fexp_scaled(xarg(zd[e], c2, nmd)) * inv_sd;
+    } else if (!use_p && job.kind == JOB_ONEHOT) {
+      q = (i == job.d) ? 1.0 : 0.0;
+    }
+    const double r = use_p ? p : p - q;
+    w[e] = r > 0.0 ? r : 0.0;
+  }
+}
+
+struct PickShared {
+  double mass[kTile];
+  int amb[kTile];
+  double red[kDrawWaves];
+  double base;
+  int namb, cand, last, hit, lastpos;
+};
+
+// The sequence's drawn token and flags (the scan's bits plus what the draw adds), written once.
+__device__ __forceinline__ void finish(DP& prm, int64_t b, const Job& job, int32_t tok, uint32_t extra) {
+  prm.token[b] = tok;
+  if (prm.flags) prm.flags[b] = job.flags | extra;
+}
+
+// The exact search inside chunk cstar by the whole workgroup (thread tid holds kPT consecutive elements): the first
+// element whose running sum from cbase exceeds t, else (clamp, or rounding) the chunk's last element with weight.
+template <typename T>
+__device__ void search_chunk(DP& prm, int64_t b, const Job& job, int64_t cstar, double cbase, bool clamp,
+                             double t, double mt, double inv_st, double md, double inv_sd, bool use_p, PickShared& sh) {
+  constexpr int BLOCK = kDrawBlock;
+  const int tid = threadIdx.x;
+  const bool resid = job.kind == JOB_RESID;
+  const T* rt = static_cast<const T*>(prm.tgt) + b * prm.t_seq + int64_t(job.row) * prm.t_row;
+  const T* rd = resid ? static_cast<const T*>(prm.dft) + b * prm.d_seq + int64_t(job.row) * prm.d_row : nullptr;
+  if (tid == 0) { sh.hit = INT_MAX; sh.lastpos = -1; }
+  double w[kPT];
+  chunk_weights_t<T>(job, rt, rd, cstar, tid, prm.V, mt, inv_st, md, inv_sd, prm.c2, use_p, w);
+  double mine = 0.0;
+#pragma unroll
+  for (int e = 0; e < kPT; ++e) mine += w[e];
+  double tot;
+  double acc = cbase + block_excl_scan<BLOCK>(mine, sh.red, tot);
+  int hit = INT_MAX, lastpos = -1;
+#pragma unroll
+  for (int e = 0; e < kPT; ++e) {
+    acc += w[e];
+    if (w[e] > 0.0) lastpos = tid * kPT + e;
+    if (hit == INT_MAX && !clamp && w[e] > 0.0 && acc > t) hit = tid * kPT + e;
+  }
+  if (hit != INT_MAX) atomicMin(&sh.hit, hit);
+  if (lastpos >= 0) atomicMax(&sh.lastpos, lastpos);
+  __syncthreads();
+  if (tid == 0) {
+    const int e = sh.hit != INT_MAX ? sh.hit : sh.lastpos;
+    finish(prm, b, job, e >= 0 ? int32_t(cstar * kChunk + e) : -1, use_p ? SV_FLAG_EMPTY_RESIDUAL : 0u);
+  }
+}
+
+// The pick of sequence b by one workgroup, after every task of the sequence has finished: normalisers from the task
+// partials, chunk masses, their running sum, the chunk that holds t = u * total, and an exact search inside it.
+template <typename T>
+__device__ __noinline__ void pick_seq(DP& prm_arg, int64_t b, const Job& job, PickShared& sh) {
+  DP& prm = uniform_params(prm_arg);
+  constexpr int BLOCK = kDrawBlock, NW = kDrawWaves;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nseg = prm.nseg2;
+  const int ntask = prm.ntask;
   const int64_t nch = prm.nch, V = prm.V;
   const ChunkRec* ch = prm.chunks + b * nch;
   double* mg = prm.masses + b * nch;
-  const double4* ps = prm.part2a + b * nseg;
-  const double invT = prm.invT;
+  const double4* ps = prm.part2 + b * ntask;
+  const double c2 = prm.c2;
   const bool resid = job.kind == JOB_RESID, bonus = job.kind == JOB_BONUS;
-  const ExpArg eaP{invT, invT * 92.332482616893656};
 
-  // normalisers from the segment partials, combined in a fixed order
+  // normalisers from the task partials, combined in a fixed order
   double lm = -INFINITY;
   int bad = 0;
-  for (int s = tid; s < nseg; s += BLOCK) {
-    const double4 p = ps[s];
+  for (int s = tid; s < ntask; s += BLOCK) {
+    const double4 p = ld_task(ps + s);
     lm = fmax(lm, p.x);
     bad |= isnan(p.y) || isnan(p.w);
   }
-  const double mt = block_max_d<BLOCK>(lm, sh_d);
+  const double mt = block_max_d<BLOCK>(lm, sh.red);
   bad = __syncthreads_or(bad);
   double lst = 0.0, lsd = 0.0;
-  for (int s = tid; s < nseg; s += BLOCK) {
-    const double4 p = ps[s];
-    const double f = (!bonus || p.x == mt) ? 1.0 : (p.x == -INFINITY ? 0.0 : fexp_scaled(p.x - mt, eaP, tab));
+  for (int s = tid; s < ntask; s += BLOCK) {
+    const double4 p = ld_task(ps + s);
+    const double f = (!bonus || p.x == mt) ? 1.0 : (p.x == -INFINITY ? 0.0 : fexp_scaled((p.x - mt) * c2));
     lst += p.y * f;
     lsd += p.w;
   }
-  const double St = block_sum<BLOCK>(lst, sh_d);
-  const double Sd = block_sum<BLOCK>(lsd, sh_d);
+  const double St = block_sum<BLOCK>(lst, sh.red);
+  const double Sd = block_sum<BLOCK>(lsd, sh.red);
   if (bad || !(St > 0.0) || isinf(mt) || (resid && !(Sd > 0.0))) {    // only a bonus row can be bad here
     if (tid == 0) {
-      prm.token[b] = -1;
-      if (prm.flags) prm.flags[b] |= SV_FLAG_NONFINITE;
+      finish(prm, b, job, -1, SV_FLAG_NONFINITE);
     }
     return;
   }
@@ -875,37 +1101,37 @@ __global__ __launch_bounds__(BLOCK) void k_draw_pick(DenseParams prm) {
   const bool one_tile = nch <= kTile;
   double w[kPer];
 
-  // Masses of the chunks of one tile into s_mass (and back to global memory when there are several tiles).
+  // Masses of the chunks of one tile into sh.mass (and to global memory when there are several tiles).
   auto tile_masses = [&](int64_t t0, int n, bool use_p) {
-    if (tid == 0) s_namb = 0;
+    if (tid == 0) sh.namb = 0;
     __syncthreads();
     for (int i = tid; i < n; i += BLOCK) {
       const int64_t c = t0 + i;
       const ChunkRec& rc = ch[c];
-      const int namb = rc.n_amb;
+      const int namb = ld_dev(&rc.n_amb);
       if (use_p || namb > kAmbMax) {
-        s_amb[atomicAdd(&s_namb, 1)] = i;
+        sh.amb[atomicAdd(&sh.namb, 1)] = i;
       } else {
-        const double f = bonus ? fexp_scaled(ps[c / prm.cpw].x - mt, eaP, tab) : 1.0;
-        double m = f * (rc.A * inv_st - rc.D * inv_sd);
+        const double f = bonus ? fexp_scaled((ld_dev(&rc.mref) - mt) * c2) : 1.0;
+        double m = f * (ld_dev(&rc.A) * inv_st - ld_dev(&rc.D) * inv_sd);
         for (int q = 0; q < namb; ++q) {               // undecided elements, exactly: max(p - q, 0)
-          const double r = rc.et[q] * inv_st - rc.ed[q] * inv_sd;
+          const double r = ld_dev(&rc.et[q]) * inv_st - ld_dev(&rc.ed[q]) * inv_sd;
           m += r > 0.0 ? r : 0.0;
         }
-        s_mass[i] = m;
+        sh.mass[i] = m;
       }
     }
     __syncthreads();
-    const int namb = s_namb;
+    const int namb = sh.namb;
     for (int q = wave; q < namb; q += NW) {
-      const int i = s_amb[q];
-      chunk_weights<T>(job, rt, rd, vec, t0 + i, lane, V, mt, inv_st, md, inv_sd, invT, use_p, tab, w);
+      const int i = sh.amb[q];
+      chunk_weights<T>(job, rt, rd, vec, t0 + i, lane, V, mt, inv_st, md, inv_sd, c2, use_p, w);
       const double m = wave_sum(lane_sum16(w));
-      if (lane == 0) s_mass[i] = m;
+      if (lane == 0) sh.mass[i] = m;
     }
     __syncthreads();
     if (!one_tile)
-      for (int i = tid; i < n; i += BLOCK) mg[t0 + i] = s_mass[i];
+      for (int i = tid; i < n; i += BLOCK) mg[t0 + i] = sh.mass[i];
   };
   // Running sum over one tile: thread-contiguous ranges, exclusive base per thread, tile total.
   auto tile_scan = [&](int n, double& mine_excl, int& ia, int& ib) {
@@ -913,9 +1139,9 @@ __global__ __launch_bounds__(BLOCK) void k_draw_pick(DenseParams prm) {
     ia = min(n, per * tid);
     ib = min(n, per * (tid + 1));
     double mine = 0.0;
-    for (int i = ia; i < ib; ++i) mine += s_mass[i];
+    for (int i = ia; i < ib; ++i) mine += sh.mass[i];
     double tot;
-    mine_excl = block_excl_scan<BLOCK>(mine, sh_d, tot);
+    mine_excl = block_excl_scan<BLOCK>(mine, sh.red, tot);
     return tot;
   };
 
@@ -935,7 +1161,7 @@ __global__ __launch_bounds__(BLOCK) void k_draw_pick(DenseParams prm) {
   const double t = double(job.u) * total;
 
   // Locate the chunk whose running sum first exceeds t (else the last chunk with mass).
-  if (tid == 0) { s_cand = INT_MAX; s_last = -1; }
+  if (tid == 0) { sh.cand = INT_MAX; sh.last = -1; }
   __syncthreads();
   double run = 0.0;
   for (int64_t t0 = 0; t0 < nch; t0 += kTile) {
@@ -944,7 +1170,7 @@ __global__ __launch_bounds__(BLOCK) void k_draw_pick(DenseParams prm) {
     if (!one_tile) {
       __threadfence_block();
       __syncthreads();
-      for (int i = tid; i < n; i += BLOCK) s_mass[i] = *reinterpret_cast<const volatile double*>(&mg[t0 + i]);
+      for (int i = tid; i < n; i += BLOCK) sh.mass[i] = *reinterpret_cast<const volatile double*>(&mg[t0 + i]);
       __syncthreads();
       tile_total = tile_scan(n, excl, ia, ib);
     }
@@ -952,95 +1178,437 @@ __global__ __launch_bounds__(BLOCK) void k_draw_pick(DenseParams prm) {
     int cand = INT_MAX, last = -1;
     double cbase = 0.0;
     for (int i = ia; i < ib; ++i) {
-      const double m = s_mass[i];
+      const double m = sh.mass[i];
       if (m > 0.0) last = int(t0 + i);
       if (cand == INT_MAX && acc + m > t) { cand = int(t0 + i); cbase = acc; }
       acc += m;
     }
-    atomicMin(&s_cand, cand);
-    atomicMax(&s_last, last);
+    atomicMin(&sh.cand, cand);
+    atomicMax(&sh.last, last);
     __syncthreads();
-    if (cand != INT_MAX && cand == s_cand) s_base = cbase;
+    if (cand != INT_MAX && cand == sh.cand) sh.base = cbase;
     __syncthreads();
-    if (s_cand != INT_MAX) break;
+    if (sh.cand != INT_MAX) break;
     run += tile_total;
   }
-  const bool clamp = s_cand == INT_MAX;
-  const int64_t cstar = clamp ? s_last : s_cand;
-  if (wave != 0) return;
+  const bool clamp = sh.cand == INT_MAX;
+  const int64_t cstar = clamp ? sh.last : sh.cand;
   if (cstar < 0) {
-    if (lane == 0) prm.token[b] = -1;
+    if (tid == 0) finish(prm, b, job, -1, 0u);
     return;
   }
-  // exact search inside the chunk, one wave
-  chunk_weights<T>(job, rt, rd, vec, cstar, lane, V, mt, inv_st, md, inv_sd, invT, use_p, tab, w);
-  const double lsum = lane_sum16(w);
-  const double incl = wave_incl_scan(lsum, lane);
-  double acc = (clamp ? 0.0 : s_base) + (incl - lsum);
-  int hit = -1, lastpos = -1;
+  search_chunk<T>(prm, b, job, cstar, clamp ? 0.0 : sh.base, clamp, t, mt, inv_st, md, inv_sd, use_p, sh);
+}
+
+// The common case of the pick, for rows of at most kLeanChunks chunks whose records need no recomputation: wave 0
+// forms the normalisers and the chunk masses and locates the chunk that holds t with wave-level operations (lane l
+// owns a contiguous run of chunks); the whole workgroup then searches that chunk. Returns false, with nothing
+// written, when the general pick must run instead (an undecided chunk, an empty residual).
+constexpr int kLeanChunks = 512;       // the lean pick: at most 8 chunks per lane, at most 64 tasks
+
+struct LeanShared {
+  double mt, inv_st, inv_sd, t, cbase;
+  int64_t cstar;
+  int clamp, state;                   // state: 0 search, 1 general pick, 2 bad bonus row
+};
+
+
+template <typename T>
+__device__ __forceinline__ bool pick_lean(DP& prm, int64_t b, const Job& job, PickShared& sh, LeanShared& ls) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t nch = prm.nch;
+  const int ntask = prm.ntask;
+  const double c2 = prm.c2;
+  const bool resid = job.kind == JOB_RESID, bonus = job.kind == JOB_BONUS;
+  if (wave == 0) {
+    // One round of loads: lane l's task partial (at most 64 tasks) and the records of its chunks (at most 8).
+    const ChunkRec* ch = prm.chunks + b * nch;
+    const int q = int((nch + 63) / 64);
+    const int64_t ca = min<int64_t>(nch, int64_t(lane) * q), cb = min<int64_t>(nch, ca + q);
+    constexpr int KB = kLeanChunks / 64;
+    int namb[KB];
+    double A[KB], D[KB], mr[KB];
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    acc += w[e];
-    if (w[e] > 0.0) lastpos = e;
-    if (hit < 0 && !clamp && w[e] > 0.0 && acc > t) hit = e;
+    for (int k = 0; k < KB; ++k) {                   // clamped indices: every load is issued, none is conditional
+      const int64_t c = min<int64_t>(ca + k, nch - 1);
+      namb[k] = ld_dev(&ch[c].n_amb);
+      A[k] = ld_dev(&ch[c].A);
+      D[k] = ld_dev(&ch[c].D);
+      mr[k] = ld_dev(&ch[c].mref);
+    }
+    const bool has_task = lane < ntask;
+    const double4 p = ld_task(prm.part2 + b * ntask + min(lane, ntask - 1));
+    const double mt = wave_max_d(has_task ? p.x : -INFINITY);
+    const int bad = has_task && (isnan(p.y) || isnan(p.w));
+    double lst = 0.0, lsd = 0.0;
+    if (has_task) {
+      const double f = (!bonus || p.x == mt) ? 1.0 : (p.x == -INFINITY ? 0.0 : fexp_scaled((p.x - mt) * c2));
+      lst = p.y * f;
+      lsd = p.w;
+    }
+    const double St = wave_sum(lst), Sd = wave_sum(lsd);
+    int state = 0;
+    if (__any(bad) || !(St > 0.0) || isinf(mt) || (resid && !(Sd > 0.0))) state = 2;   // only a bonus row
+    const double inv_st = 1.0 / St, inv_sd = resid ? 1.0 / Sd : 0.0;
+    int64_t cstar = -1;
+    double cbase = 0.0, t = 0.0;
+    int clamp = 0;
+    if (state == 0) {
+      double lsum = 0.0;
+      int slow = 0;
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        const int64_t c = ca + k;
+        if (c >= cb) break;
+        double m = 0.0;
+        if (namb[k] > kAmbMax) {
+          slow = 1;
+        } else {
+          const double f = bonus ? fexp_scaled((mr[k] - mt) * c2) : 1.0;
+          m = f * (A[k] * inv_st - D[k] * inv_sd);
+          for (int u = 0; u < namb[k]; ++u) {          // undecided elements, exactly: max(p - q, 0)
+            const double r = ld_dev(&ch[c].et[u]) * inv_st - ld_dev(&ch[c].ed[u]) * inv_sd;
+            m += r > 0.0 ? r : 0.0;
+          }
+        }
+        sh.mass[c] = m;
+        lsum += m;
+      }
+      if (__any(slow)) {
+        state = 1;
+      } else {
+        const double incl = wave_incl_scan(lsum);
+        const double total = readlane_d(incl, 63);
+        if (!(total > 0.0)) {
+          state = 1;                                   // empty residual: the general pick draws from p
+        } else {
+          t = double(job.u) * total;
+          double acc = incl - lsum;
+          int64_t cand = -1, last = -1;
+          double cbl = 0.0;
+          for (int64_t c = ca; c < cb; ++c) {
+            const double m = sh.mass[c];
+            if (m > 0.0) last = c;
+            if (cand < 0 && acc + m > t) { cand = c; cbl = acc; }
+            acc += m;
+          }
+          const uint64_t hm = __ballot(cand >= 0);
+          if (hm) {
+            const int l = __builtin_ctzll(hm);
+            cstar = __shfl(cand, l);
+            cbase = readlane_d(cbl, l);
+          } else {                                     // rounding: the last chunk with mass
+            clamp = 1;
+            const uint64_t pm = __ballot(last >= 0);
+            cstar = pm ? __shfl(last, 63 - __builtin_clzll(pm)) : -1;
+          }
+        }
+      }
+    }
+    if (lane == 0) {
+      ls.mt = mt; ls.inv_st = inv_st; ls.inv_sd = inv_sd; ls.t = t; ls.cbase = cbase;
+      ls.cstar = cstar; ls.clamp = clamp; ls.state = state;
+    }
   }
-  const uint64_t hm = __ballot(hit >= 0);
-  const uint64_t pm = __ballot(lastpos >= 0);
-  int64_t tok = -1;
-  if (hm) {
-    const int l = __builtin_ctzll(hm);
-    tok = cstar * kChunk + int64_t(l) * kPer + __shfl(hit, l);
-  } else if (pm) {
-    const int l = 63 - __builtin_clzll(pm);
-    tok = cstar * kChunk + int64_t(l) * kPer + __shfl(lastpos, l);
+  __syncthreads();
+  const int state = ls.state;
+  if (state == 1) return false;
+  if (state == 2) {
+    if (tid == 0) {
+      finish(prm, b, job, -1, SV_FLAG_NONFINITE);
+    }
+    return true;
   }
-  if (lane == 0) {
-    prm.token[b] = int32_t(tok);
-    if (use_p && prm.flags) prm.flags[b] |= SV_FLAG_EMPTY_RESIDUAL;
+  const int64_t cstar = ls.cstar;
+  if (cstar < 0) {
+    if (tid == 0) finish(prm, b, job, -1, 0u);
+    return true;
+  }
+  search_chunk<T>(prm, b, job, cstar, ls.cbase, ls.clamp != 0, ls.t, ls.mt, ls.inv_st, double(job.m_d), ls.inv_sd,
+                  false, sh);
+  return true;
+}
+
+// Per-sequence counters. They start at zero (the workspace is zero-filled before its first use) and every launch
+// leaves them at zero again: the last draw task of a sequence clears that sequence's counters.
+__device__ __forceinline__ int32_t ld_ctr(const int32_t* p) {
+  return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+__device__ __forceinline__ void st_job(Job* p, const Job& j) {
+  const uint32_t* s = reinterpret_cast<const uint32_t*>(&j);
+  uint32_t* d = reinterpret_cast<uint32_t*>(p);
+#pragma unroll
+  for (int i = 0; i < int(sizeof(Job) / 4); ++i) st_dev(d + i, s[i]);
+}
+__device__ __forceinline__ Job ld_job(const Job* p) {
+  Job j;
+  const uint32_t* s = reinterpret_cast<const uint32_t*>(p);
+  uint32_t* d = reinterpret_cast<uint32_t*>(&j);
+#pragma unroll
+  for (int i = 0; i < int(sizeof(Job) / 4); ++i) d[i] = ld_dev(s + i);
+  return j;
+}
+
+// What workgroup i does. The queue holds, per sequence s in order, the statistics items of s followed by the scan of
+// sequence s - lag (so a scan rarely waits for its statistics); then the scans of the last lag sequences; then the
+// draw tasks of every sequence, in sequence order. Every wait is on a lower index.
+enum ItemKind : int32_t { ITEM_STATS = 0, ITEM_SCAN = 1, ITEM_DRAW = 2 };
+struct ItemRef {
+  int32_t kind;
+  int32_t b;
+  int32_t sub;    // statistics item within the sequence, or draw task
+};
+__device__ __forceinline__ ItemRef decode_item(uint32_t i, uint32_t B, uint32_t n1, uint32_t nt, uint32_t lag) {
+  const uint32_t head = lag * n1;
+  if (i < head) return ItemRef{ITEM_STATS, int32_t(i / n1), int32_t(i % n1)};
+  i -= head;
+  const uint32_t per = n1 + 1, mid = (B - lag) * per;
+  if (i < mid) {
+    const uint32_t q = i / per, r = i % per;
+    return r < n1 ? ItemRef{ITEM_STATS, int32_t(lag + q), int32_t(r)} : ItemRef{ITEM_SCAN, int32_t(q), 0};
+  }
+  i -= mid;
+  if (i < lag) return ItemRef{ITEM_SCAN, int32_t(B - lag + i), 0};
+  i -= lag;
+  return ItemRef{ITEM_DRAW, int32_t(i / nt), int32_t(i % nt)};
+}
+
+struct DrawShared {
+  Job job;
+  float max[kDrawWaves];
+  int nan[kDrawWaves];
+  double sum[kDrawWaves][2];
+};
+
+// Draw task `task` of sequence b, once its job is published: the float64 masses of chunks
+// [task * nch / ntask, (task + 1) * nch / ntask) of the draw row(s), dealt to the waves in turn, and the task's
+// partial normalisers. Returns true in the workgroup whose task is the sequence's last to finish.
+template <typename T>
+__device__ __noinline__ bool draw_task(DP& prm_arg, int64_t b, int task, const Job& job, DrawShared& ds,
+                                       int* s_flag) {
+  DP& prm = uniform_params(prm_arg);
+  constexpr int NW = kDrawWaves;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (job.kind != JOB_NONE) {                       // uniform over the workgroup
+    const int64_t V = prm.V;
+    const int64_t cbeg = int64_t(task) * prm.nch / prm.ntask;
+    const int64_t c1 = int64_t(task + 1) * prm.nch / prm.ntask;
+    const int64_t c0 = cbeg + (wave + NW / 2) % NW;
+    const T* rt = static_cast<const T*>(prm.tgt) + b * prm.t_seq + int64_t(job.row) * prm.t_row;
+    const bool resid = job.kind == JOB_RESID;
+    const T* rd = resid ? static_cast<const T*>(prm.dft) + b * prm.d_seq + int64_t(job.row) * prm.d_row : nullptr;
+    const bool vec = (reinterpret_cast<uintptr_t>(rt) & 15u) == 0 &&
+                     (!resid || (reinterpret_cast<uintptr_t>(rd) & 15u) == 0);
+    double mt = job.m_t;
+    int has_nan = 0;
+    if (job.kind == JOB_BONUS) {            // the bonus row was not in the statistics items: this task's max
+      float zt[kPer];
+      float m = -INFINITY;
+      for (int64_t c = c0; c < c1; c += NW) {
+        load_lane<T>(rt, c * kChunk + int64_t(lane) * kPer, V, vec, zt);
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) { m = fmaxf(m, zt[e]); has_nan |= (zt[e] != zt[e]); }
+      }
+      m = wave_max_f(m);
+      has_nan = __any(has_nan);
+      if (lane == 0) { ds.max[wave] = m; ds.nan[wave] = has_nan; }
+      __syncthreads();
+      m = ds.max[0];
+      has_nan = ds.nan[0];
+      for (int i = 1; i < NW; ++i) { m = fmaxf(m, ds.max[i]); has_nan |= ds.nan[i]; }
+      mt = m;
+    }
+    double st = 0.0, sd = 0.0;
+    if (mt == -INFINITY) {                  // a task of -inf only (bonus row): no mass
+      if (lane == 0) {
+        for (int64_t c = c0; c < c1; c += NW) {
+          ChunkRec* rec = prm.chunks + b * prm.nch + c;
+          st_dev(&rec->A, 0.0);
+          st_dev(&rec->D, 0.0);
+          st_dev(&rec->n_amb, 0);
+          st_dev(&rec->mref, -double(INFINITY));
+        }
+      }
+    } else if (resid) {
+      mass_chunks<T, JOB_RESID>(prm, job, b, c0, c1, NW, rt, rd, vec, mt, st, sd);
+    } else if (job.kind == JOB_ONEHOT) {
+      mass_chunks<T, JOB_ONEHOT>(prm, job, b, c0, c1, NW, rt, rd, vec, mt, st, sd);
+    } else {
+      mass_chunks<T, JOB_BONUS>(prm, job, b, c0, c1, NW, rt, rd, vec, mt, st, sd);
+    }
+    st = wave_sum(st);
+    if (resid) sd = wave_sum(sd);
+    if (lane == 0) { ds.sum[wave][0] = st; ds.sum[wave][1] = sd; }
+    __syncthreads();
+    if (tid == 0) {
+      double S = 0.0, D = 0.0;
+      for (int i = 0; i < NW; ++i) { S += ds.sum[i][0]; D += ds.sum[i][1]; }
+      st_task(prm.part2 + b * prm.ntask + task, make_double4(mt, has_nan ? NAN : S, job.m_d, D));
+    }
+  }
+  // this workgroup's records are complete before it is counted; the last one picks
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) *s_flag = ctr_add(prm.done + b * kCtrStride) == prm.ntask - 1;
+  __syncthreads();
+  return *s_flag != 0;
+}
+
+__device__ __forceinline__ void ctr_inc(int32_t* p) {
+  (void)__hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// Waits (thread 0 polls, the others hold at the barrier) until the counter reaches `target`. Returns false when it
+// gave up after kSpinCap polls, which only happens if the hardware broke the dispatch order.
+__device__ __forceinline__ bool wait_count(const int32_t* ctr, int32_t target, int* s_flag) {
+  if (threadIdx.x == 0) {
+    int32_t polls = 0;
+    while (ld_ctr(ctr) < target && polls < kSpinCap) {
+      __builtin_amdgcn_s_sleep(SV_SLEEP);
+      ++polls;
+    }
+    *s_flag = polls < kSpinCap;
+  }
+  __syncthreads();
+  return *s_flag != 0;
+}
+
+// One workgroup per work item, in the queue order of decode_item (the hardware dispatches workgroups in index
+// order, so everything a workgroup waits for was dispatched before it and is running or done):
+//  - statistics item: streams its segment, writes its partial and counts itself on the sequence's counter;
+//  - scan: once the sequence's statistics are all counted, the accept tests, the first-rejection scan, the per-row
+//    outputs and the draw job, published by one more count;
+//  - draw task: once the job is published, the float64 masses of its chunks; the last task of the sequence picks the
+//    token and returns the sequence's counters to zero.
+template <typename T>
+__global__ __launch_bounds__(kDrawBlock) __attribute__((amdgpu_waves_per_eu(kWpe, kWpe))) void k_verify(DenseParams kp) {
+  (void)kp;
+  DP& prm = kernel_params();
+  __shared__ float sh_f[kDrawWaves];
+  __shared__ double sh_d[kDrawWaves];
+  __shared__ uint32_t seen[SV_MAX_GAMMA / 32];
+  __shared__ DrawShared ds;
+  __shared__ PickShared psh;
+  __shared__ LeanShared ls;
+  __shared__ int s_flag;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const ItemRef it = decode_item(blockIdx.x, uint32_t(prm.B), uint32_t(prm.n1), uint32_t(prm.ntask),
+                                 uint32_t(prm.lag));
+  const int64_t b = it.b;
+  int32_t* ready = prm.ready + b * kCtrStride;
+  if (it.kind == ITEM_STATS) {
+    stats_item<T, kStatsBlock, kUnroll, kNonTemporal>(prm, b, it.sub, sh_f, sh_d);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) ctr_inc(ready);
+    return;
+  }
+  if (it.kind == ITEM_SCAN) {
+    // the scan and the pick are short serial chains on the critical path: their waves get issue priority over the
+    // streaming and float64 waves that share their SIMDs
+    __builtin_amdgcn_s_setprio(3);
+    const bool ok = wait_count(ready, prm.n1, &s_flag);
+    if (wave == 0) {
+      Job j;
+      if (ok) {
+        j = seq_scan(prm, b, true, seen);
+      } else {                                       // gave up waiting: report the sequence as not verified
+        j = Job{};
+        j.kind = JOB_NONE;
+        j.flags = SV_FLAG_NONFINITE | SV_FLAG_ID_RANGE;
+        j.new_start = -1;
+      }
+      if (lane == 0) {
+        st_job(prm.jobs + b, j);
+        __builtin_amdgcn_s_waitcnt(0);
+        ctr_inc(ready);                              // n1 + 1: the job is published
+      }
+    }
+    return;
+  }
+  s_exp2tab[tid] = exp2(double(tid) * 0.00390625);   // the draw's exp2 table (kDrawBlock == 256 entries)
+  if (tid == 0) {
+    Job j;
+    int32_t polls = 0;
+    while (ld_ctr(ready) < prm.n1 + 1 && polls < kSpinCap) {
+      __builtin_amdgcn_s_sleep(SV_SLEEP);
+      ++polls;
+    }
+    if (polls < kSpinCap) {
+      j = ld_job(prm.jobs + b);
+    } else {
+      j = Job{};
+      j.kind = JOB_NONE;
+      j.flags = SV_FLAG_NONFINITE | SV_FLAG_ID_RANGE;
+      j.new_start = -1;
+    }
+    ds.job = j;
+  }
+  __syncthreads();
+  const Job job = ds.job;
+  if (draw_task<T>(prm, b, it.sub, job, ds, &s_flag)) {
+    __builtin_amdgcn_s_setprio(3);
+    if (tid == 0 && prm.start && job.new_start >= 0) prm.start[b] = job.new_start;
+    if (job.kind == JOB_NONE) {
+      if (tid == 0) finish(prm, b, job, -1, 0u);
+    } else if (!(prm.nch <= kLeanChunks && prm.ntask <= 64 && pick_lean<T>(prm, b, job, psh, ls))) {
+      pick_seq<T>(prm, b, job, psh);
+    }
+    if (tid == 0) {                                  // every item of sequence b has finished
+      st_dev(ready, 0);
+      st_dev(prm.done + b * kCtrStride, 0);
+    }
   }
 }
 
-// Workgroups of the statistics pass: every work item, capped at kStatsWgPerCu per compute unit (the kernel then
-// loops over items).
-int64_t stats_grid(int64_t items) {
+// Resident workgroups of the kernel on the current device (compute units x workgroups per compute unit).
+int resident_workgroups() {
+  static int cached[64] = {};
   int dev = 0, ncu = 0;
-  if (kStatsWgPerCu <= 0 || hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
-    return items;
-  const int64_t cap = int64_t(ncu) * kStatsWgPerCu;
-  return items < cap ? items : cap;
+  if (hipGetDevice(&dev) != hipSuccess) return 1024;
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0) ncu = 256;
+  const int r = ncu * kWpe;          // four 4-wave workgroups per compute unit at 4 waves per SIMD
+  if (dev >= 0 && dev < 64) cached[dev] = r;
+  return r;
 }
 
 template <typename T>
 hipError_t launch_typed(const DensePlan& plan, const DenseArgs& a, hipStream_t stream) {
   char* ws = a.ws;
-  Partial1* part1 = reinterpret_cast<Partial1*>(ws + plan.off_part1);
-  Job* jobs = reinterpret_cast<Job*>(ws + plan.off_jobs);
-  double4* part2a = reinterpret_cast<double4*>(ws + plan.off_part2a);
-  ChunkRec* chunks = reinterpret_cast<ChunkRec*>(ws + plan.off_chunks);
-  double* masses = reinterpret_cast<double*>(ws + plan.off_masses);
   const double T_ = double(a.temperature);
   const float c = float(1.4426950408889634074 / T_);          // log2(e) / T
-
-  StatsParams sp{a.tgt, a.t_seq, a.t_row, a.dft, a.d_seq, a.d_row, plan.B, plan.G, plan.V, plan.nseg1, plan.ntens,
-                 c, a.start, a.order, a.ids, part1};
-  const int64_t g1 = int64_t(plan.ntens) * plan.B * plan.G * plan.nseg1;
-  const int64_t grid1 = stats_grid(g1);
+  DenseParams dp{};
+  dp.tgt = a.tgt; dp.t_seq = a.t_seq; dp.t_row = a.t_row;
+  dp.dft = a.dft; dp.d_seq = a.d_seq; dp.d_row = a.d_row;
+  dp.B = plan.B; dp.G = plan.G; dp.V = plan.V; dp.nseg1 = plan.nseg1; dp.ntens = plan.ntens; dp.bonus = a.bonus;
+  dp.c = c; dp.c2 = 1.4426950408889634074 / T_;
+  dp.ids = a.ids; dp.ua = a.ua; dp.us = a.us; dp.start = a.start; dp.order = a.order;
+  dp.accept = a.accept; dp.n_acc = a.n_acc; dp.token = a.token; dp.p_draft = a.p_draft; dp.q_draft = a.q_draft;
+  dp.flags = a.flags;
+  dp.n1 = plan.n1; dp.ntask = plan.ntask; dp.nch = plan.nch;
+  const int R = resident_workgroups();
+  int64_t lag = (int64_t(R) * kLagRounds + plan.n1 - 1) / plan.n1;
+  if (lag > plan.B) lag = plan.B;
+  if (lag < 1) lag = 1;
+  dp.lag = int32_t(lag);
+  dp.n_items = int32_t(plan.B * (int64_t(plan.n1) + 1 + plan.ntask));
+  dp.ready = reinterpret_cast<int32_t*>(ws + plan.off_ready);
+  dp.done = reinterpret_cast<int32_t*>(ws + plan.off_done);
+  dp.jobs = reinterpret_cast<Job*>(ws + plan.off_jobs);
+  dp.part1 = reinterpret_cast<Partial1*>(ws + plan.off_part1);
+  dp.part2 = reinterpret_cast<double4*>(ws + plan.off_part2);
+  dp.chunks = reinterpret_cast<ChunkRec*>(ws + plan.off_chunks);
+  dp.masses = reinterpret_cast<double*>(ws + plan.off_masses);
+  const unsigned grid = unsigned(dp.n_items);
+  auto kern = k_verify<T>;
   if (a.ev_start) {      // events taken from the dispatch packet itself: no marker packets around the kernel
-    hipExtLaunchKernelGGL((k_stats<T, kStatsBlock, kUnroll, kNonTemporal, kStatsWpe>), dim3(unsigned(grid1)),
-                          dim3(kStatsBlock), 0, stream, static_cast<hipEvent_t>(a.ev_start),
-                          static_cast<hipEvent_t>(a.ev_stop), 0, sp);
+    hipExtLaunchKernelGGL(kern, dim3(grid), dim3(kDrawBlock), 0, stream, static_cast<hipEvent_t>(a.ev_start),
+                          static_cast<hipEvent_t>(a.ev_stop), 0, dp);
   } else {
-    hipLaunchKernelGGL((k_stats<T, kStatsBlock, kUnroll, kNonTemporal, kStatsWpe>), dim3(unsigned(grid1)),
-                       dim3(kStatsBlock), 0, stream, sp);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kDrawBlock), 0, stream, dp);
   }
-
-  DenseParams dp{a.tgt, a.t_seq, a.t_row, a.dft, a.d_seq, a.d_row, plan.B, plan.G, plan.V, plan.nseg1, a.bonus, c,
-                 1.0 / T_, a.ids, a.ua, a.us, a.start, a.order, a.accept, a.n_acc, a.token, a.p_draft, a.q_draft,
-                 a.flags, part1, jobs, plan.nseg2, plan.cpw, plan.nch, part2a, chunks, masses};
-  const int64_t g2 = plan.B * plan.nseg2;
-  hipLaunchKernelGGL((k_draw_mass<T>), dim3(unsigned(g2)), dim3(64), 0, stream, dp);
-  hipLaunchKernelGGL((k_draw_pick<T, kDrawBlock>), dim3(unsigned(plan.B)), dim3(kDrawBlock), 0, stream, dp);
   return hipGetLastError();
 }
 
@@ -1048,28 +1616,28 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace
 
-DensePlan make_dense_plan(int64_t B, int32_t G, int64_t V, int32_t ntens) {
+DensePlan make_dense_plan(int64_t B, int32_t G, int64_t V, int32_t ntens, int dtype) {
   DensePlan p;
   p.B = B; p.G = G; p.V = V; p.ntens = ntens;
-  const int64_t rows = int64_t(ntens) * B * G;
-  // statistics pass: aim for >= 2048 workgroups (8 per CU on 256 CUs), segments of >= 8192 elements
-  int64_t s1 = (2048 + rows - 1) / rows;
+  const int64_t es = dtype == SV_BF16 ? 2 : 4;
+  // statistics items of about kItemBytes of logits, at least 8192 elements each
+  int64_t s1 = (V * es + kItemBytes - 1) / kItemBytes;
   const int64_t cap1 = V / 8192 > 1 ? V / 8192 : 1;
   if (s1 > cap1) s1 = cap1;
   if (s1 < 1) s1 = 1;
   p.nseg1 = int32_t(s1);
-  // draw pass: rows cut into chunks of kChunk elements; one-wave workgroups of cpw chunks each, cpw chosen so that
-  // the B row pairs give about 8192 workgroups
+  p.n1 = int64_t(ntens) * G * s1;
+  // draw: rows cut into chunks of kChunk elements, kTaskChunks consecutive chunks per task
   p.nch = (V + kChunk - 1) / kChunk;
-  int64_t cpw = (int64_t(B) * p.nch + 8191) / 8192;
-  if (cpw < 1) cpw = 1;
-  if (cpw > 64) cpw = 64;
-  p.cpw = int32_t(cpw);
-  p.nseg2 = int32_t((p.nch + cpw - 1) / cpw);
+  int64_t ntask = (p.nch + kTaskChunks - 1) / kTaskChunks;
+  if (ntask < 1) ntask = 1;
+  p.ntask = int32_t(ntask);
   size_t off = 0;
-  p.off_part1 = off; off = align_up(off + size_t(rows) * p.nseg1 * sizeof(Partial1), 256);
+  p.off_ready = off; off = align_up(off + size_t(B) * kCtrStride * sizeof(int32_t), 256);
+  p.off_done = off;  off = align_up(off + size_t(B) * kCtrStride * sizeof(int32_t), 256);
   p.off_jobs = off;  off = align_up(off + size_t(B) * sizeof(Job), 256);
-  p.off_part2a = off; off = align_up(off + size_t(B) * p.nseg2 * sizeof(double4), 256);
+  p.off_part1 = off; off = align_up(off + size_t(ntens) * size_t(B) * G * p.nseg1 * sizeof(Partial1), 256);
+  p.off_part2 = off; off = align_up(off + size_t(B) * p.ntask * sizeof(double4), 256);
   p.off_chunks = off; off = align_up(off + size_t(B) * size_t(p.nch) * sizeof(ChunkRec), 256);
   p.off_masses = off; off = align_up(off + size_t(B) * size_t(p.nch) * sizeof(double), 256);
   p.total = off;

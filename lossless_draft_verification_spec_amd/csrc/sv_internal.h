@@ -16,40 +16,43 @@ enum JobKind : int32_t {
   JOB_BONUS = 3,     // bonus draw from p of target row gamma
 };
 
-// One record per sequence, written by the leader workgroup of the mass pass and read by the pick.
+// What the scan of one sequence decides, published to the sequence's draw tasks.
 struct alignas(16) Job {
   int32_t kind;      // JobKind
   int32_t row;       // storage row of the draw (gamma for the bonus)
   int32_t d;         // draft id at that row (one-hot residual)
-  int32_t pad0;
+  uint32_t flags;    // the sequence's SV_FLAG_* bits from the scan
   float u;           // the uniform of the draw
   float m_t;         // exact max of the target row (from the statistics pass; unused for the bonus)
   float m_d;         // exact max of the draft row
   float pad1;
   double kappa;      // S_d / S_t of the row pair as estimated by the statistics pass (float32 sums)
-  int32_t new_start; // start for the next call (-1: leave unchanged), written by the pick
+  int32_t new_start; // start for the next call (-1: leave unchanged)
   int32_t pad2;
 };
 
-// Sizes and workspace layout of one dense / one-hot call. Depends only on (B, gamma, V, number of tensors).
+// Sizes, work queue and workspace layout of one dense / one-hot call. Depends only on (B, gamma, V, number of
+// tensors, dtype); the float32 plan is the larger, so it sizes the workspace for both dtypes.
 struct DensePlan {
   int64_t B = 0;
   int32_t G = 0;
   int64_t V = 0;
   int32_t ntens = 0;     // 2: target + draft; 1: target only (one-hot)
-  int32_t nseg1 = 1;     // segments per row in the statistics pass
-  int32_t nseg2 = 1;     // segments per row in the float64 draw passes
-  int64_t nch = 1;       // 1024-element chunks per row in the draw passes
-  int32_t cpw = 1;       // chunks per workgroup of the draw's mass pass
-  size_t off_part1 = 0;  // float2 (max, sum) per (tensor, b, row, seg1)
+  int32_t nseg1 = 1;     // statistics items (segments) per row
+  int64_t n1 = 1;        // statistics items per sequence: ntens * G * nseg1
+  int32_t ntask = 1;     // draw tasks per sequence
+  int64_t nch = 1;       // 512-element chunks per row in the draw
+  size_t off_ready = 0;  // int32 per b (one per 256 bytes): statistics items finished, + 1 once the job is published
+  size_t off_done = 0;   // int32 per b (one per 256 bytes): draw tasks finished
   size_t off_jobs = 0;   // Job per b
-  size_t off_part2a = 0; // double4 (m_seg, S_t, m_d, S_d) per (b, seg2)
+  size_t off_part1 = 0;  // (max, logit at the id, float64 sum) per (tensor, b, row, segment)
+  size_t off_part2 = 0;  // double4 (m_task, S_t, m_d, S_d) per (b, task)
   size_t off_chunks = 0; // chunk record per (b, chunk)
   size_t off_masses = 0; // double per (b, chunk)
   size_t total = 0;
 };
 
-DensePlan make_dense_plan(int64_t B, int32_t G, int64_t V, int32_t ntens);
+DensePlan make_dense_plan(int64_t B, int32_t G, int64_t V, int32_t ntens, int dtype);
 
 struct DenseArgs {
   const void* tgt; int64_t t_seq, t_row;

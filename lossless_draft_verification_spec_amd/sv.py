@@ -110,7 +110,7 @@ def workspace(kind: int, B: int, gamma: int, V_or_k: int, device) -> torch.Tenso
         raise SVError(-2)
     if n == 0:
         return None
-    ws = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    ws = torch.zeros(n + 256, dtype=torch.uint8, device=device)   # control words must start at zero
     off = (-ws.data_ptr()) % 256
     return ws[off:off + n]
 

@@ -162,8 +162,8 @@ def test_dense_data_faults():
 
 @pytest.mark.parametrize("V", [30_000, 600_001])
 def test_dense_near_equal_distributions(V):
-    """Draft = target + tiny noise: the residual's sign is undecided for most elements, so the draw recomputes most
-    chunks exactly (at V = 600001 more chunks than the pick's queue holds). Uniforms near 1 force rejections."""
+    """Draft = target + tiny noise: the residual's sign is undecided for most elements, so the pick recomputes most
+    chunks exactly. Uniforms near 1 force rejections."""
     B, G = 3, 2
     case = W.dense_case(B, G, V, dtype="f32", sigma_t=2.0, sigma_d=2e-5, seed=16)
     case["u_accept"][:] = np.float32(0.99999)
@@ -173,6 +173,21 @@ def test_dense_near_equal_distributions(V):
     compare_probs(g, o, "p_draft", "f32")
     log(f"near-equal V={V}: {s}, n {g['n_accepted'].tolist()}")
     assert (g["n_accepted"] < G).any()
+
+
+def test_dense_rows_longer_than_one_pick_tile():
+    """V = 1300003: more 1024-element chunks per row than the pick holds at once, so chunk masses go through global
+    memory tile by tile. Sequence 0 accepts every draft (bonus draw over the long row); the others reject."""
+    B, G, V = 3, 2, 1_300_003
+    case = W.dense_case(B, G, V, dtype="f32", sigma_t=2.0, sigma_d=0.5, seed=17)
+    case["u_accept"][0] = 0.0
+    case["u_accept"][1:] = np.float32(0.99999)
+    g = run_dense(case)
+    o = oracle_dense(case)
+    s = compare_decisions(g, o, "multi-tile")
+    compare_probs(g, o, "p_draft", "f32")
+    log(f"multi-tile: {s}, n {g['n_accepted'].tolist()}, tokens {g['out_token'].tolist()}")
+    assert g["n_accepted"][0] == G and (g["n_accepted"][1:] < G).any()
 
 
 def test_dense_is_deterministic():
