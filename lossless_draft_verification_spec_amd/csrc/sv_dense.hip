@@ -43,21 +43,28 @@ constexpr int kUnroll = 4;          // 16-byte vectors per thread per group
 #define SV_STATS_NT 1
 #endif
 constexpr bool kNonTemporal = SV_STATS_NT != 0;   // streaming loads that bypass cache retention
-constexpr int kWpe = 4;             // waves per SIMD the kernel is compiled for (more waves stream worse)
+#ifndef SV_WPE
+#define SV_WPE 4
+#endif
+constexpr int kWpe = SV_WPE;        // waves per SIMD the kernel is compiled for
 constexpr int kDrawBlock = 256;     // threads per workgroup, both kinds of item
 #ifndef SV_ITEM_BYTES
-#define SV_ITEM_BYTES 131072
+#define SV_ITEM_BYTES 1048576
 #endif
 constexpr int64_t kItemBytes = SV_ITEM_BYTES;   // target bytes of logits per statistics item
 #ifndef SV_TASK_CHUNKS
 #define SV_TASK_CHUNKS 16
 #endif
 constexpr int64_t kTaskChunks = SV_TASK_CHUNKS; // chunks per draw task (four per wave)
-#ifndef SV_LAG_ROUNDS
-#define SV_LAG_ROUNDS 1
+#ifndef SV_SCAN_LAG_ROUNDS
+#define SV_SCAN_LAG_ROUNDS 1
 #endif
-constexpr int kLagRounds = SV_LAG_ROUNDS;       // resident rounds of statistics items between a sequence's statistics
-                                                // and its scan
+#ifndef SV_DRAW_LAG_ROUNDS
+#define SV_DRAW_LAG_ROUNDS 0
+#endif
+constexpr int kScanLagRounds = SV_SCAN_LAG_ROUNDS;  // resident rounds of statistics items between a sequence's
+                                                    // statistics and its scan
+constexpr int kDrawLagRounds = SV_DRAW_LAG_ROUNDS;  // ... and its draw tasks (0: after every statistics item)
 constexpr int kCtrStride = 64;                  // int32 slots between per-sequence counters (one 256-byte line each)
 #ifndef SV_SLEEP
 #define SV_SLEEP 16
@@ -267,9 +274,8 @@ struct DenseParams {
   const int32_t* ids; const float* ua; const float* us;
   int32_t* start; const int32_t* order;
   uint8_t* accept; int32_t* n_acc; int32_t* token; float* p_draft; float* q_draft; uint32_t* flags;
-  // work queue: per sequence n1 statistics items and ntask draw tasks; the draw tasks of sequence b follow the
-  // statistics items of sequence b + lag
-  int32_t n1; int32_t ntask; int32_t lag; int32_t n_items;
+  // work queue: per sequence n1 statistics items, one scan and ntask draw tasks, in the order of decode_item
+  int32_t n1; int32_t ntask; int32_t lag1; int32_t lag2; int32_t n_items;
   int64_t nch;                                // 1024-element chunks per row
   int32_t* ready;                             // per b (stride kCtrStride): statistics items finished
   int32_t* done;                              // per b (stride kCtrStride): draw tasks finished
@@ -974,6 +980,7 @@ __device__ __forceinline__ void mass_chunks(DP& prm, const Job& job, int64_t b, 
 // kPT * tid .. kPT * tid + kPT - 1), evaluated exactly as chunk_weights does. Every load is issued before the first
 // weight is formed.
 constexpr int kPT = kChunk / kDrawBlock;
+constexpr int kLeanChunks = 512;    // the lean pick: at most 8 chunks per lane (and at most 64 tasks)
 template <typename T>
 __device__ __forceinline__ void chunk_weights_t(const Job& job, const T* rt, const T* rd, int64_t c, int tid, int64_t V,
                                                 double mt, double inv_st, double md, double inv_sd, double c2,
@@ -1200,133 +1207,136 @@ __device__ __noinline__ void pick_seq(DP& prm_arg, int64_t b, const Job& job, Pi
   search_chunk<T>(prm, b, job, cstar, clamp ? 0.0 : sh.base, clamp, t, mt, inv_st, md, inv_sd, use_p, sh);
 }
 
-// The common case of the pick, for rows of at most kLeanChunks chunks whose records need no recomputation: wave 0
-// forms the normalisers and the chunk masses and locates the chunk that holds t with wave-level operations (lane l
-// owns a contiguous run of chunks); the whole workgroup then searches that chunk. Returns false, with nothing
-// written, when the general pick must run instead (an undecided chunk, an empty residual).
-constexpr int kLeanChunks = 512;       // the lean pick: at most 8 chunks per lane, at most 64 tasks
-
-struct LeanShared {
-  double mt, inv_st, inv_sd, t, cbase;
-  int64_t cstar;
-  int clamp, state;                   // state: 0 search, 1 general pick, 2 bad bonus row
-};
-
-
+// The common case of the pick, for rows of at most kLeanChunks chunks and at most 64 draw tasks whose chunk records
+// need no recomputation, by wave 0 alone (no barrier, no shared memory): one round of loads brings the task partials
+// and every chunk record (lane l owns a contiguous run of at most 8 chunks); the normalisers, the chunk masses, their
+// running sum and the chunk that holds t = u * total follow with wave-level operations; that chunk is then searched
+// with the mass pass's layout (lane l holds its kPer consecutive elements). Returns 0 when done (token and flags
+// written), 1 when the general pick must run instead (an undecided chunk, an empty residual), with nothing written.
 template <typename T>
-__device__ __forceinline__ bool pick_lean(DP& prm, int64_t b, const Job& job, PickShared& sh, LeanShared& ls) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t nch = prm.nch;
+__device__ __forceinline__ int pick_lean(DP& prm, int64_t b, const Job& job) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nch = prm.nch, V = prm.V;
   const int ntask = prm.ntask;
   const double c2 = prm.c2;
   const bool resid = job.kind == JOB_RESID, bonus = job.kind == JOB_BONUS;
-  if (wave == 0) {
-    // One round of loads: lane l's task partial (at most 64 tasks) and the records of its chunks (at most 8).
-    const ChunkRec* ch = prm.chunks + b * nch;
-    const int q = int((nch + 63) / 64);
-    const int64_t ca = min<int64_t>(nch, int64_t(lane) * q), cb = min<int64_t>(nch, ca + q);
-    constexpr int KB = kLeanChunks / 64;
-    int namb[KB];
-    double A[KB], D[KB], mr[KB];
+  const ChunkRec* ch = prm.chunks + b * nch;
+  const int q = int((nch + 63) / 64);
+  const int64_t ca = min<int64_t>(nch, int64_t(lane) * q), cb = min<int64_t>(nch, ca + q);
+  constexpr int KB = kLeanChunks / 64;
+  int namb[KB];
+  double A[KB], D[KB], mr[KB];
 #pragma unroll
-    for (int k = 0; k < KB; ++k) {                   // clamped indices: every load is issued, none is conditional
-      const int64_t c = min<int64_t>(ca + k, nch - 1);
-      namb[k] = ld_dev(&ch[c].n_amb);
-      A[k] = ld_dev(&ch[c].A);
-      D[k] = ld_dev(&ch[c].D);
-      mr[k] = ld_dev(&ch[c].mref);
-    }
-    const bool has_task = lane < ntask;
-    const double4 p = ld_task(prm.part2 + b * ntask + min(lane, ntask - 1));
-    const double mt = wave_max_d(has_task ? p.x : -INFINITY);
-    const int bad = has_task && (isnan(p.y) || isnan(p.w));
-    double lst = 0.0, lsd = 0.0;
-    if (has_task) {
-      const double f = (!bonus || p.x == mt) ? 1.0 : (p.x == -INFINITY ? 0.0 : fexp_scaled((p.x - mt) * c2));
-      lst = p.y * f;
-      lsd = p.w;
-    }
-    const double St = wave_sum(lst), Sd = wave_sum(lsd);
-    int state = 0;
-    if (__any(bad) || !(St > 0.0) || isinf(mt) || (resid && !(Sd > 0.0))) state = 2;   // only a bonus row
-    const double inv_st = 1.0 / St, inv_sd = resid ? 1.0 / Sd : 0.0;
-    int64_t cstar = -1;
-    double cbase = 0.0, t = 0.0;
-    int clamp = 0;
-    if (state == 0) {
-      double lsum = 0.0;
-      int slow = 0;
+  for (int k = 0; k < KB; ++k) {                     // clamped indices: every load is issued, none is conditional
+    const int64_t c = min<int64_t>(ca + k, nch - 1);
+    namb[k] = ld_dev(&ch[c].n_amb);
+    A[k] = ld_dev(&ch[c].A);
+    D[k] = ld_dev(&ch[c].D);
+    mr[k] = ld_dev(&ch[c].mref);
+  }
+  const bool has_task = lane < ntask;
+  const double4 p = ld_task(prm.part2 + b * ntask + min(lane, ntask - 1));
+  const double mt = wave_max_d(has_task ? p.x : -INFINITY);
+  const int bad = __any(has_task && (isnan(p.y) || isnan(p.w)));
+  double lst = 0.0, lsd = 0.0;
+  if (has_task) {
+    const double f = (!bonus || p.x == mt) ? 1.0 : (p.x == -INFINITY ? 0.0 : fexp_scaled((p.x - mt) * c2));
+    lst = p.y * f;
+    lsd = p.w;
+  }
+  const double St = wave_sum(lst), Sd = wave_sum(lsd);
+  if (bad || !(St > 0.0) || isinf(mt) || (resid && !(Sd > 0.0))) {     // only a bonus row can be bad here
+    if (lane == 0) finish(prm, b, job, -1, SV_FLAG_NONFINITE);
+    return 0;
+  }
+  const double inv_st = 1.0 / St, inv_sd = resid ? 1.0 / Sd : 0.0;
+  double m[KB];
+  double lsum = 0.0;
+  int slow = 0;
 #pragma unroll
-      for (int k = 0; k < KB; ++k) {
-        const int64_t c = ca + k;
-        if (c >= cb) break;
-        double m = 0.0;
-        if (namb[k] > kAmbMax) {
-          slow = 1;
-        } else {
-          const double f = bonus ? fexp_scaled((mr[k] - mt) * c2) : 1.0;
-          m = f * (A[k] * inv_st - D[k] * inv_sd);
-          for (int u = 0; u < namb[k]; ++u) {          // undecided elements, exactly: max(p - q, 0)
-            const double r = ld_dev(&ch[c].et[u]) * inv_st - ld_dev(&ch[c].ed[u]) * inv_sd;
-            m += r > 0.0 ? r : 0.0;
-          }
-        }
-        sh.mass[c] = m;
-        lsum += m;
-      }
-      if (__any(slow)) {
-        state = 1;
-      } else {
-        const double incl = wave_incl_scan(lsum);
-        const double total = readlane_d(incl, 63);
-        if (!(total > 0.0)) {
-          state = 1;                                   // empty residual: the general pick draws from p
-        } else {
-          t = double(job.u) * total;
-          double acc = incl - lsum;
-          int64_t cand = -1, last = -1;
-          double cbl = 0.0;
-          for (int64_t c = ca; c < cb; ++c) {
-            const double m = sh.mass[c];
-            if (m > 0.0) last = c;
-            if (cand < 0 && acc + m > t) { cand = c; cbl = acc; }
-            acc += m;
-          }
-          const uint64_t hm = __ballot(cand >= 0);
-          if (hm) {
-            const int l = __builtin_ctzll(hm);
-            cstar = __shfl(cand, l);
-            cbase = readlane_d(cbl, l);
-          } else {                                     // rounding: the last chunk with mass
-            clamp = 1;
-            const uint64_t pm = __ballot(last >= 0);
-            cstar = pm ? __shfl(last, 63 - __builtin_clzll(pm)) : -1;
-          }
-        }
-      }
+  for (int k = 0; k < KB; ++k) {
+    m[k] = 0.0;
+    if (ca + k >= cb) continue;
+    if (namb[k] > kAmbMax) {
+      slow = 1;
+      continue;
     }
-    if (lane == 0) {
-      ls.mt = mt; ls.inv_st = inv_st; ls.inv_sd = inv_sd; ls.t = t; ls.cbase = cbase;
-      ls.cstar = cstar; ls.clamp = clamp; ls.state = state;
+    const double f = bonus ? fexp_scaled((mr[k] - mt) * c2) : 1.0;
+    m[k] = f * (A[k] * inv_st - D[k] * inv_sd);
+    for (int u = 0; u < namb[k]; ++u) {              // undecided elements, exactly: max(p - q, 0)
+      const double r = ld_dev(&ch[ca + k].et[u]) * inv_st - ld_dev(&ch[ca + k].ed[u]) * inv_sd;
+      m[k] += r > 0.0 ? r : 0.0;
     }
+    lsum += m[k];
   }
-  __syncthreads();
-  const int state = ls.state;
-  if (state == 1) return false;
-  if (state == 2) {
-    if (tid == 0) {
-      finish(prm, b, job, -1, SV_FLAG_NONFINITE);
-    }
-    return true;
+  if (__any(slow)) return 1;
+  const double incl = wave_incl_scan(lsum);
+  const double total = readlane_d(incl, 63);
+  if (!(total > 0.0)) return 1;                      // empty residual: the general pick draws from p
+  const double t = double(job.u) * total;
+
+  // the chunk whose running sum first exceeds t (else, rounding, the last chunk with mass)
+  double acc = incl - lsum, cbl = 0.0;
+  int64_t cand = -1, last = -1;
+#pragma unroll
+  for (int k = 0; k < KB; ++k) {
+    if (ca + k >= cb) continue;
+    if (m[k] > 0.0) last = ca + k;
+    if (cand < 0 && acc + m[k] > t) { cand = ca + k; cbl = acc; }
+    acc += m[k];
   }
-  const int64_t cstar = ls.cstar;
+  int64_t cstar;
+  double cbase = 0.0;
+  bool clamp = false;
+  const uint64_t hm = __ballot(cand >= 0);
+  if (hm) {
+    const int l = __builtin_ctzll(hm);
+    cstar = __shfl(cand, l);
+    cbase = readlane_d(cbl, l);
+  } else {
+    clamp = true;
+    const uint64_t pm = __ballot(last >= 0);
+    cstar = pm ? __shfl(last, 63 - __builtin_clzll(pm)) : -1;
+  }
   if (cstar < 0) {
-    if (tid == 0) finish(prm, b, job, -1, 0u);
-    return true;
+    if (lane == 0) finish(prm, b, job, -1, 0u);
+    return 0;
   }
-  search_chunk<T>(prm, b, job, cstar, ls.cbase, ls.clamp != 0, ls.t, ls.mt, ls.inv_st, double(job.m_d), ls.inv_sd,
-                  false, sh);
-  return true;
+
+  // the exact search inside chunk cstar: the first element whose running sum from cbase exceeds t, else (clamp,
+  // or rounding) the chunk's last element with weight
+  const T* rt = static_cast<const T*>(prm.tgt) + b * prm.t_seq + int64_t(job.row) * prm.t_row;
+  const T* rd = resid ? static_cast<const T*>(prm.dft) + b * prm.d_seq + int64_t(job.row) * prm.d_row : nullptr;
+  const bool vec = (reinterpret_cast<uintptr_t>(rt) & 15u) == 0 &&
+                   (!resid || (reinterpret_cast<uintptr_t>(rd) & 15u) == 0);
+  double w[kPer];
+  chunk_weights<T>(job, rt, rd, vec, cstar, lane, V, mt, inv_st, double(job.m_d), inv_sd, c2, false, w);
+  double mine = 0.0;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) mine += w[e];
+  const double inc2 = wave_incl_scan(mine);
+  double run = cbase + (inc2 - mine);
+  int hit = -1, lastpos = -1;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    run += w[e];
+    if (w[e] > 0.0) lastpos = e;
+    if (hit < 0 && !clamp && w[e] > 0.0 && run > t) hit = e;
+  }
+  int32_t tok = -1;
+  const uint64_t hh = __ballot(hit >= 0);
+  if (hh) {
+    const int l = __builtin_ctzll(hh);
+    tok = int32_t(cstar * kChunk + int64_t(l) * kPer + __shfl(hit, l));
+  } else {
+    const uint64_t lp = __ballot(lastpos >= 0);
+    if (lp) {
+      const int l = 63 - __builtin_clzll(lp);
+      tok = int32_t(cstar * kChunk + int64_t(l) * kPer + __shfl(lastpos, l));
+    }
+  }
+  if (lane == 0) finish(prm, b, job, tok, 0u);
+  return 0;
 }
 
 // Per-sequence counters. They start at zero (the workspace is zero-filled before its first use) and every launch
@@ -1350,28 +1360,44 @@ __device__ __forceinline__ Job ld_job(const Job* p) {
   return j;
 }
 
-// What workgroup i does. The queue holds, per sequence s in order, the statistics items of s followed by the scan of
-// sequence s - lag (so a scan rarely waits for its statistics); then the scans of the last lag sequences; then the
-// draw tasks of every sequence, in sequence order. Every wait is on a lower index.
+// What workgroup i does. The queue is a sequence of steps s = 0, 1, ...; step s holds the statistics items of
+// sequence s, then the scan of sequence s - lag1, then the draw tasks of sequence s - lag2 (each part only when that
+// sequence exists), with 1 <= lag1 <= lag2 <= B. A scan thus comes about one resident round of statistics items after
+// its own, and draw tasks lag2 steps after theirs (lag2 = B puts every draw task after every statistics item).
+// Every wait is on a lower index.
 enum ItemKind : int32_t { ITEM_STATS = 0, ITEM_SCAN = 1, ITEM_DRAW = 2 };
 struct ItemRef {
   int32_t kind;
   int32_t b;
   int32_t sub;    // statistics item within the sequence, or draw task
 };
-__device__ __forceinline__ ItemRef decode_item(uint32_t i, uint32_t B, uint32_t n1, uint32_t nt, uint32_t lag) {
-  const uint32_t head = lag * n1;
-  if (i < head) return ItemRef{ITEM_STATS, int32_t(i / n1), int32_t(i % n1)};
-  i -= head;
-  const uint32_t per = n1 + 1, mid = (B - lag) * per;
-  if (i < mid) {
-    const uint32_t q = i / per, r = i % per;
-    return r < n1 ? ItemRef{ITEM_STATS, int32_t(lag + q), int32_t(r)} : ItemRef{ITEM_SCAN, int32_t(q), 0};
+__device__ __forceinline__ ItemRef decode_item(uint32_t i, uint32_t B, uint32_t n1, uint32_t nt, uint32_t lag1,
+                                               uint32_t lag2) {
+  // steps [0, lag1): stats | [lag1, lag2): stats, scan | [lag2, B): stats, scan, draws |
+  // [B, B + lag1): scan, draws | [B + lag1, B + lag2): draws
+  const uint32_t bounds[5] = {lag1, lag2, B, B + lag1, B + lag2};
+  uint32_t s0 = 0;
+  for (int r = 0; r < 5; ++r) {
+    const bool has_st = r <= 2, has_sc = r >= 1 && r <= 3, has_dr = r >= 2;
+    const uint32_t per = (has_st ? n1 : 0u) + (has_sc ? 1u : 0u) + (has_dr ? nt : 0u);
+    const uint32_t steps = bounds[r] - s0;
+    if (i < steps * per) {
+      const uint32_t s = s0 + i / per;
+      uint32_t k = i % per;
+      if (has_st) {
+        if (k < n1) return ItemRef{ITEM_STATS, int32_t(s), int32_t(k)};
+        k -= n1;
+      }
+      if (has_sc) {
+        if (k == 0) return ItemRef{ITEM_SCAN, int32_t(s - lag1), 0};
+        k -= 1;
+      }
+      return ItemRef{ITEM_DRAW, int32_t(s - lag2), int32_t(k)};
+    }
+    i -= steps * per;
+    s0 = bounds[r];
   }
-  i -= mid;
-  if (i < lag) return ItemRef{ITEM_SCAN, int32_t(B - lag + i), 0};
-  i -= lag;
-  return ItemRef{ITEM_DRAW, int32_t(i / nt), int32_t(i % nt)};
+  return ItemRef{ITEM_DRAW, 0, 0};     // not reached: the grid holds exactly B * (n1 + 1 + nt) items
 }
 
 struct DrawShared {
@@ -1490,11 +1516,10 @@ __global__ __launch_bounds__(kDrawBlock) __attribute__((amdgpu_waves_per_eu(kWpe
   __shared__ uint32_t seen[SV_MAX_GAMMA / 32];
   __shared__ DrawShared ds;
   __shared__ PickShared psh;
-  __shared__ LeanShared ls;
   __shared__ int s_flag;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const ItemRef it = decode_item(blockIdx.x, uint32_t(prm.B), uint32_t(prm.n1), uint32_t(prm.ntask),
-                                 uint32_t(prm.lag));
+                                 uint32_t(prm.lag1), uint32_t(prm.lag2));
   const int64_t b = it.b;
   int32_t* ready = prm.ready + b * kCtrStride;
   if (it.kind == ITEM_STATS) {
@@ -1552,8 +1577,17 @@ __global__ __launch_bounds__(kDrawBlock) __attribute__((amdgpu_waves_per_eu(kWpe
     if (tid == 0 && prm.start && job.new_start >= 0) prm.start[b] = job.new_start;
     if (job.kind == JOB_NONE) {
       if (tid == 0) finish(prm, b, job, -1, 0u);
-    } else if (!(prm.nch <= kLeanChunks && prm.ntask <= 64 && pick_lean<T>(prm, b, job, psh, ls))) {
-      pick_seq<T>(prm, b, job, psh);
+    } else {
+      int general = 1;
+      if (prm.nch <= kLeanChunks && prm.ntask <= 64) {
+        if (wave == 0) {
+          const int r = pick_lean<T>(prm, b, job);
+          if (lane == 0) s_flag = r;
+        }
+        __syncthreads();
+        general = s_flag;
+      }
+      if (general) pick_seq<T>(prm, b, job, psh);
     }
     if (tid == 0) {                                  // every item of sequence b has finished
       st_dev(ready, 0);
@@ -1569,7 +1603,7 @@ int resident_workgroups() {
   if (hipGetDevice(&dev) != hipSuccess) return 1024;
   if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
   if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0) ncu = 256;
-  const int r = ncu * kWpe;          // four 4-wave workgroups per compute unit at 4 waves per SIMD
+  const int r = ncu * kWpe;          // kWpe 4-wave workgroups per compute unit at kWpe waves per SIMD
   if (dev >= 0 && dev < 64) cached[dev] = r;
   return r;
 }
@@ -1589,10 +1623,16 @@ hipError_t launch_typed(const DensePlan& plan, const DenseArgs& a, hipStream_t s
   dp.flags = a.flags;
   dp.n1 = plan.n1; dp.ntask = plan.ntask; dp.nch = plan.nch;
   const int R = resident_workgroups();
-  int64_t lag = (int64_t(R) * kLagRounds + plan.n1 - 1) / plan.n1;
-  if (lag > plan.B) lag = plan.B;
-  if (lag < 1) lag = 1;
-  dp.lag = int32_t(lag);
+  auto lag_for = [&](int64_t rounds) {          // sequences whose statistics fill `rounds` resident rounds
+    if (rounds <= 0) return int64_t(plan.B);
+    int64_t l = (int64_t(R) * rounds + plan.n1 - 1) / plan.n1;
+    return l < 1 ? int64_t(1) : (l > plan.B ? plan.B : l);
+  };
+  const int64_t lag1 = lag_for(kScanLagRounds);
+  int64_t lag2 = lag_for(kDrawLagRounds);
+  if (lag2 < lag1) lag2 = lag1;
+  dp.lag1 = int32_t(lag1);
+  dp.lag2 = int32_t(lag2);
   dp.n_items = int32_t(plan.B * (int64_t(plan.n1) + 1 + plan.ntask));
   dp.ready = reinterpret_cast<int32_t*>(ws + plan.off_ready);
   dp.done = reinterpret_cast<int32_t*>(ws + plan.off_done);
