@@ -156,6 +156,50 @@ __device__ __forceinline__ double dpp_d(double old, double v) {
   return __hiloint2double(dpp_i<CTRL, ROWS>(__double2hiint(old), __double2hiint(v)),
                           dpp_i<CTRL, ROWS>(__double2loint(old), __double2loint(v)));
 }
+// v moved by CTRL where every lane's source lies inside its row and every row takes part (no `old` operand needed).
+template <int CTRL>
+__device__ __forceinline__ double dpp_full_d(double v) {
+  return __hiloint2double(__builtin_amdgcn_mov_dpp(__double2hiint(v), CTRL, 0xF, 0xF, true),
+                          __builtin_amdgcn_mov_dpp(__double2loint(v), CTRL, 0xF, 0xF, true));
+}
+// The job's fields are the same in every lane (read from shared memory after a barrier): moved to scalar registers,
+// so that branches on them are uniform.
+__device__ __forceinline__ Job uniform_job(const Job& j) {
+  Job r;
+  const uint32_t* s = reinterpret_cast<const uint32_t*>(&j);
+  uint32_t* d = reinterpret_cast<uint32_t*>(&r);
+#pragma unroll
+  for (int i = 0; i < int(sizeof(Job) / 4); ++i) d[i] = __builtin_amdgcn_readfirstlane(s[i]);
+  return r;
+}
+
+// A job as three 16-byte vectors: the form in which it is handed to the functions that are not inlined (vectors
+// travel in registers, where a structure argument would be copied through the stack).
+struct JobWords {
+  uint4 w[3];
+};
+static_assert(sizeof(Job) == sizeof(JobWords), "a job is three 16-byte words");
+__device__ __forceinline__ void job_words(const Job& j, uint4& a, uint4& b, uint4& c) {
+  JobWords w;
+  __builtin_memcpy(&w, &j, sizeof(Job));
+  a = w.w[0];
+  b = w.w[1];
+  c = w.w[2];
+}
+__device__ __forceinline__ Job job_from_words(uint4 a, uint4 b, uint4 c) {
+  JobWords w;
+  w.w[0] = a;
+  w.w[1] = b;
+  w.w[2] = c;
+  Job j;
+  __builtin_memcpy(&j, &w, sizeof(Job));
+  return uniform_job(j);
+}
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+  const uint64_t u = uint64_t(v);
+  return int64_t((uint64_t(__builtin_amdgcn_readfirstlane(uint32_t(u >> 32))) << 32) |
+                 __builtin_amdgcn_readfirstlane(uint32_t(u)));
+}
 __device__ __forceinline__ double readlane_d(double v, int l) {
   return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
                           __builtin_amdgcn_readlane(__double2loint(v), l));
@@ -165,10 +209,10 @@ __device__ __forceinline__ float readlane_f(float v, int l) {
 }
 
 __device__ __forceinline__ double wave_sum(double v) {
-  v += dpp_d<kDppXor1>(0.0, v);
-  v += dpp_d<kDppXor2>(0.0, v);
-  v += dpp_d<kDppHalfMirror>(0.0, v);
-  v += dpp_d<kDppMirror>(0.0, v);
+  v += dpp_full_d<kDppXor1>(v);
+  v += dpp_full_d<kDppXor2>(v);
+  v += dpp_full_d<kDppHalfMirror>(v);
+  v += dpp_full_d<kDppMirror>(v);
   return (readlane_d(v, 0) + readlane_d(v, 16)) + (readlane_d(v, 32) + readlane_d(v, 48));
 }
 
@@ -705,7 +749,7 @@ __device__ __forceinline__ Job seq_scan(DP& prm, int64_t b, bool leader, uint32_
 // ldexp. Every workgroup that draws fills the table first (one entry per thread).
 __shared__ double s_exp2tab[256];
 
-// The core assumes a finite y >= -1020.
+// The core takes a finite y in [-2000, 1023]; below -1075 its result is exactly 0 (ldexp underflows).
 __device__ __forceinline__ double fexp_core(double y) {
   const double kMagic = 26388279066624.0;                      // 1.5 * 2^44: its ulp is 1/256
   const double t = y + kMagic;
@@ -718,11 +762,9 @@ __device__ __forceinline__ double fexp_core(double y) {
   return ldexp(s_exp2tab[n & 255] * q, n >> 8);
 }
 
-// Any y: below the range (y < -1074), -inf and NaN are evaluated on garbage and replaced by 0 (NaN stays NaN).
-__device__ __forceinline__ double fexp_scaled(double y) {
-  const double res = fexp_core(y >= -1074.0 ? y : 0.0);
-  return (y >= -1074.0) ? res : (y != y ? y : 0.0);
-}
+// Any y up to 1023: the argument is clamped at -2000 (one instruction), so -inf and every y below -1075 give exactly
+// 0. NaN gives 0 too: a row holding NaN or +inf is reported as non-finite before any weight of it is used.
+__device__ __forceinline__ double fexp_scaled(double y) { return fexp_core(fmax(y, -2000.0)); }
 
 // The exponent (z - m) * log2(e) / T of an element, formed as z * c2 + nm with one rounding, nm = -(m * c2). Every
 // evaluation of an element's weight goes through here, so repeated evaluations agree bit for bit.
@@ -827,29 +869,19 @@ __device__ __forceinline__ void st_task(double4* p, double4 v) {
   st_dev(d + 3, v.w);
 }
 
-// Elements of the lane: all finite and within exp's range of the reference max (so the guard-free core applies).
-__device__ __forceinline__ bool lane_safe(const float* z, double m, double c2) {
-  float lo = z[0], hi = z[0];
-#pragma unroll
-  for (int e = 1; e < kPer; ++e) { lo = fminf(lo, z[e]); hi = fmaxf(hi, z[e]); }
-  // NaN makes both comparisons false; +inf fails the upper bound check; -inf fails the lower one
-  return (double(lo) - m) * c2 >= -1020.0 && double(hi) <= m && hi == hi && lo == lo;
-}
-
 // One lane's kPer elements: exp of both logits, the residual's sign test and the sums. A and D are accumulated as
-// fma(e, w, .) with w = 1 where the residual is positive and 0 elsewhere.
-template <int KIND, bool SAFE>
+// fma(e, w, .) with w = 1 where the residual is positive and 0 elsewhere; amb is set when an element's sign could not
+// be decided (the caller recomputes which one).
+template <int KIND>
 __device__ __forceinline__ void mass_lane(const float* zt, const float* zd, double c2, double nmt, double nmd,
                                           int64_t i0, int32_t d, double k_lo, double k_hi, double& st, double& sd,
-                                          double& A, double& D, uint32_t& amb) {
+                                          double& A, double& D, bool& amb) {
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
-    const double xt = xarg(zt[e], c2, nmt);
-    const double et = SAFE ? fexp_core(xt) : fexp_scaled(xt);
+    const double et = fexp_scaled(xarg(zt[e], c2, nmt));
     st += et;
     if constexpr (KIND == JOB_RESID) {
-      const double xd = xarg(zd[e], c2, nmd);
-      const double ed = SAFE ? fexp_core(xd) : fexp_scaled(xd);
+      const double ed = fexp_scaled(xarg(zd[e], c2, nmd));
       sd += ed;
       // r_e > 0 iff et * (S_d / S_t) > ed; kappa brackets S_d / S_t within kBand
       const bool pos = et * k_lo > ed;
@@ -857,10 +889,13 @@ __device__ __forceinline__ void mass_lane(const float* zt, const float* zd, doub
       const double w = pos ? 1.0 : 0.0;
       A = fma(et, w, A);
       D = fma(ed, w, D);
-      amb |= (!(pos || neg) ? 1u : 0u) << e;
+      amb |= !(pos || neg);
     } else if constexpr (KIND == JOB_ONEHOT) {
       A = fma(et, (i0 + e == d) ? 0.0 : 1.0, A);
     }
+    // the sums are pinned here every two elements: otherwise the compiler defers them to the end of the chunk and
+    // holds every exp of the lane at once, past the loop's register budget (other waves on the SIMD hide latency)
+    if (e & 1) asm volatile("" : "+v"(st), "+v"(sd), "+v"(A), "+v"(D));
   }
 }
 
@@ -868,18 +903,12 @@ __device__ __forceinline__ void mass_lane(const float* zt, const float* zd, doub
 // chunk's record.
 template <int KIND>
 __device__ __forceinline__ void chunk_body(DP& prm, const Job& job, int64_t b, int64_t c, int64_t i0,
-                                           const float* zt, const float* zd, double mt, double md, double c2,
-                                           double nmt, double nmd, double k_lo, double k_hi, double& st, double& sd) {
+                                           const float* zt, const float* zd, double mt, double c2, double nmt,
+                                           double nmd, double k_lo, double k_hi, double& st, double& sd) {
   const int lane = threadIdx.x & 63;
-  bool safe = i0 + kPer <= prm.V && lane_safe(zt, mt, c2);
-  if constexpr (KIND == JOB_RESID) safe = safe && lane_safe(zd, md, c2);
-  safe = __all(safe);
   double A = 0.0, D = 0.0, cst = 0.0, csd = 0.0;     // this chunk's sums
-  uint32_t amb = 0;                                  // bit e: element e undecided
-  if (safe)
-    mass_lane<KIND, true>(zt, zd, c2, nmt, nmd, i0, job.d, k_lo, k_hi, cst, csd, A, D, amb);
-  else
-    mass_lane<KIND, false>(zt, zd, c2, nmt, nmd, i0, job.d, k_lo, k_hi, cst, csd, A, D, amb);
+  bool amb = false;
+  mass_lane<KIND>(zt, zd, c2, nmt, nmd, i0, job.d, k_lo, k_hi, cst, csd, A, D, amb);
   st += cst;
   sd += csd;
   if constexpr (KIND == JOB_BONUS) A = cst;          // the bonus draws from p: the chunk's whole sum
@@ -888,8 +917,22 @@ __device__ __forceinline__ void chunk_body(DP& prm, const Job& job, int64_t b, i
   ChunkRec* rec = prm.chunks + b * prm.nch + c;
   int namb = 0;
   if constexpr (KIND == JOB_RESID) {
-    if (__any(amb != 0)) {                           // rare: list the undecided elements in element order
-      const int mine = __popc(amb);
+    if (__any(amb)) {                                // rare: list the undecided elements in element order
+      uint32_t bits = 0;                             // bit e: element e undecided, recomputed exactly as above
+      double et[kPer], ed[kPer];
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        // the logits pass through an empty asm so that the compiler recomputes here instead of keeping the main
+        // loop's exps alive across the reductions (same operations on the same values: the same bits)
+        float a = zt[e], d = zd[e];
+        asm volatile("" : "+v"(a), "+v"(d));
+        et[e] = fexp_scaled(xarg(a, c2, nmt));
+        ed[e] = fexp_scaled(xarg(d, c2, nmd));
+        const bool pos = et[e] * k_lo > ed[e];
+        const bool neg = et[e] * k_hi <= ed[e];
+        bits |= (!(pos || neg) ? 1u : 0u) << e;
+      }
+      const int mine = __popc(bits);
       int before = mine;                             // inclusive prefix over lanes
       for (int o = 1; o < 64; o <<= 1) {
         const int n = __shfl_up(before, o);
@@ -897,11 +940,12 @@ __device__ __forceinline__ void chunk_body(DP& prm, const Job& job, int64_t b, i
       }
       namb = __shfl(before, 63);
       int pos = before - mine;
+#pragma unroll
       for (int e = 0; e < kPer; ++e) {
-        if ((amb >> e) & 1u) {                       // recomputed exactly as in mass_lane
+        if ((bits >> e) & 1u) {
           if (pos < kAmbMax) {
-            st_dev(&rec->et[pos], fexp_scaled(xarg(zt[e], c2, nmt)));
-            st_dev(&rec->ed[pos], fexp_scaled(xarg(zd[e], c2, nmd)));
+            st_dev(&rec->et[pos], et[e]);
+            st_dev(&rec->ed[pos], ed[e]);
           }
           ++pos;
         }
@@ -917,13 +961,14 @@ __device__ __forceinline__ void chunk_body(DP& prm, const Job& job, int64_t b, i
 }
 
 // Chunk loop of the mass pass for one kind of draw (KIND is uniform per sequence): chunks c0, c0 + stride, ... below
-// c1. Chunks that lie wholly inside a 16-byte aligned row take the vector loop, with the next chunk's loads in flight
-// while the current one is evaluated; a partial last chunk, or a row off the 16-byte grid, takes element loads.
+// c1. Chunks that lie wholly inside a 16-byte aligned row take the vector loop, with the next two chunks' loads in
+// flight while the current one is evaluated; a partial last chunk, or a row off the 16-byte grid, takes element loads.
 template <typename T, int KIND>
 __device__ __forceinline__ void mass_chunks(DP& prm, const Job& job, int64_t b, int64_t c0, int64_t c1,
                                             int stride, const T* rt, const T* rd, bool vec, double mt,
                                             double& st, double& sd) {
   constexpr int NV = kPer / Vec<T>::kEPV;
+  constexpr int EPV = Vec<T>::kEPV;
   const int lane = threadIdx.x & 63;
   const int64_t V = prm.V;
   const double md = job.m_d;
@@ -932,38 +977,53 @@ __device__ __forceinline__ void mass_chunks(DP& prm, const Job& job, int64_t b, 
   const double k_lo = job.kappa * (1.0 - kBand), k_hi = job.kappa * (1.0 + kBand);
   const int64_t step = int64_t(stride) * kChunk;
   float zt[kPer], zd[kPer];
-  const int64_t c_vec = vec ? min<int64_t>(c1, V / kChunk) : c0;   // chunks below V / kChunk are whole
+  // the chunk range is the same in every lane of the wave: kept in scalar registers, so the loop's branches are uniform
+  c0 = uniform_i64(c0);
+  c1 = uniform_i64(c1);
+  const int64_t c_vec = uniform_i64(vec ? min<int64_t>(c1, V / kChunk) : c0);   // chunks below V / kChunk are whole
   int64_t c = c0;
   int64_t i0 = c0 * kChunk + int64_t(lane) * kPer;
   if (c < c_vec) {
-    uint4 nt[NV], nd[NV];                            // the chunk in flight
+    // two buffer sets used in turn (the loop is unrolled twice so that no register copy waits on a load): while
+    // chunk c is evaluated, the loads of chunks c + stride and c + 2 * stride are in flight
+    uint4 xt[2][NV], xd[2][NV];
     const uint4* pt = reinterpret_cast<const uint4*>(rt + i0);
-    const uint4* pd = KIND == JOB_RESID ? reinterpret_cast<const uint4*>(rd + i0) : nullptr;
-    const int64_t vstep = step / Vec<T>::kEPV;       // in 16-byte vectors
+    const uint4* pd = KIND == JOB_RESID ? reinterpret_cast<const uint4*>(rd + i0) : pt;
+    const int64_t vstep = step / EPV;                // in 16-byte vectors
 #pragma unroll
-    for (int k = 0; k < NV; ++k) nt[k] = gload4(pt + k);
-    if constexpr (KIND == JOB_RESID) {
+    for (int h = 0; h < 2; ++h) {
+      const int64_t ahead = (h == 1 && c + stride < c_vec) ? vstep : 0;
 #pragma unroll
-      for (int k = 0; k < NV; ++k) nd[k] = gload4(pd + k);
-    }
-    for (; c < c_vec; c += stride, i0 += step, pt += vstep) {
-#pragma unroll
-      for (int k = 0; k < NV; ++k) Vec<T>::unpack(nt[k], zt + k * Vec<T>::kEPV);
-      if constexpr (KIND == JOB_RESID) {
-#pragma unroll
-        for (int k = 0; k < NV; ++k) Vec<T>::unpack(nd[k], zd + k * Vec<T>::kEPV);
+      for (int k = 0; k < NV; ++k) {
+        xt[h][k] = gload4(pt + ahead + k);
+        if constexpr (KIND == JOB_RESID) xd[h][k] = gload4(pd + ahead + k);
       }
-      if (c + stride < c_vec) {                      // next chunk's loads overlap this chunk's arithmetic
-#pragma unroll
-        for (int k = 0; k < NV; ++k) nt[k] = gload4(pt + vstep + k);
-        if constexpr (KIND == JOB_RESID) {
-#pragma unroll
-          for (int k = 0; k < NV; ++k) nd[k] = gload4(pd + vstep + k);
-        }
-      }
-      if constexpr (KIND == JOB_RESID) pd += vstep;
-      chunk_body<KIND>(prm, job, b, c, i0, zt, zd, mt, md, c2, nmt, nmd, k_lo, k_hi, st, sd);
     }
+    // chunk c from buffer set h: unpack, refill the set with the chunk after next (past the last chunk: the current
+    // one again, so that every load is unconditional), evaluate
+    auto half = [&](uint4 (&bt)[NV], uint4 (&bd)[NV]) {
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        Vec<T>::unpack(bt[k], zt + k * EPV);
+        if constexpr (KIND == JOB_RESID) Vec<T>::unpack(bd[k], zd + k * EPV);
+      }
+      const int64_t ahead = c + 2 * stride < c_vec ? 2 * vstep : 0;
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        bt[k] = gload4(pt + ahead + k);
+        if constexpr (KIND == JOB_RESID) bd[k] = gload4(pd + ahead + k);
+      }
+      chunk_body<KIND>(prm, job, b, c, i0, zt, zd, mt, c2, nmt, nmd, k_lo, k_hi, st, sd);
+      c += stride;
+      i0 += step;
+      pt += vstep;
+      pd += vstep;
+    };
+    while (c + stride < c_vec) {                     // two chunks per pass, one from each set
+      half(xt[0], xd[0]);
+      half(xt[1], xd[1]);
+    }
+    if (c < c_vec) half(xt[0], xd[0]);               // an odd last chunk
   }
   for (; c < c1; c += stride, i0 += step) {
 #pragma unroll
@@ -972,7 +1032,7 @@ __device__ __forceinline__ void mass_chunks(DP& prm, const Job& job, int64_t b, 
 #pragma unroll
       for (int e = 0; e < kPer; ++e) zd[e] = elem_or_ninf<T>(rd, i0 + e, V);
     }
-    chunk_body<KIND>(prm, job, b, c, i0, zt, zd, mt, md, c2, nmt, nmd, k_lo, k_hi, st, sd);
+    chunk_body<KIND>(prm, job, b, c, i0, zt, zd, mt, c2, nmt, nmd, k_lo, k_hi, st, sd);
   }
 }
 
@@ -1018,6 +1078,7 @@ struct PickShared {
   double base;
   int namb, cand, last, hit, lastpos;
 };
+__shared__ PickShared s_pick;     // at file scope: reached with LDS instructions from the functions not inlined
 
 // The sequence's drawn token and flags (the scan's bits plus what the draw adds), written once.
 __device__ __forceinline__ void finish(DP& prm, int64_t b, const Job& job, int32_t tok, uint32_t extra) {
@@ -1028,8 +1089,9 @@ __device__ __forceinline__ void finish(DP& prm, int64_t b, const Job& job, int32
 // The exact search inside chunk cstar by the whole workgroup (thread tid holds kPT consecutive elements): the first
 // element whose running sum from cbase exceeds t, else (clamp, or rounding) the chunk's last element with weight.
 template <typename T>
-__device__ void search_chunk(DP& prm, int64_t b, const Job& job, int64_t cstar, double cbase, bool clamp,
-                             double t, double mt, double inv_st, double md, double inv_sd, bool use_p, PickShared& sh) {
+__device__ __forceinline__ void search_chunk(DP& prm, int64_t b, const Job& job, int64_t cstar, double cbase, bool clamp, double t,
+                             double mt, double inv_st, double md, double inv_sd, bool use_p) {
+  PickShared& sh = s_pick;
   constexpr int BLOCK = kDrawBlock;
   const int tid = threadIdx.x;
   const bool resid = job.kind == JOB_RESID;
@@ -1062,7 +1124,9 @@ __device__ void search_chunk(DP& prm, int64_t b, const Job& job, int64_t cstar, 
 // The pick of sequence b by one workgroup, after every task of the sequence has finished: normalisers from the task
 // partials, chunk masses, their running sum, the chunk that holds t = u * total, and an exact search inside it.
 template <typename T>
-__device__ __noinline__ void pick_seq(DP& prm_arg, int64_t b, const Job& job, PickShared& sh) {
+__device__ __forceinline__ void pick_seq(DP& prm_arg, int64_t b, uint4 j0, uint4 j1, uint4 j2) {
+  PickShared& sh = s_pick;
+  const Job job = job_from_words(j0, j1, j2);
   DP& prm = uniform_params(prm_arg);
   constexpr int BLOCK = kDrawBlock, NW = kDrawWaves;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1204,7 +1268,7 @@ __device__ __noinline__ void pick_seq(DP& prm_arg, int64_t b, const Job& job, Pi
     if (tid == 0) finish(prm, b, job, -1, 0u);
     return;
   }
-  search_chunk<T>(prm, b, job, cstar, clamp ? 0.0 : sh.base, clamp, t, mt, inv_st, md, inv_sd, use_p, sh);
+  search_chunk<T>(prm, b, job, cstar, clamp ? 0.0 : sh.base, clamp, t, mt, inv_st, md, inv_sd, use_p);
 }
 
 // The common case of the pick, for rows of at most kLeanChunks chunks and at most 64 draw tasks whose chunk records
@@ -1406,14 +1470,21 @@ struct DrawShared {
   int nan[kDrawWaves];
   double sum[kDrawWaves][2];
 };
+// Workgroup-shared state of the draw tasks and the pick, at file scope so that the functions that are not inlined
+// reach it with LDS instructions (a reference parameter would be a generic pointer: flat accesses through the vector
+// memory path).
+__shared__ DrawShared s_draw;
+__shared__ int s_flag;
+
 
 // Draw task `task` of sequence b, once its job is published: the float64 masses of chunks
 // [task * nch / ntask, (task + 1) * nch / ntask) of the draw row(s), dealt to the waves in turn, and the task's
 // partial normalisers. Returns true in the workgroup whose task is the sequence's last to finish.
 template <typename T>
-__device__ __noinline__ bool draw_task(DP& prm_arg, int64_t b, int task, const Job& job, DrawShared& ds,
-                                       int* s_flag) {
+__device__ __forceinline__ bool draw_task(DP& prm_arg, int64_t b, int task, uint4 j0, uint4 j1, uint4 j2) {
   DP& prm = uniform_params(prm_arg);
+  const Job job = job_from_words(j0, j1, j2);
+  DrawShared& ds = s_draw;
   constexpr int NW = kDrawWaves;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   if (job.kind != JOB_NONE) {                       // uniform over the workgroup
@@ -1476,9 +1547,9 @@ __device__ __noinline__ bool draw_task(DP& prm_arg, int64_t b, int task, const J
   // this workgroup's records are complete before it is counted; the last one picks
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tid == 0) *s_flag = ctr_add(prm.done + b * kCtrStride) == prm.ntask - 1;
+  if (tid == 0) s_flag = ctr_add(prm.done + b * kCtrStride) == prm.ntask - 1;
   __syncthreads();
-  return *s_flag != 0;
+  return s_flag != 0;
 }
 
 __device__ __forceinline__ void ctr_inc(int32_t* p) {
@@ -1487,17 +1558,17 @@ __device__ __forceinline__ void ctr_inc(int32_t* p) {
 
 // Waits (thread 0 polls, the others hold at the barrier) until the counter reaches `target`. Returns false when it
 // gave up after kSpinCap polls, which only happens if the hardware broke the dispatch order.
-__device__ __forceinline__ bool wait_count(const int32_t* ctr, int32_t target, int* s_flag) {
+__device__ __forceinline__ bool wait_count(const int32_t* ctr, int32_t target) {
   if (threadIdx.x == 0) {
     int32_t polls = 0;
     while (ld_ctr(ctr) < target && polls < kSpinCap) {
       __builtin_amdgcn_s_sleep(SV_SLEEP);
       ++polls;
     }
-    *s_flag = polls < kSpinCap;
+    s_flag = polls < kSpinCap;
   }
   __syncthreads();
-  return *s_flag != 0;
+  return s_flag != 0;
 }
 
 // One workgroup per work item, in the queue order of decode_item (the hardware dispatches workgroups in index
@@ -1514,9 +1585,6 @@ __global__ __launch_bounds__(kDrawBlock) __attribute__((amdgpu_waves_per_eu(kWpe
   __shared__ float sh_f[kDrawWaves];
   __shared__ double sh_d[kDrawWaves];
   __shared__ uint32_t seen[SV_MAX_GAMMA / 32];
-  __shared__ DrawShared ds;
-  __shared__ PickShared psh;
-  __shared__ int s_flag;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const ItemRef it = decode_item(blockIdx.x, uint32_t(prm.B), uint32_t(prm.n1), uint32_t(prm.ntask),
                                  uint32_t(prm.lag1), uint32_t(prm.lag2));
@@ -1533,7 +1601,7 @@ __global__ __launch_bounds__(kDrawBlock) __attribute__((amdgpu_waves_per_eu(kWpe
     // the scan and the pick are short serial chains on the critical path: their waves get issue priority over the
     // streaming and float64 waves that share their SIMDs
     __builtin_amdgcn_s_setprio(3);
-    const bool ok = wait_count(ready, prm.n1, &s_flag);
+    const bool ok = wait_count(ready, prm.n1);
     if (wave == 0) {
       Job j;
       if (ok) {
@@ -1568,11 +1636,13 @@ __global__ __launch_bounds__(kDrawBlock) __attribute__((amdgpu_waves_per_eu(kWpe
       j.flags = SV_FLAG_NONFINITE | SV_FLAG_ID_RANGE;
       j.new_start = -1;
     }
-    ds.job = j;
+    s_draw.job = j;
   }
   __syncthreads();
-  const Job job = ds.job;
-  if (draw_task<T>(prm, b, it.sub, job, ds, &s_flag)) {
+  const Job job = uniform_job(s_draw.job);
+  uint4 j0, j1, j2;
+  job_words(job, j0, j1, j2);
+  if (draw_task<T>(prm, b, it.sub, j0, j1, j2)) {
     __builtin_amdgcn_s_setprio(3);
     if (tid == 0 && prm.start && job.new_start >= 0) prm.start[b] = job.new_start;
     if (job.kind == JOB_NONE) {
@@ -1587,7 +1657,7 @@ __global__ __launch_bounds__(kDrawBlock) __attribute__((amdgpu_waves_per_eu(kWpe
         __syncthreads();
         general = s_flag;
       }
-      if (general) pick_seq<T>(prm, b, job, psh);
+      if (general) pick_seq<T>(prm, b, j0, j1, j2);
     }
     if (tid == 0) {                                  // every item of sequence b has finished
       st_dev(ready, 0);
