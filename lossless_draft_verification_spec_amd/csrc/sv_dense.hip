@@ -306,8 +306,6 @@ __device__ __forceinline__ int32_t ctr_add(int32_t* p) {
 // 1. row statistics
 // ----------------------------------------------------------------------------------------------------------------
 
-struct ChunkRec;
-
 // Everything one call needs, shared by both kinds of work item.
 struct DenseParams {
   const void* tgt; int64_t t_seq, t_row;
@@ -320,13 +318,17 @@ struct DenseParams {
   uint8_t* accept; int32_t* n_acc; int32_t* token; float* p_draft; float* q_draft; uint32_t* flags;
   // work queue: per sequence n1 statistics items, one scan and ntask draw tasks, in the order of decode_item
   int32_t n1; int32_t ntask; int32_t lag1; int32_t lag2; int32_t n_items;
-  int64_t nch;                                // 1024-element chunks per row
+  int64_t nch;                                // kChunk-element chunks per row
   int32_t* ready;                             // per b (stride kCtrStride): statistics items finished
   int32_t* done;                              // per b (stride kCtrStride): draw tasks finished
   Job* jobs;                                  // per b: the draw job
   Partial1* part1;                            // per (tensor, b, row, segment)
   double4* part2;            // per (b, task): reference max, sum e_t (relative to it), m_d, sum e_d
-  ChunkRec* chunks;          // per (b, chunk), see ChunkRec
+  // chunk records of the mass pass, one array per field so that the pick reads them coalesced (see chunk_body)
+  double* recA;              // per (b, chunk)
+  double* recD;              // per (b, chunk)
+  int32_t* recN;             // per (b, chunk)
+  double2* recU;             // per (b, chunk, kAmbMax)
   double* masses;            // per (b, chunk): chunk masses, written by the pick when the chunks exceed one tile
 };
 
@@ -846,16 +848,17 @@ __device__ __forceinline__ double lane_sum16(const double* w) {
   return s;
 }
 
-// Per-chunk record of the mass pass. A = sum of e_t and D = sum of e_d over the elements whose residual is positive;
-// up to kAmbMax elements whose sign could not be decided are kept as (e_t, e_d) pairs (n_amb of them); n_amb > kAmbMax
-// means the chunk must be recomputed from the logits.
+// Per-chunk record of the mass pass: A = sum of e_t and D = sum of e_d over the elements whose residual is known to be
+// positive (bonus and one-hot: A = sum of e_t over every element but the one-hot id, D = 0); N = number of elements
+// whose sign could not be decided, kept as (e_t, e_d) pairs in U when N <= kAmbMax (N > kAmbMax: the chunk must be
+// recomputed from the logits). The exps are relative to the draw row's max, except for a bonus row, where they are
+// relative to the max of the chunk's draw task (the first field of that task's partial).
 constexpr int kAmbMax = 4;
-struct alignas(16) ChunkRec {
-  double A, D;
-  int32_t n_amb, pad0;
-  double mref;                       // the max the exps are taken against (for a bonus row: the task's max)
-  double et[kAmbMax], ed[kAmbMax];
-};
+
+// The draw task that chunk c belongs to: the largest t with t * nch / ntask <= c.
+__device__ __forceinline__ int task_of_chunk(int64_t c, int64_t nch, int ntask) {
+  return int(((c + 1) * ntask - 1) / nch);
+}
 
 __device__ __forceinline__ double4 ld_task(const double4* p) {
   const double* d = reinterpret_cast<const double*>(p);
@@ -914,7 +917,7 @@ __device__ __forceinline__ void chunk_body(DP& prm, const Job& job, int64_t b, i
   if constexpr (KIND == JOB_BONUS) A = cst;          // the bonus draws from p: the chunk's whole sum
   A = wave_sum(A);
   if constexpr (KIND == JOB_RESID) D = wave_sum(D);
-  ChunkRec* rec = prm.chunks + b * prm.nch + c;
+  const int64_t rc = b * prm.nch + c;
   int namb = 0;
   if constexpr (KIND == JOB_RESID) {
     if (__any(amb)) {                                // rare: list the undecided elements in element order
@@ -944,20 +947,20 @@ __device__ __forceinline__ void chunk_body(DP& prm, const Job& job, int64_t b, i
       for (int e = 0; e < kPer; ++e) {
         if ((bits >> e) & 1u) {
           if (pos < kAmbMax) {
-            st_dev(&rec->et[pos], et[e]);
-            st_dev(&rec->ed[pos], ed[e]);
+            st_dev(&prm.recU[rc * kAmbMax + pos].x, et[e]);
+            st_dev(&prm.recU[rc * kAmbMax + pos].y, ed[e]);
           }
           ++pos;
         }
       }
     }
   }
-  if (lane == 0) {
-    st_dev(&rec->A, A);
-    st_dev(&rec->D, D);
-    st_dev(&rec->n_amb, namb);
-    st_dev(&rec->mref, mt);
-  }
+  // every lane stores the same values (no branch around the stores: a store skipped on some path would leave the
+  // compiler's count of outstanding memory operations too low, and the next chunk's wait would also wait for the
+  // loads still in flight)
+  st_dev(&prm.recA[rc], A);
+  st_dev(&prm.recD[rc], D);
+  st_dev(&prm.recN[rc], namb);
 }
 
 // Chunk loop of the mass pass for one kind of draw (KIND is uniform per sequence): chunks c0, c0 + stride, ... below
@@ -1132,7 +1135,10 @@ __device__ __forceinline__ void pick_seq(DP& prm_arg, int64_t b, uint4 j0, uint4
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ntask = prm.ntask;
   const int64_t nch = prm.nch, V = prm.V;
-  const ChunkRec* ch = prm.chunks + b * nch;
+  const double* rA = prm.recA + b * nch;
+  const double* rD = prm.recD + b * nch;
+  const int32_t* rN = prm.recN + b * nch;
+  const double2* rU = prm.recU + b * nch * kAmbMax;
   double* mg = prm.masses + b * nch;
   const double4* ps = prm.part2 + b * ntask;
   const double c2 = prm.c2;
@@ -1178,15 +1184,18 @@ __device__ __forceinline__ void pick_seq(DP& prm_arg, int64_t b, uint4 j0, uint4
     __syncthreads();
     for (int i = tid; i < n; i += BLOCK) {
       const int64_t c = t0 + i;
-      const ChunkRec& rc = ch[c];
-      const int namb = ld_dev(&rc.n_amb);
+      const int namb = ld_dev(rN + c);
       if (use_p || namb > kAmbMax) {
         sh.amb[atomicAdd(&sh.namb, 1)] = i;
       } else {
-        const double f = bonus ? fexp_scaled((ld_dev(&rc.mref) - mt) * c2) : 1.0;
-        double m = f * (ld_dev(&rc.A) * inv_st - ld_dev(&rc.D) * inv_sd);
+        double f = 1.0;
+        if (bonus) {                                   // the chunk's exps are relative to its task's max
+          const double mref = ld_dev(reinterpret_cast<const double*>(ps + task_of_chunk(c, nch, ntask)));
+          f = mref == -INFINITY ? 0.0 : fexp_scaled((mref - mt) * c2);
+        }
+        double m = f * (ld_dev(rA + c) * inv_st - ld_dev(rD + c) * inv_sd);
         for (int q = 0; q < namb; ++q) {               // undecided elements, exactly: max(p - q, 0)
-          const double r = ld_dev(&rc.et[q]) * inv_st - ld_dev(&rc.ed[q]) * inv_sd;
+          const double r = ld_dev(&rU[c * kAmbMax + q].x) * inv_st - ld_dev(&rU[c * kAmbMax + q].y) * inv_sd;
           m += r > 0.0 ? r : 0.0;
         }
         sh.mass[i] = m;
@@ -1273,9 +1282,10 @@ __device__ __forceinline__ void pick_seq(DP& prm_arg, int64_t b, uint4 j0, uint4
 
 // The common case of the pick, for rows of at most kLeanChunks chunks and at most 64 draw tasks whose chunk records
 // need no recomputation, by wave 0 alone (no barrier, no shared memory): one round of loads brings the task partials
-// and every chunk record (lane l owns a contiguous run of at most 8 chunks); the normalisers, the chunk masses, their
-// running sum and the chunk that holds t = u * total follow with wave-level operations; that chunk is then searched
-// with the mass pass's layout (lane l holds its kPer consecutive elements). Returns 0 when done (token and flags
+// and every chunk record (lane l holds chunks l, l + 64, l + 128, ...: each load of a record field is 64 consecutive
+// values); the normalisers, the chunk masses, their running sum in chunk order (one wave scan per group of 64
+// chunks) and the chunk that holds t = u * total follow with wave-level operations; that chunk is then searched with
+// the mass pass's layout (lane l holds its kPer consecutive elements). Returns 0 when done (token and flags
 // written), 1 when the general pick must run instead (an undecided chunk, an empty residual), with nothing written.
 template <typename T>
 __device__ __forceinline__ int pick_lean(DP& prm, int64_t b, const Job& job) {
@@ -1284,28 +1294,32 @@ __device__ __forceinline__ int pick_lean(DP& prm, int64_t b, const Job& job) {
   const int ntask = prm.ntask;
   const double c2 = prm.c2;
   const bool resid = job.kind == JOB_RESID, bonus = job.kind == JOB_BONUS;
-  const ChunkRec* ch = prm.chunks + b * nch;
-  const int q = int((nch + 63) / 64);
-  const int64_t ca = min<int64_t>(nch, int64_t(lane) * q), cb = min<int64_t>(nch, ca + q);
-  constexpr int KB = kLeanChunks / 64;
-  int namb[KB];
-  double A[KB], D[KB], mr[KB];
+  const double* rA = prm.recA + b * nch;
+  const double* rD = prm.recD + b * nch;
+  const int32_t* rN = prm.recN + b * nch;
+  constexpr int KM = kLeanChunks / 64;
+  const int kb = int((nch + 63) / 64);               // groups of 64 chunks in use (uniform)
+  int namb[KM];
+  double A[KM], D[KM];
 #pragma unroll
-  for (int k = 0; k < KB; ++k) {                     // clamped indices: every load is issued, none is conditional
-    const int64_t c = min<int64_t>(ca + k, nch - 1);
-    namb[k] = ld_dev(&ch[c].n_amb);
-    A[k] = ld_dev(&ch[c].A);
-    D[k] = ld_dev(&ch[c].D);
-    mr[k] = ld_dev(&ch[c].mref);
+  for (int k = 0; k < KM; ++k) {                     // clamped indices: every load is issued, none is conditional
+    namb[k] = 0;
+    A[k] = D[k] = 0.0;
+    if (k < kb) {
+      const int64_t c = min<int64_t>(int64_t(k) * 64 + lane, nch - 1);
+      namb[k] = ld_dev(rN + c);
+      A[k] = ld_dev(rA + c);
+      D[k] = ld_dev(rD + c);
+    }
   }
   const bool has_task = lane < ntask;
   const double4 p = ld_task(prm.part2 + b * ntask + min(lane, ntask - 1));
   const double mt = wave_max_d(has_task ? p.x : -INFINITY);
   const int bad = __any(has_task && (isnan(p.y) || isnan(p.w)));
-  double lst = 0.0, lsd = 0.0;
+  double lst = 0.0, lsd = 0.0, ftask = 1.0;          // ftask: rescaling of task lane's exps to the row max (bonus)
   if (has_task) {
-    const double f = (!bonus || p.x == mt) ? 1.0 : (p.x == -INFINITY ? 0.0 : fexp_scaled((p.x - mt) * c2));
-    lst = p.y * f;
+    ftask = (!bonus || p.x == mt) ? 1.0 : (p.x == -INFINITY ? 0.0 : fexp_scaled((p.x - mt) * c2));
+    lst = p.y * ftask;
     lsd = p.w;
   }
   const double St = wave_sum(lst), Sd = wave_sum(lsd);
@@ -1314,53 +1328,70 @@ __device__ __forceinline__ int pick_lean(DP& prm, int64_t b, const Job& job) {
     return 0;
   }
   const double inv_st = 1.0 / St, inv_sd = resid ? 1.0 / Sd : 0.0;
-  double m[KB];
-  double lsum = 0.0;
+  double m[KM];
   int slow = 0;
 #pragma unroll
-  for (int k = 0; k < KB; ++k) {
+  for (int k = 0; k < KM; ++k) {
     m[k] = 0.0;
-    if (ca + k >= cb) continue;
+    if (k >= kb) continue;
+    const int64_t c = int64_t(k) * 64 + lane;
+    // the task's rescaling factor, from the lane that holds that task's partial (every lane takes part)
+    const double f = bonus ? __shfl(ftask, task_of_chunk(min<int64_t>(c, nch - 1), nch, ntask)) : 1.0;
+    if (c >= nch) continue;
     if (namb[k] > kAmbMax) {
       slow = 1;
       continue;
     }
-    const double f = bonus ? fexp_scaled((mr[k] - mt) * c2) : 1.0;
     m[k] = f * (A[k] * inv_st - D[k] * inv_sd);
     for (int u = 0; u < namb[k]; ++u) {              // undecided elements, exactly: max(p - q, 0)
-      const double r = ld_dev(&ch[ca + k].et[u]) * inv_st - ld_dev(&ch[ca + k].ed[u]) * inv_sd;
+      const double2* pu = prm.recU + (b * nch + c) * kAmbMax + u;
+      const double r = ld_dev(&pu->x) * inv_st - ld_dev(&pu->y) * inv_sd;
       m[k] += r > 0.0 ? r : 0.0;
     }
-    lsum += m[k];
   }
   if (__any(slow)) return 1;
-  const double incl = wave_incl_scan(lsum);
-  const double total = readlane_d(incl, 63);
+  // running sums: inclusive scan of each group of 64 chunks, groups in order
+  double incl[KM], tot[KM];
+  double total = 0.0;
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+    incl[k] = tot[k] = 0.0;
+    if (k >= kb) continue;
+    incl[k] = wave_incl_scan(m[k]);
+    tot[k] = readlane_d(incl[k], 63);
+  }
+#pragma unroll
+  for (int k = 0; k < KM; ++k) total += tot[k];
   if (!(total > 0.0)) return 1;                      // empty residual: the general pick draws from p
   const double t = double(job.u) * total;
 
   // the chunk whose running sum first exceeds t (else, rounding, the last chunk with mass)
-  double acc = incl - lsum, cbl = 0.0;
-  int64_t cand = -1, last = -1;
+  int64_t cstar = -1, last = -1;
+  double cbase = 0.0, carry = 0.0;
+  bool found = false;
 #pragma unroll
-  for (int k = 0; k < KB; ++k) {
-    if (ca + k >= cb) continue;
-    if (m[k] > 0.0) last = ca + k;
-    if (cand < 0 && acc + m[k] > t) { cand = ca + k; cbl = acc; }
-    acc += m[k];
+  for (int k = 0; k < KM; ++k) {
+    if (k >= kb) continue;
+    if (m[k] > 0.0) last = int64_t(k) * 64 + lane;
+    if (!found && carry + tot[k] > t) {
+      const uint64_t hm = __ballot(carry + incl[k] > t);
+      const int l = hm ? __builtin_ctzll(hm) : 63;
+      cstar = int64_t(k) * 64 + l;
+      cbase = carry + (readlane_d(incl[k], l) - readlane_d(m[k], l));
+      found = true;
+    }
+    carry += tot[k];
   }
-  int64_t cstar;
-  double cbase = 0.0;
   bool clamp = false;
-  const uint64_t hm = __ballot(cand >= 0);
-  if (hm) {
-    const int l = __builtin_ctzll(hm);
-    cstar = __shfl(cand, l);
-    cbase = readlane_d(cbl, l);
-  } else {
+  if (!found) {
     clamp = true;
     const uint64_t pm = __ballot(last >= 0);
-    cstar = pm ? __shfl(last, 63 - __builtin_clzll(pm)) : -1;
+    cstar = -1;
+    if (pm) {                                        // the largest chunk index with mass over all lanes
+      int64_t best = last;
+      for (int o = 1; o < 64; o <<= 1) best = max<int64_t>(best, __shfl_xor(best, o));
+      cstar = best;
+    }
   }
   if (cstar < 0) {
     if (lane == 0) finish(prm, b, job, -1, 0u);
@@ -1520,11 +1551,9 @@ __device__ __forceinline__ bool draw_task(DP& prm_arg, int64_t b, int task, uint
     if (mt == -INFINITY) {                  // a task of -inf only (bonus row): no mass
       if (lane == 0) {
         for (int64_t c = c0; c < c1; c += NW) {
-          ChunkRec* rec = prm.chunks + b * prm.nch + c;
-          st_dev(&rec->A, 0.0);
-          st_dev(&rec->D, 0.0);
-          st_dev(&rec->n_amb, 0);
-          st_dev(&rec->mref, -double(INFINITY));
+          st_dev(&prm.recA[b * prm.nch + c], 0.0);
+          st_dev(&prm.recD[b * prm.nch + c], 0.0);
+          st_dev(&prm.recN[b * prm.nch + c], 0);
         }
       }
     } else if (resid) {
@@ -1709,7 +1738,10 @@ hipError_t launch_typed(const DensePlan& plan, const DenseArgs& a, hipStream_t s
   dp.jobs = reinterpret_cast<Job*>(ws + plan.off_jobs);
   dp.part1 = reinterpret_cast<Partial1*>(ws + plan.off_part1);
   dp.part2 = reinterpret_cast<double4*>(ws + plan.off_part2);
-  dp.chunks = reinterpret_cast<ChunkRec*>(ws + plan.off_chunks);
+  dp.recA = reinterpret_cast<double*>(ws + plan.off_recA);
+  dp.recD = reinterpret_cast<double*>(ws + plan.off_recD);
+  dp.recN = reinterpret_cast<int32_t*>(ws + plan.off_recN);
+  dp.recU = reinterpret_cast<double2*>(ws + plan.off_recU);
   dp.masses = reinterpret_cast<double*>(ws + plan.off_masses);
   const unsigned grid = unsigned(dp.n_items);
   auto kern = k_verify<T>;
@@ -1748,7 +1780,10 @@ DensePlan make_dense_plan(int64_t B, int32_t G, int64_t V, int32_t ntens, int dt
   p.off_jobs = off;  off = align_up(off + size_t(B) * sizeof(Job), 256);
   p.off_part1 = off; off = align_up(off + size_t(ntens) * size_t(B) * G * p.nseg1 * sizeof(Partial1), 256);
   p.off_part2 = off; off = align_up(off + size_t(B) * p.ntask * sizeof(double4), 256);
-  p.off_chunks = off; off = align_up(off + size_t(B) * size_t(p.nch) * sizeof(ChunkRec), 256);
+  p.off_recA = off; off = align_up(off + size_t(B) * size_t(p.nch) * sizeof(double), 256);
+  p.off_recD = off; off = align_up(off + size_t(B) * size_t(p.nch) * sizeof(double), 256);
+  p.off_recN = off; off = align_up(off + size_t(B) * size_t(p.nch) * sizeof(int32_t), 256);
+  p.off_recU = off; off = align_up(off + size_t(B) * size_t(p.nch) * kAmbMax * sizeof(double2), 256);
   p.off_masses = off; off = align_up(off + size_t(B) * size_t(p.nch) * sizeof(double), 256);
   p.total = off;
   return p;

@@ -47,7 +47,10 @@ struct DensePlan {
   size_t off_jobs = 0;   // Job per b
   size_t off_part1 = 0;  // (max, logit at the id, float64 sum) per (tensor, b, row, segment)
   size_t off_part2 = 0;  // double4 (m_task, S_t, m_d, S_d) per (b, task)
-  size_t off_chunks = 0; // chunk record per (b, chunk)
+  size_t off_recA = 0;   // double per (b, chunk): the chunk's A (see the draw's chunk records)
+  size_t off_recD = 0;   // double per (b, chunk): the chunk's D
+  size_t off_recN = 0;   // int32 per (b, chunk): the chunk's undecided elements
+  size_t off_recU = 0;   // 4 (e_t, e_d) pairs per (b, chunk): the undecided elements themselves
   size_t off_masses = 0; // double per (b, chunk)
   size_t total = 0;
 };
