@@ -321,7 +321,7 @@ struct DenseParams {
   int64_t nch;                                // kChunk-element chunks per row
   int32_t* ready;                             // per b (stride kCtrStride): statistics items finished
   int32_t* done;                              // per b (stride kCtrStride): draw tasks finished
-  Job* jobs;                                  // per b: the draw job
+  Job* jobs;                                  // per b (one per kJobStride bytes): the draw job, sealed
   Partial1* part1;                            // per (tensor, b, row, segment)
   double4* part2;            // per (b, task): reference max, sum e_t (relative to it), m_d, sum e_d
   // chunk records of the mass pass, one array per field so that the pick reads them coalesced (see chunk_body)
@@ -855,10 +855,8 @@ __device__ __forceinline__ double lane_sum16(const double* w) {
 // relative to the max of the chunk's draw task (the first field of that task's partial).
 constexpr int kAmbMax = 4;
 
-// The draw task that chunk c belongs to: the largest t with t * nch / ntask <= c.
-__device__ __forceinline__ int task_of_chunk(int64_t c, int64_t nch, int ntask) {
-  return int(((c + 1) * ntask - 1) / nch);
-}
+// The draw task that chunk c belongs to (task t holds chunks t * kTaskChunks .. t * kTaskChunks + kTaskChunks - 1).
+__device__ __forceinline__ int task_of_chunk(int64_t c) { return int(c / kTaskChunks); }
 
 __device__ __forceinline__ double4 ld_task(const double4* p) {
   const double* d = reinterpret_cast<const double*>(p);
@@ -872,12 +870,12 @@ __device__ __forceinline__ void st_task(double4* p, double4 v) {
   st_dev(d + 3, v.w);
 }
 
-// One lane's kPer elements: exp of both logits, the residual's sign test and the sums. A and D are accumulated as
-// fma(e, w, .) with w = 1 where the residual is positive and 0 elsewhere; amb is set when an element's sign could not
-// be decided (the caller recomputes which one).
+// One lane's kPer elements: exp of both logits, the residual's sign test and the sums. For a residual draw A and D are
+// accumulated as fma(e, w, .) with w = 1 where the residual is positive and 0 elsewhere; amb is set when an element's
+// sign could not be decided (the caller recomputes which one). Bonus and one-hot draws only sum e_t here.
 template <int KIND>
 __device__ __forceinline__ void mass_lane(const float* zt, const float* zd, double c2, double nmt, double nmd,
-                                          int64_t i0, int32_t d, double k_lo, double k_hi, double& st, double& sd,
+                                          double k_lo, double k_hi, double& st, double& sd,
                                           double& A, double& D, bool& amb) {
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
@@ -893,8 +891,6 @@ __device__ __forceinline__ void mass_lane(const float* zt, const float* zd, doub
       A = fma(et, w, A);
       D = fma(ed, w, D);
       amb |= !(pos || neg);
-    } else if constexpr (KIND == JOB_ONEHOT) {
-      A = fma(et, (i0 + e == d) ? 0.0 : 1.0, A);
     }
     // the sums are pinned here every two elements: otherwise the compiler defers them to the end of the chunk and
     // holds every exp of the lane at once, past the loop's register budget (other waves on the SIMD hide latency)
@@ -911,10 +907,28 @@ __device__ __forceinline__ void chunk_body(DP& prm, const Job& job, int64_t b, i
   const int lane = threadIdx.x & 63;
   double A = 0.0, D = 0.0, cst = 0.0, csd = 0.0;     // this chunk's sums
   bool amb = false;
-  mass_lane<KIND>(zt, zd, c2, nmt, nmd, i0, job.d, k_lo, k_hi, cst, csd, A, D, amb);
+  mass_lane<KIND>(zt, zd, c2, nmt, nmd, k_lo, k_hi, cst, csd, A, D, amb);
   st += cst;
   sd += csd;
-  if constexpr (KIND == JOB_BONUS) A = cst;          // the bonus draws from p: the chunk's whole sum
+  if constexpr (KIND != JOB_RESID) A = cst;          // the bonus draws from p: the chunk's whole sum
+  if constexpr (KIND == JOB_ONEHOT) {
+    // q is one-hot at the draft id d, so the residual is p without element d: in the chunk that holds d, the lane
+    // that holds it sums its other elements again (same operations, so the same bits for every other element)
+    if (c == job.d / kChunk) {
+      const int64_t ed = int64_t(job.d) - i0;
+      if (ed >= 0 && ed < kPer) {
+        double a = 0.0;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+          float z = zt[e];
+          asm volatile("" : "+v"(z));
+          const double et = fexp_scaled(xarg(z, c2, nmt));
+          if (e != ed) a += et;
+        }
+        A = a;
+      }
+    }
+  }
   A = wave_sum(A);
   if constexpr (KIND == JOB_RESID) D = wave_sum(D);
   const int64_t rc = b * prm.nch + c;
@@ -1190,7 +1204,7 @@ __device__ __forceinline__ void pick_seq(DP& prm_arg, int64_t b, uint4 j0, uint4
       } else {
         double f = 1.0;
         if (bonus) {                                   // the chunk's exps are relative to its task's max
-          const double mref = ld_dev(reinterpret_cast<const double*>(ps + task_of_chunk(c, nch, ntask)));
+          const double mref = ld_dev(reinterpret_cast<const double*>(ps + task_of_chunk(c)));
           f = mref == -INFINITY ? 0.0 : fexp_scaled((mref - mt) * c2);
         }
         double m = f * (ld_dev(rA + c) * inv_st - ld_dev(rD + c) * inv_sd);
@@ -1336,7 +1350,7 @@ __device__ __forceinline__ int pick_lean(DP& prm, int64_t b, const Job& job) {
     if (k >= kb) continue;
     const int64_t c = int64_t(k) * 64 + lane;
     // the task's rescaling factor, from the lane that holds that task's partial (every lane takes part)
-    const double f = bonus ? __shfl(ftask, task_of_chunk(min<int64_t>(c, nch - 1), nch, ntask)) : 1.0;
+    const double f = bonus ? __shfl(ftask, task_of_chunk(min<int64_t>(c, nch - 1))) : 1.0;
     if (c >= nch) continue;
     if (namb[k] > kAmbMax) {
       slow = 1;
@@ -1440,19 +1454,37 @@ __device__ __forceinline__ int32_t ld_ctr(const int32_t* p) {
   return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-__device__ __forceinline__ void st_job(Job* p, const Job& j) {
-  const uint32_t* s = reinterpret_cast<const uint32_t*>(&j);
-  uint32_t* d = reinterpret_cast<uint32_t*>(p);
-#pragma unroll
-  for (int i = 0; i < int(sizeof(Job) / 4); ++i) st_dev(d + i, s[i]);
+// The job of sequence b sits alone in a 64-byte aligned slot (one cache line). The scan writes every word but the seal,
+// waits until those stores have completed, then sets the seal; the sequence's last draw task clears it again once
+// every task has read the job (the workspace starts zero-filled: unsealed).
+constexpr int kJobWords = int(sizeof(Job) / 4);
+__device__ __forceinline__ uint32_t* job_slot(DP& prm, int64_t b) {
+  return reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(prm.jobs) + b * kJobStride);
 }
-__device__ __forceinline__ Job ld_job(const Job* p) {
-  Job j;
-  const uint32_t* s = reinterpret_cast<const uint32_t*>(p);
+__device__ __forceinline__ void st_job(uint32_t* slot, const Job& j) {
+  const uint32_t* s = reinterpret_cast<const uint32_t*>(&j);
+#pragma unroll
+  for (int i = 0; i < kJobWords; ++i)
+    if (i != kJobSealWord) st_dev(slot + i, s[i]);
+  __builtin_amdgcn_s_waitcnt(0);
+  st_dev(slot + kJobSealWord, 1u);
+}
+// One load instruction of wave 0 (lane i reads word i of the slot): a single cache-line request, so the words form a
+// snapshot of the line; when that snapshot holds the seal, it holds every word the scan wrote before it. Polls until
+// sealed (at most kSpinCap times). Returns false when it gave up.
+__device__ __forceinline__ bool ld_job_sealed(const uint32_t* slot, Job& j) {
+  const int lane = threadIdx.x & 63;
+  uint32_t w = 0;
+  int32_t polls = 0;
+  for (;;) {
+    w = lane < kJobWords ? ld_dev(slot + lane) : 0u;
+    if (__builtin_amdgcn_readlane(w, kJobSealWord) != 0u || ++polls >= kSpinCap) break;
+    __builtin_amdgcn_s_sleep(SV_SLEEP);
+  }
   uint32_t* d = reinterpret_cast<uint32_t*>(&j);
 #pragma unroll
-  for (int i = 0; i < int(sizeof(Job) / 4); ++i) d[i] = ld_dev(s + i);
-  return j;
+  for (int i = 0; i < kJobWords; ++i) d[i] = __builtin_amdgcn_readlane(w, i);
+  return polls < kSpinCap;
 }
 
 // What workgroup i does. The queue is a sequence of steps s = 0, 1, ...; step s holds the statistics items of
@@ -1508,6 +1540,25 @@ __shared__ DrawShared s_draw;
 __shared__ int s_flag;
 
 
+__device__ __forceinline__ void ctr_inc(int32_t* p) {
+  (void)__hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// Waits (thread 0 polls, the others hold at the barrier) until the counter reaches `target`. Returns false when it
+// gave up after kSpinCap polls, which only happens if the hardware broke the dispatch order.
+__device__ __forceinline__ bool wait_count(const int32_t* ctr, int32_t target) {
+  if (threadIdx.x == 0) {
+    int32_t polls = 0;
+    while (ld_ctr(ctr) < target && polls < kSpinCap) {
+      __builtin_amdgcn_s_sleep(SV_SLEEP);
+      ++polls;
+    }
+    s_flag = polls < kSpinCap;
+  }
+  __syncthreads();
+  return s_flag != 0;
+}
+
 // Draw task `task` of sequence b, once its job is published: the float64 masses of chunks
 // [task * nch / ntask, (task + 1) * nch / ntask) of the draw row(s), dealt to the waves in turn, and the task's
 // partial normalisers. Returns true in the workgroup whose task is the sequence's last to finish.
@@ -1520,8 +1571,8 @@ __device__ __forceinline__ bool draw_task(DP& prm_arg, int64_t b, int task, uint
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   if (job.kind != JOB_NONE) {                       // uniform over the workgroup
     const int64_t V = prm.V;
-    const int64_t cbeg = int64_t(task) * prm.nch / prm.ntask;
-    const int64_t c1 = int64_t(task + 1) * prm.nch / prm.ntask;
+    const int64_t cbeg = int64_t(task) * kTaskChunks;
+    const int64_t c1 = min<int64_t>(cbeg + kTaskChunks, prm.nch);
     const int64_t c0 = cbeg + (wave + NW / 2) % NW;
     const T* rt = static_cast<const T*>(prm.tgt) + b * prm.t_seq + int64_t(job.row) * prm.t_row;
     const bool resid = job.kind == JOB_RESID;
@@ -1573,32 +1624,23 @@ __device__ __forceinline__ bool draw_task(DP& prm_arg, int64_t b, int task, uint
       st_task(prm.part2 + b * prm.ntask + task, make_double4(mt, has_nan ? NAN : S, job.m_d, D));
     }
   }
-  // this workgroup's records are complete before it is counted; the last one picks
+  // this workgroup's records are complete before it is counted (the count does not wait for a reply); the
+  // sequence's last task picks once every task has counted itself (the others were dispatched before it)
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tid == 0) s_flag = ctr_add(prm.done + b * kCtrStride) == prm.ntask - 1;
-  __syncthreads();
-  return s_flag != 0;
-}
-
-__device__ __forceinline__ void ctr_inc(int32_t* p) {
-  (void)__hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
-
-// Waits (thread 0 polls, the others hold at the barrier) until the counter reaches `target`. Returns false when it
-// gave up after kSpinCap polls, which only happens if the hardware broke the dispatch order.
-__device__ __forceinline__ bool wait_count(const int32_t* ctr, int32_t target) {
-  if (threadIdx.x == 0) {
-    int32_t polls = 0;
-    while (ld_ctr(ctr) < target && polls < kSpinCap) {
-      __builtin_amdgcn_s_sleep(SV_SLEEP);
-      ++polls;
+  int32_t* done = prm.done + b * kCtrStride;
+  if (tid == 0) ctr_inc(done);
+  if (task != prm.ntask - 1) return false;
+  if (!wait_count(done, prm.ntask)) {               // gave up: report the sequence as not verified
+    if (tid == 0) {
+      prm.token[b] = -1;
+      if (prm.flags) prm.flags[b] = SV_FLAG_NONFINITE | SV_FLAG_ID_RANGE;
     }
-    s_flag = polls < kSpinCap;
+    return false;
   }
-  __syncthreads();
-  return s_flag != 0;
+  return true;
 }
+
 
 // One workgroup per work item, in the queue order of decode_item (the hardware dispatches workgroups in index
 // order, so everything a workgroup waits for was dispatched before it and is running or done):
@@ -1641,31 +1683,20 @@ __global__ __launch_bounds__(kDrawBlock) __attribute__((amdgpu_waves_per_eu(kWpe
         j.flags = SV_FLAG_NONFINITE | SV_FLAG_ID_RANGE;
         j.new_start = -1;
       }
-      if (lane == 0) {
-        st_job(prm.jobs + b, j);
-        __builtin_amdgcn_s_waitcnt(0);
-        ctr_inc(ready);                              // n1 + 1: the job is published
-      }
+      if (lane == 0) st_job(job_slot(prm, b), j);    // published: the draw tasks read it once sealed
     }
     return;
   }
   s_exp2tab[tid] = exp2(double(tid) * 0.00390625);   // the draw's exp2 table (kDrawBlock == 256 entries)
-  if (tid == 0) {
+  if (wave == 0) {
     Job j;
-    int32_t polls = 0;
-    while (ld_ctr(ready) < prm.n1 + 1 && polls < kSpinCap) {
-      __builtin_amdgcn_s_sleep(SV_SLEEP);
-      ++polls;
-    }
-    if (polls < kSpinCap) {
-      j = ld_job(prm.jobs + b);
-    } else {
+    if (!ld_job_sealed(job_slot(prm, b), j)) {       // gave up waiting: report the sequence as not verified
       j = Job{};
       j.kind = JOB_NONE;
       j.flags = SV_FLAG_NONFINITE | SV_FLAG_ID_RANGE;
       j.new_start = -1;
     }
-    s_draw.job = j;
+    if (lane == 0) s_draw.job = j;
   }
   __syncthreads();
   const Job job = uniform_job(s_draw.job);
@@ -1691,6 +1722,7 @@ __global__ __launch_bounds__(kDrawBlock) __attribute__((amdgpu_waves_per_eu(kWpe
     if (tid == 0) {                                  // every item of sequence b has finished
       st_dev(ready, 0);
       st_dev(prm.done + b * kCtrStride, 0);
+      st_dev(job_slot(prm, b) + kJobSealWord, 0u);
     }
   }
 }
@@ -1777,7 +1809,7 @@ DensePlan make_dense_plan(int64_t B, int32_t G, int64_t V, int32_t ntens, int dt
   size_t off = 0;
   p.off_ready = off; off = align_up(off + size_t(B) * kCtrStride * sizeof(int32_t), 256);
   p.off_done = off;  off = align_up(off + size_t(B) * kCtrStride * sizeof(int32_t), 256);
-  p.off_jobs = off;  off = align_up(off + size_t(B) * sizeof(Job), 256);
+  p.off_jobs = off;  off = align_up(off + size_t(B) * kJobStride, 256);
   p.off_part1 = off; off = align_up(off + size_t(ntens) * size_t(B) * G * p.nseg1 * sizeof(Partial1), 256);
   p.off_part2 = off; off = align_up(off + size_t(B) * p.ntask * sizeof(double4), 256);
   p.off_recA = off; off = align_up(off + size_t(B) * size_t(p.nch) * sizeof(double), 256);

@@ -28,8 +28,11 @@ struct alignas(16) Job {
   float pad1;
   double kappa;      // S_d / S_t of the row pair as estimated by the statistics pass (float32 sums)
   int32_t new_start; // start for the next call (-1: leave unchanged)
-  int32_t pad2;
+  uint32_t seal;     // in the workspace: 1 once the scan has written the job, 0 again at the end of the call
 };
+constexpr int kJobSealWord = 11;   // the seal's position in 32-bit words
+constexpr int kJobStride = 64;     // bytes per job in the workspace (one cache line each)
+static_assert(offsetof(Job, seal) == 4 * kJobSealWord && sizeof(Job) <= kJobStride, "job layout");
 
 // Sizes, work queue and workspace layout of one dense / one-hot call. Depends only on (B, gamma, V, number of
 // tensors, dtype); the float32 plan is the larger, so it sizes the workspace for both dtypes.
@@ -44,7 +47,7 @@ struct DensePlan {
   int64_t nch = 1;       // 512-element chunks per row in the draw
   size_t off_ready = 0;  // int32 per b (one per 256 bytes): statistics items finished, + 1 once the job is published
   size_t off_done = 0;   // int32 per b (one per 256 bytes): draw tasks finished
-  size_t off_jobs = 0;   // Job per b
+  size_t off_jobs = 0;   // Job per b, kJobStride bytes apart
   size_t off_part1 = 0;  // (max, logit at the id, float64 sum) per (tensor, b, row, segment)
   size_t off_part2 = 0;  // double4 (m_task, S_t, m_d, S_d) per (b, task)
   size_t off_recA = 0;   // double per (b, chunk): the chunk's A (see the draw's chunk records)
