@@ -43,7 +43,7 @@ int check_dense_common(const void* tgt, int64_t t_seq, int64_t t_row, int dtype,
 // Grids of the plan must fit the launch limits.
 // The work queue (one workgroup per item) must fit a one-dimensional grid of int32 indices.
 int check_grid(const sv::DensePlan& p) {
-  if (double(p.B) * (double(p.n1) + 1.0 + double(p.ntask)) > double(kMaxI32)) return SV_ERR_SHAPE;
+  if (double(p.B) * (double(p.n1) + 1.0) + double(p.nslots) > double(kMaxI32)) return SV_ERR_SHAPE;
   return SV_OK;
 }
 

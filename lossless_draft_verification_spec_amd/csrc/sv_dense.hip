@@ -26,6 +26,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cfloat>
 #include <climits>
 #include <cmath>
@@ -59,12 +60,16 @@ constexpr int64_t kTaskChunks = SV_TASK_CHUNKS; // chunks per draw task (four pe
 #ifndef SV_SCAN_LAG_ROUNDS
 #define SV_SCAN_LAG_ROUNDS 1
 #endif
-#ifndef SV_DRAW_LAG_ROUNDS
-#define SV_DRAW_LAG_ROUNDS 0
-#endif
 constexpr int kScanLagRounds = SV_SCAN_LAG_ROUNDS;  // resident rounds of statistics items between a sequence's
                                                     // statistics and its scan
-constexpr int kDrawLagRounds = SV_DRAW_LAG_ROUNDS;  // ... and its draw tasks (0: after every statistics item)
+#ifndef SV_DRAW_SLACK_PCT
+#define SV_DRAW_SLACK_PCT 25
+#endif
+#ifndef SV_DRAW_SLACK_MAX
+#define SV_DRAW_SLACK_MAX 256
+#endif
+constexpr int64_t kDrawSlackPct = SV_DRAW_SLACK_PCT;  // draw slots beyond the draw tasks, in percent of them ...
+constexpr int64_t kDrawSlackMax = SV_DRAW_SLACK_MAX;  // ... and at most this many
 constexpr int kCtrStride = 64;                  // int32 slots between per-sequence counters (one 256-byte line each)
 #ifndef SV_SLEEP
 #define SV_SLEEP 16
@@ -173,28 +178,6 @@ __device__ __forceinline__ Job uniform_job(const Job& j) {
   return r;
 }
 
-// A job as three 16-byte vectors: the form in which it is handed to the functions that are not inlined (vectors
-// travel in registers, where a structure argument would be copied through the stack).
-struct JobWords {
-  uint4 w[3];
-};
-static_assert(sizeof(Job) == sizeof(JobWords), "a job is three 16-byte words");
-__device__ __forceinline__ void job_words(const Job& j, uint4& a, uint4& b, uint4& c) {
-  JobWords w;
-  __builtin_memcpy(&w, &j, sizeof(Job));
-  a = w.w[0];
-  b = w.w[1];
-  c = w.w[2];
-}
-__device__ __forceinline__ Job job_from_words(uint4 a, uint4 b, uint4 c) {
-  JobWords w;
-  w.w[0] = a;
-  w.w[1] = b;
-  w.w[2] = c;
-  Job j;
-  __builtin_memcpy(&j, &w, sizeof(Job));
-  return uniform_job(j);
-}
 __device__ __forceinline__ int64_t uniform_i64(int64_t v) {
   const uint64_t u = uint64_t(v);
   return int64_t((uint64_t(__builtin_amdgcn_readfirstlane(uint32_t(u >> 32))) << 32) |
@@ -317,10 +300,12 @@ struct DenseParams {
   int32_t* start; const int32_t* order;
   uint8_t* accept; int32_t* n_acc; int32_t* token; float* p_draft; float* q_draft; uint32_t* flags;
   // work queue: per sequence n1 statistics items, one scan and ntask draw tasks, in the order of decode_item
-  int32_t n1; int32_t ntask; int32_t lag1; int32_t lag2; int32_t n_items;
+  int32_t n1; int32_t ntask; int32_t lag1; int32_t n_items;
   int64_t nch;                                // kChunk-element chunks per row
   int32_t* ready;                             // per b (stride kCtrStride): statistics items finished
   int32_t* done;                              // per b (stride kCtrStride): draw tasks finished
+  int32_t* tickets;                           // draw slots started in this call (each takes one ticket)
+  int32_t nslots;                             // draw slots in the queue (at least B * ntask)
   Job* jobs;                                  // per b (one per kJobStride bytes): the draw job, sealed
   Partial1* part1;                            // per (tensor, b, row, segment)
   double4* part2;            // per (b, task): reference max, sum e_t (relative to it), m_d, sum e_d
@@ -566,6 +551,15 @@ __device__ __forceinline__ RowPair row_pair_stats(const Partial1* pt, const Part
   r.zt = ld_dev(&pt[0].zx);
   const float zd0 = ld_dev(&qd[0].zx);
   r.zd = pd ? zd0 : 0.f;
+  if (nseg == 1) {                               // one statistics item per row: its partial is the row's
+    r.mt = ld_dev(&pt[0].m);
+    r.St = ld_dev(&pt[0].s);
+    const float md = ld_dev(&qd[0].m);
+    const double sd = ld_dev(&qd[0].s);
+    r.md = pd ? md : 0.f;
+    r.Sd = pd ? sd : 1.0;
+    return r;
+  }
   float Mt = -INFINITY, Md = -INFINITY;
   double St = 0.0, Sd = 0.0;
   bool nt = false, nd = false;
@@ -1141,9 +1135,9 @@ __device__ __forceinline__ void search_chunk(DP& prm, int64_t b, const Job& job,
 // The pick of sequence b by one workgroup, after every task of the sequence has finished: normalisers from the task
 // partials, chunk masses, their running sum, the chunk that holds t = u * total, and an exact search inside it.
 template <typename T>
-__device__ __forceinline__ void pick_seq(DP& prm_arg, int64_t b, uint4 j0, uint4 j1, uint4 j2) {
+__device__ __forceinline__ void pick_seq(DP& prm_arg, int64_t b, const Job& job_arg) {
   PickShared& sh = s_pick;
-  const Job job = job_from_words(j0, j1, j2);
+  const Job job = uniform_job(job_arg);
   DP& prm = uniform_params(prm_arg);
   constexpr int BLOCK = kDrawBlock, NW = kDrawWaves;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1454,31 +1448,37 @@ __device__ __forceinline__ int32_t ld_ctr(const int32_t* p) {
   return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// The job of sequence b sits alone in a 64-byte aligned slot (one cache line). The scan writes every word but the seal,
-// waits until those stores have completed, then sets the seal; the sequence's last draw task clears it again once
-// every task has read the job (the workspace starts zero-filled: unsealed).
+// The job of sequence b fills a 64-byte aligned slot (one cache line): four 16-byte groups, each with a seal word. The
+// scan writes the whole slot with one store instruction (lane i: word i, seals set), and a draw task reads it with one
+// load instruction; a 16-byte group moves as a unit, so a group whose seal reads 1 holds this call's words, and a job
+// is taken only when all four seals read 1. The sequence's last draw task clears the slot once every task has read
+// it (the workspace starts zero-filled: unsealed).
 constexpr int kJobWords = int(sizeof(Job) / 4);
+static_assert(kJobWords == 16, "a job is four 16-byte groups");
 __device__ __forceinline__ uint32_t* job_slot(DP& prm, int64_t b) {
   return reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(prm.jobs) + b * kJobStride);
 }
+// By every lane of one wave; j is the same in every lane.
 __device__ __forceinline__ void st_job(uint32_t* slot, const Job& j) {
-  const uint32_t* s = reinterpret_cast<const uint32_t*>(&j);
+  const int lane = threadIdx.x & 63;
+  Job s = j;
+  s.seal0 = s.seal1 = s.seal2 = s.seal3 = 1u;
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(&s);
+  uint32_t v = 0;
 #pragma unroll
-  for (int i = 0; i < kJobWords; ++i)
-    if (i != kJobSealWord) st_dev(slot + i, s[i]);
-  __builtin_amdgcn_s_waitcnt(0);
-  st_dev(slot + kJobSealWord, 1u);
+  for (int i = 0; i < kJobWords; ++i) v = lane == i ? w[i] : v;
+  if (lane < kJobWords) st_dev(slot + lane, v);
 }
-// One load instruction of wave 0 (lane i reads word i of the slot): a single cache-line request, so the words form a
-// snapshot of the line; when that snapshot holds the seal, it holds every word the scan wrote before it. Polls until
-// sealed (at most kSpinCap times). Returns false when it gave up.
+// By every lane of one wave. Polls until sealed (at most kSpinCap times); returns false when it gave up.
 __device__ __forceinline__ bool ld_job_sealed(const uint32_t* slot, Job& j) {
   const int lane = threadIdx.x & 63;
   uint32_t w = 0;
   int32_t polls = 0;
   for (;;) {
     w = lane < kJobWords ? ld_dev(slot + lane) : 0u;
-    if (__builtin_amdgcn_readlane(w, kJobSealWord) != 0u || ++polls >= kSpinCap) break;
+    const bool sealed = (__builtin_amdgcn_readlane(w, 3) & __builtin_amdgcn_readlane(w, 7) &
+                         __builtin_amdgcn_readlane(w, 11) & __builtin_amdgcn_readlane(w, 15)) != 0u;
+    if (sealed || ++polls >= kSpinCap) break;
     __builtin_amdgcn_s_sleep(SV_SLEEP);
   }
   uint32_t* d = reinterpret_cast<uint32_t*>(&j);
@@ -1487,48 +1487,34 @@ __device__ __forceinline__ bool ld_job_sealed(const uint32_t* slot, Job& j) {
   return polls < kSpinCap;
 }
 
-// What workgroup i does. The queue is a sequence of steps s = 0, 1, ...; step s holds the statistics items of
-// sequence s, then the scan of sequence s - lag1, then the draw tasks of sequence s - lag2 (each part only when that
-// sequence exists), with 1 <= lag1 <= lag2 <= B. A scan thus comes about one resident round of statistics items after
-// its own, and draw tasks lag2 steps after theirs (lag2 = B puts every draw task after every statistics item).
-// Every wait is on a lower index.
+// What workgroup i does. The queue holds, in this order: steps s = 0 .. B-1, each the statistics items of sequence s
+// followed by the scan of sequence s - lag1 (when s >= lag1), so that a scan comes about one resident round of
+// statistics items after its own; then the scans of the last lag1 sequences; then B * ntask draw slots. The hardware
+// dispatches each XCD's share of the workgroups in index order, so every scan waits only on lower-indexed items. A
+// draw slot takes the next draw task from a ticket counter when it starts (tasks in sequence order), which keeps the
+// XCDs busy until the last task whatever their relative speed; its job's scan lies before every draw slot.
 enum ItemKind : int32_t { ITEM_STATS = 0, ITEM_SCAN = 1, ITEM_DRAW = 2 };
 struct ItemRef {
   int32_t kind;
   int32_t b;
-  int32_t sub;    // statistics item within the sequence, or draw task
+  int32_t sub;    // statistics item within the sequence (draw slots: unused)
 };
-__device__ __forceinline__ ItemRef decode_item(uint32_t i, uint32_t B, uint32_t n1, uint32_t nt, uint32_t lag1,
-                                               uint32_t lag2) {
-  // steps [0, lag1): stats | [lag1, lag2): stats, scan | [lag2, B): stats, scan, draws |
-  // [B, B + lag1): scan, draws | [B + lag1, B + lag2): draws
-  const uint32_t bounds[5] = {lag1, lag2, B, B + lag1, B + lag2};
-  uint32_t s0 = 0;
-  for (int r = 0; r < 5; ++r) {
-    const bool has_st = r <= 2, has_sc = r >= 1 && r <= 3, has_dr = r >= 2;
-    const uint32_t per = (has_st ? n1 : 0u) + (has_sc ? 1u : 0u) + (has_dr ? nt : 0u);
-    const uint32_t steps = bounds[r] - s0;
-    if (i < steps * per) {
-      const uint32_t s = s0 + i / per;
-      uint32_t k = i % per;
-      if (has_st) {
-        if (k < n1) return ItemRef{ITEM_STATS, int32_t(s), int32_t(k)};
-        k -= n1;
-      }
-      if (has_sc) {
-        if (k == 0) return ItemRef{ITEM_SCAN, int32_t(s - lag1), 0};
-        k -= 1;
-      }
-      return ItemRef{ITEM_DRAW, int32_t(s - lag2), int32_t(k)};
-    }
-    i -= steps * per;
-    s0 = bounds[r];
+__device__ __forceinline__ ItemRef decode_item(uint32_t i, uint32_t B, uint32_t n1, uint32_t lag1) {
+  const uint32_t head = lag1 * n1;                         // steps before the first scan: statistics only
+  const uint32_t body = head + (B - lag1) * (n1 + 1);
+  if (i < head) return ItemRef{ITEM_STATS, int32_t(i / n1), int32_t(i % n1)};
+  if (i < body) {
+    const uint32_t j = i - head, s = lag1 + j / (n1 + 1), k = j % (n1 + 1);
+    if (k < n1) return ItemRef{ITEM_STATS, int32_t(s), int32_t(k)};
+    return ItemRef{ITEM_SCAN, int32_t(s - lag1), 0};
   }
-  return ItemRef{ITEM_DRAW, 0, 0};     // not reached: the grid holds exactly B * (n1 + 1 + nt) items
+  if (i < body + lag1) return ItemRef{ITEM_SCAN, int32_t(B - lag1 + (i - body)), 0};
+  return ItemRef{ITEM_DRAW, 0, 0};
 }
 
 struct DrawShared {
   Job job;
+  int32_t ticket;
   float max[kDrawWaves];
   int nan[kDrawWaves];
   double sum[kDrawWaves][2];
@@ -1563,9 +1549,9 @@ __device__ __forceinline__ bool wait_count(const int32_t* ctr, int32_t target) {
 // [task * nch / ntask, (task + 1) * nch / ntask) of the draw row(s), dealt to the waves in turn, and the task's
 // partial normalisers. Returns true in the workgroup whose task is the sequence's last to finish.
 template <typename T>
-__device__ __forceinline__ bool draw_task(DP& prm_arg, int64_t b, int task, uint4 j0, uint4 j1, uint4 j2) {
+__device__ __forceinline__ bool draw_task(DP& prm_arg, int64_t b, int task, const Job& job_arg) {
   DP& prm = uniform_params(prm_arg);
-  const Job job = job_from_words(j0, j1, j2);
+  const Job job = uniform_job(job_arg);
   DrawShared& ds = s_draw;
   constexpr int NW = kDrawWaves;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -1657,8 +1643,7 @@ __global__ __launch_bounds__(kDrawBlock) __attribute__((amdgpu_waves_per_eu(kWpe
   __shared__ double sh_d[kDrawWaves];
   __shared__ uint32_t seen[SV_MAX_GAMMA / 32];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const ItemRef it = decode_item(blockIdx.x, uint32_t(prm.B), uint32_t(prm.n1), uint32_t(prm.ntask),
-                                 uint32_t(prm.lag1), uint32_t(prm.lag2));
+  const ItemRef it = decode_item(blockIdx.x, uint32_t(prm.B), uint32_t(prm.n1), uint32_t(prm.lag1));
   const int64_t b = it.b;
   int32_t* ready = prm.ready + b * kCtrStride;
   if (it.kind == ITEM_STATS) {
@@ -1683,26 +1668,42 @@ __global__ __launch_bounds__(kDrawBlock) __attribute__((amdgpu_waves_per_eu(kWpe
         j.flags = SV_FLAG_NONFINITE | SV_FLAG_ID_RANGE;
         j.new_start = -1;
       }
-      if (lane == 0) st_job(job_slot(prm, b), j);    // published: the draw tasks read it once sealed
+      st_job(job_slot(prm, b), j);                   // published: the draw tasks take it once sealed
     }
     return;
   }
+  // draw slot: the next draw task from the ticket counter (ticket tk: sequence tk / ntask, task tk % ntask), then that
+  // sequence's job. There are more draw slots than tasks: the XCDs that run faster start more slots and take more of
+  // the tasks; a slot that finds none left ends at once.
   s_exp2tab[tid] = exp2(double(tid) * 0.00390625);   // the draw's exp2 table (kDrawBlock == 256 entries)
+  const int64_t ntot = prm.B * int64_t(prm.ntask);
   if (wave == 0) {
-    Job j;
-    if (!ld_job_sealed(job_slot(prm, b), j)) {       // gave up waiting: report the sequence as not verified
-      j = Job{};
-      j.kind = JOB_NONE;
-      j.flags = SV_FLAG_NONFINITE | SV_FLAG_ID_RANGE;
-      j.new_start = -1;
+    int32_t tk = 0;
+    if (lane == 0) {
+      tk = __hip_atomic_fetch_add(prm.tickets, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // the slot that takes the last ticket of this call returns the counter to zero for the next call (every other
+      // slot has taken its ticket already)
+      if (tk == prm.nslots - 1) st_dev(prm.tickets, 0);
     }
-    if (lane == 0) s_draw.job = j;
+    tk = __builtin_amdgcn_readfirstlane(tk);
+    Job j{};
+    if (tk >= 0 && tk < ntot) {
+      if (!ld_job_sealed(job_slot(prm, tk / prm.ntask), j)) {   // gave up waiting: report it as not verified
+        j = Job{};
+        j.kind = JOB_NONE;
+        j.flags = SV_FLAG_NONFINITE | SV_FLAG_ID_RANGE;
+        j.new_start = -1;
+      }
+    }
+    if (lane == 0) { s_draw.job = j; s_draw.ticket = tk; }
   }
   __syncthreads();
+  const int32_t tk = __builtin_amdgcn_readfirstlane(s_draw.ticket);
+  if (tk < 0 || tk >= ntot) return;
+  const int64_t bd = tk / prm.ntask;
   const Job job = uniform_job(s_draw.job);
-  uint4 j0, j1, j2;
-  job_words(job, j0, j1, j2);
-  if (draw_task<T>(prm, b, it.sub, j0, j1, j2)) {
+  if (draw_task<T>(prm, bd, tk % prm.ntask, job)) {
+    const int64_t b = bd;
     __builtin_amdgcn_s_setprio(3);
     if (tid == 0 && prm.start && job.new_start >= 0) prm.start[b] = job.new_start;
     if (job.kind == JOB_NONE) {
@@ -1717,13 +1718,13 @@ __global__ __launch_bounds__(kDrawBlock) __attribute__((amdgpu_waves_per_eu(kWpe
         __syncthreads();
         general = s_flag;
       }
-      if (general) pick_seq<T>(prm, b, j0, j1, j2);
+      if (general) pick_seq<T>(prm, b, job);
     }
     if (tid == 0) {                                  // every item of sequence b has finished
-      st_dev(ready, 0);
+      st_dev(prm.ready + b * kCtrStride, 0);
       st_dev(prm.done + b * kCtrStride, 0);
-      st_dev(job_slot(prm, b) + kJobSealWord, 0u);
     }
+    if (tid < kJobWords) st_dev(job_slot(prm, b) + tid, 0u);
   }
 }
 
@@ -1752,21 +1753,18 @@ hipError_t launch_typed(const DensePlan& plan, const DenseArgs& a, hipStream_t s
   dp.ids = a.ids; dp.ua = a.ua; dp.us = a.us; dp.start = a.start; dp.order = a.order;
   dp.accept = a.accept; dp.n_acc = a.n_acc; dp.token = a.token; dp.p_draft = a.p_draft; dp.q_draft = a.q_draft;
   dp.flags = a.flags;
-  dp.n1 = plan.n1; dp.ntask = plan.ntask; dp.nch = plan.nch;
+  dp.n1 = plan.n1; dp.ntask = plan.ntask; dp.nch = plan.nch; dp.nslots = int32_t(plan.nslots);
   const int R = resident_workgroups();
   auto lag_for = [&](int64_t rounds) {          // sequences whose statistics fill `rounds` resident rounds
     if (rounds <= 0) return int64_t(plan.B);
     int64_t l = (int64_t(R) * rounds + plan.n1 - 1) / plan.n1;
     return l < 1 ? int64_t(1) : (l > plan.B ? plan.B : l);
   };
-  const int64_t lag1 = lag_for(kScanLagRounds);
-  int64_t lag2 = lag_for(kDrawLagRounds);
-  if (lag2 < lag1) lag2 = lag1;
-  dp.lag1 = int32_t(lag1);
-  dp.lag2 = int32_t(lag2);
-  dp.n_items = int32_t(plan.B * (int64_t(plan.n1) + 1 + plan.ntask));
+  dp.lag1 = int32_t(lag_for(kScanLagRounds));
+  dp.n_items = int32_t(plan.B * (int64_t(plan.n1) + 1) + plan.nslots);
   dp.ready = reinterpret_cast<int32_t*>(ws + plan.off_ready);
   dp.done = reinterpret_cast<int32_t*>(ws + plan.off_done);
+  dp.tickets = reinterpret_cast<int32_t*>(ws + plan.off_tickets);
   dp.jobs = reinterpret_cast<Job*>(ws + plan.off_jobs);
   dp.part1 = reinterpret_cast<Partial1*>(ws + plan.off_part1);
   dp.part2 = reinterpret_cast<double4*>(ws + plan.off_part2);
@@ -1806,9 +1804,12 @@ DensePlan make_dense_plan(int64_t B, int32_t G, int64_t V, int32_t ntens, int dt
   int64_t ntask = (p.nch + kTaskChunks - 1) / kTaskChunks;
   if (ntask < 1) ntask = 1;
   p.ntask = int32_t(ntask);
+  // draw slots: the tasks plus kDrawSlackPct percent more, so that a faster XCD can take more than its share
+  p.nslots = B * ntask + std::min<int64_t>((B * ntask * kDrawSlackPct + 99) / 100, kDrawSlackMax);
   size_t off = 0;
   p.off_ready = off; off = align_up(off + size_t(B) * kCtrStride * sizeof(int32_t), 256);
   p.off_done = off;  off = align_up(off + size_t(B) * kCtrStride * sizeof(int32_t), 256);
+  p.off_tickets = off; off = align_up(off + kCtrStride * sizeof(int32_t), 256);
   p.off_jobs = off;  off = align_up(off + size_t(B) * kJobStride, 256);
   p.off_part1 = off; off = align_up(off + size_t(ntens) * size_t(B) * G * p.nseg1 * sizeof(Partial1), 256);
   p.off_part2 = off; off = align_up(off + size_t(B) * p.ntask * sizeof(double4), 256);

@@ -16,23 +16,27 @@ enum JobKind : int32_t {
   JOB_BONUS = 3,     // bonus draw from p of target row gamma
 };
 
-// What the scan of one sequence decides, published to the sequence's draw tasks.
+// What the scan of one sequence decides, published to the sequence's draw tasks. 64 bytes: four 16-byte groups, each
+// ending in a seal word (1 once the scan has written the job, 0 again at the end of the call).
 struct alignas(16) Job {
   int32_t kind;      // JobKind
   int32_t row;       // storage row of the draw (gamma for the bonus)
   int32_t d;         // draft id at that row (one-hot residual)
-  uint32_t flags;    // the sequence's SV_FLAG_* bits from the scan
+  uint32_t seal0;
   float u;           // the uniform of the draw
   float m_t;         // exact max of the target row (from the statistics pass; unused for the bonus)
   float m_d;         // exact max of the draft row
-  float pad1;
+  uint32_t seal1;
   double kappa;      // S_d / S_t of the row pair as estimated by the statistics pass (float32 sums)
   int32_t new_start; // start for the next call (-1: leave unchanged)
-  uint32_t seal;     // in the workspace: 1 once the scan has written the job, 0 again at the end of the call
+  uint32_t seal2;
+  uint32_t flags;    // the sequence's SV_FLAG_* bits from the scan
+  uint32_t pad0, pad1;
+  uint32_t seal3;
 };
-constexpr int kJobSealWord = 11;   // the seal's position in 32-bit words
 constexpr int kJobStride = 64;     // bytes per job in the workspace (one cache line each)
-static_assert(offsetof(Job, seal) == 4 * kJobSealWord && sizeof(Job) <= kJobStride, "job layout");
+static_assert(sizeof(Job) == kJobStride && offsetof(Job, seal0) == 12 && offsetof(Job, seal1) == 28 &&
+              offsetof(Job, seal2) == 44 && offsetof(Job, seal3) == 60, "job layout");
 
 // Sizes, work queue and workspace layout of one dense / one-hot call. Depends only on (B, gamma, V, number of
 // tensors, dtype); the float32 plan is the larger, so it sizes the workspace for both dtypes.
@@ -45,8 +49,10 @@ struct DensePlan {
   int64_t n1 = 1;        // statistics items per sequence: ntens * G * nseg1
   int32_t ntask = 1;     // draw tasks per sequence
   int64_t nch = 1;       // 512-element chunks per row in the draw
+  int64_t nslots = 1;    // draw slots of the work queue (at least B * ntask)
   size_t off_ready = 0;  // int32 per b (one per 256 bytes): statistics items finished, + 1 once the job is published
   size_t off_done = 0;   // int32 per b (one per 256 bytes): draw tasks finished
+  size_t off_tickets = 0; // int32: draw slots started in this call
   size_t off_jobs = 0;   // Job per b, kJobStride bytes apart
   size_t off_part1 = 0;  // (max, logit at the id, float64 sum) per (tensor, b, row, segment)
   size_t off_part2 = 0;  // double4 (m_task, S_t, m_d, S_d) per (b, task)
