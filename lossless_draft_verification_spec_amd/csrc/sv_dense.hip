@@ -39,7 +39,10 @@ namespace sv {
 namespace {
 
 constexpr int kStatsBlock = 256;
-constexpr int kUnroll = 4;          // 16-byte vectors per thread per group
+#ifndef SV_UNROLL
+#define SV_UNROLL 4
+#endif
+constexpr int kUnroll = SV_UNROLL;   // 16-byte vectors per thread per group
 #ifndef SV_STATS_NT
 #define SV_STATS_NT 1
 #endif
