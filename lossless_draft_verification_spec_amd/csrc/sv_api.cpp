@@ -76,7 +76,7 @@ size_t sv_workspace_bytes(int kind, int64_t B, int32_t gamma, int64_t V_or_k) {
     case SV_KIND_DENSE:
     case SV_KIND_ONEHOT:
       if (V_or_k > kMaxI32) return bad;
-      return sv::make_dense_plan(B, gamma, V_or_k, kind == SV_KIND_DENSE ? 2 : 1, SV_F32).total;
+      return sv::make_dense_plan(B, gamma, V_or_k, kind == SV_KIND_DENSE ? 2 : 1, SV_F32, 1).total;
     case SV_KIND_SPARSE:
       if (V_or_k > SV_MAX_K) return bad;
       return 0;
@@ -124,7 +124,7 @@ int sv_verify_dense(const void* target_logits, int64_t t_seq, int64_t t_row,
   if (double(B - 1) * double(d_seq) + double(gamma - 1) * double(d_row) + double(V) > 9.0e18) return SV_ERR_SHAPE;
   if (!aligned(draft_logits, dtype == SV_BF16 ? 2 : 4)) return SV_ERR_ALIGN;
   if (q_draft && !aligned(q_draft, 4)) return SV_ERR_ALIGN;
-  const sv::DensePlan plan = sv::make_dense_plan(B, gamma, V, 2, dtype);
+  const sv::DensePlan plan = sv::make_dense_plan(B, gamma, V, 2, dtype, sv::resident_workgroups());
   st = check_grid(plan);
   if (st != SV_OK) return st;
   st = check_workspace(workspace, workspace_bytes, plan.total);
@@ -148,7 +148,7 @@ int sv_verify_onehot_draft(const void* target_logits, int64_t t_seq, int64_t t_r
   int st = check_dense_common(target_logits, t_seq, t_row, dtype, B, gamma, V, draft_ids, u_accept, u_sample,
                               temperature, bonus, start, order, accept, n_accepted, out_token, p_draft, flags);
   if (st != SV_OK) return st;
-  const sv::DensePlan plan = sv::make_dense_plan(B, gamma, V, 1, dtype);
+  const sv::DensePlan plan = sv::make_dense_plan(B, gamma, V, 1, dtype, sv::resident_workgroups());
   st = check_grid(plan);
   if (st != SV_OK) return st;
   st = check_workspace(workspace, workspace_bytes, plan.total);

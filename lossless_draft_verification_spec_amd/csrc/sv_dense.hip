@@ -56,10 +56,18 @@ constexpr int kDrawBlock = 256;     // threads per workgroup, both kinds of item
 #define SV_ITEM_BYTES 1048576
 #endif
 constexpr int64_t kItemBytes = SV_ITEM_BYTES;   // target bytes of logits per statistics item
-#ifndef SV_TASK_CHUNKS
-#define SV_TASK_CHUNKS 16
+// Draw task sizes, in chunks. Most sequences take tasks of kTaskChunks, doubled (up to kTaskChunksMax) while the launch
+// would hold more than kTasksPerSlot tasks per resident workgroup (a task costs ~4 us of hand-off and set-up besides
+// its float64 work); the last sequences, whose draws end the launch, take tasks of kTailChunks: as many sequences as
+// hold about kTailSlots chunks per resident workgroup.
+constexpr int64_t kTaskChunks = 16;
+constexpr int64_t kTaskChunksMax = 64;
+constexpr int64_t kTasksPerSlot = 2;
+constexpr int64_t kTailChunks = 8;
+#ifndef SV_TAIL_SLOTS
+#define SV_TAIL_SLOTS 2
 #endif
-constexpr int64_t kTaskChunks = SV_TASK_CHUNKS; // chunks per draw task (four per wave)
+constexpr int64_t kTailSlots = SV_TAIL_SLOTS;
 #ifndef SV_SCAN_LAG_ROUNDS
 #define SV_SCAN_LAG_ROUNDS 1
 #endif
@@ -304,6 +312,10 @@ struct DenseParams {
   uint8_t* accept; int32_t* n_acc; int32_t* token; float* p_draft; float* q_draft; uint32_t* flags;
   // work queue: per sequence n1 statistics items, one scan and ntask draw tasks, in the order of decode_item
   int32_t n1; int32_t ntask; int32_t lag1; int32_t n_items;
+  int32_t ntask2;                             // draw tasks of each of the last tailq sequences (>= ntask)
+  int32_t chunks1;                            // chunks per draw task of the other sequences
+  int32_t tailq;                              // sequences with small draw tasks (the last ones)
+  int64_t ntot;                               // draw tasks in all
   int64_t nch;                                // kChunk-element chunks per row
   int32_t* ready;                             // per b (stride kCtrStride): statistics items finished
   int32_t* done;                              // per b (stride kCtrStride): draw tasks finished
@@ -852,8 +864,18 @@ __device__ __forceinline__ double lane_sum16(const double* w) {
 // relative to the max of the chunk's draw task (the first field of that task's partial).
 constexpr int kAmbMax = 4;
 
-// The draw task that chunk c belongs to (task t holds chunks t * kTaskChunks .. t * kTaskChunks + kTaskChunks - 1).
-__device__ __forceinline__ int task_of_chunk(int64_t c) { return int(c / kTaskChunks); }
+// The draw tasks of sequence b: the sequences before the last tailq cut their rows into tasks of kTaskChunks chunks,
+// the last tailq (whose draws end the launch) into tasks of kTailChunks, so that their draws take less time. The
+// task partials of sequence b sit at b * ntask2 + task.
+struct TaskShape {
+  int32_t ntask;     // tasks of the sequence
+  int32_t chunks;    // chunks per task (the last task may hold fewer)
+};
+__device__ __forceinline__ TaskShape task_shape(DP& prm, int64_t b) {
+  return b < prm.B - prm.tailq ? TaskShape{prm.ntask, prm.chunks1} : TaskShape{prm.ntask2, int32_t(kTailChunks)};
+}
+// The draw task that chunk c belongs to (task t holds chunks t * chunks .. t * chunks + chunks - 1).
+__device__ __forceinline__ int task_of_chunk(int64_t c, int32_t chunks) { return int(c / chunks); }
 
 __device__ __forceinline__ double4 ld_task(const double4* p) {
   const double* d = reinterpret_cast<const double*>(p);
@@ -1144,14 +1166,15 @@ __device__ __forceinline__ void pick_seq(DP& prm_arg, int64_t b, const Job& job_
   DP& prm = uniform_params(prm_arg);
   constexpr int BLOCK = kDrawBlock, NW = kDrawWaves;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ntask = prm.ntask;
+  const TaskShape shp = task_shape(prm, b);
+  const int ntask = shp.ntask;
   const int64_t nch = prm.nch, V = prm.V;
   const double* rA = prm.recA + b * nch;
   const double* rD = prm.recD + b * nch;
   const int32_t* rN = prm.recN + b * nch;
   const double2* rU = prm.recU + b * nch * kAmbMax;
   double* mg = prm.masses + b * nch;
-  const double4* ps = prm.part2 + b * ntask;
+  const double4* ps = prm.part2 + b * prm.ntask2;
   const double c2 = prm.c2;
   const bool resid = job.kind == JOB_RESID, bonus = job.kind == JOB_BONUS;
 
@@ -1201,7 +1224,7 @@ __device__ __forceinline__ void pick_seq(DP& prm_arg, int64_t b, const Job& job_
       } else {
         double f = 1.0;
         if (bonus) {                                   // the chunk's exps are relative to its task's max
-          const double mref = ld_dev(reinterpret_cast<const double*>(ps + task_of_chunk(c)));
+          const double mref = ld_dev(reinterpret_cast<const double*>(ps + task_of_chunk(c, shp.chunks)));
           f = mref == -INFINITY ? 0.0 : fexp_scaled((mref - mt) * c2);
         }
         double m = f * (ld_dev(rA + c) * inv_st - ld_dev(rD + c) * inv_sd);
@@ -1302,7 +1325,8 @@ template <typename T>
 __device__ __forceinline__ int pick_lean(DP& prm, int64_t b, const Job& job) {
   const int lane = threadIdx.x & 63;
   const int64_t nch = prm.nch, V = prm.V;
-  const int ntask = prm.ntask;
+  const TaskShape shp = task_shape(prm, b);
+  const int ntask = shp.ntask;
   const double c2 = prm.c2;
   const bool resid = job.kind == JOB_RESID, bonus = job.kind == JOB_BONUS;
   const double* rA = prm.recA + b * nch;
@@ -1324,7 +1348,7 @@ __device__ __forceinline__ int pick_lean(DP& prm, int64_t b, const Job& job) {
     }
   }
   const bool has_task = lane < ntask;
-  const double4 p = ld_task(prm.part2 + b * ntask + min(lane, ntask - 1));
+  const double4 p = ld_task(prm.part2 + b * prm.ntask2 + min(lane, ntask - 1));
   const double mt = wave_max_d(has_task ? p.x : -INFINITY);
   const int bad = __any(has_task && (isnan(p.y) || isnan(p.w)));
   double lst = 0.0, lsd = 0.0, ftask = 1.0;          // ftask: rescaling of task lane's exps to the row max (bonus)
@@ -1347,7 +1371,7 @@ __device__ __forceinline__ int pick_lean(DP& prm, int64_t b, const Job& job) {
     if (k >= kb) continue;
     const int64_t c = int64_t(k) * 64 + lane;
     // the task's rescaling factor, from the lane that holds that task's partial (every lane takes part)
-    const double f = bonus ? __shfl(ftask, task_of_chunk(min<int64_t>(c, nch - 1))) : 1.0;
+    const double f = bonus ? __shfl(ftask, task_of_chunk(min<int64_t>(c, nch - 1), shp.chunks)) : 1.0;
     if (c >= nch) continue;
     if (namb[k] > kAmbMax) {
       slow = 1;
@@ -1492,7 +1516,7 @@ __device__ __forceinline__ bool ld_job_sealed(const uint32_t* slot, Job& j) {
 
 // What workgroup i does. The queue holds, in this order: steps s = 0 .. B-1, each the statistics items of sequence s
 // followed by the scan of sequence s - lag1 (when s >= lag1), so that a scan comes about one resident round of
-// statistics items after its own; then the scans of the last lag1 sequences; then B * ntask draw slots. The hardware
+// statistics items after its own; then the scans of the last lag1 sequences; then the draw slots. The hardware
 // dispatches each XCD's share of the workgroups in index order, so every scan waits only on lower-indexed items. A
 // draw slot takes the next draw task from a ticket counter when it starts (tasks in sequence order), which keeps the
 // XCDs busy until the last task whatever their relative speed; its job's scan lies before every draw slot.
@@ -1548,9 +1572,9 @@ __device__ __forceinline__ bool wait_count(const int32_t* ctr, int32_t target) {
   return s_flag != 0;
 }
 
-// Draw task `task` of sequence b, once its job is published: the float64 masses of chunks
-// [task * nch / ntask, (task + 1) * nch / ntask) of the draw row(s), dealt to the waves in turn, and the task's
-// partial normalisers. Returns true in the workgroup whose task is the sequence's last to finish.
+// Draw task `task` of sequence b, once its job is published: the float64 masses of the task's chunks of the draw
+// row(s) (see task_shape), dealt to the waves in turn, and the task's partial normalisers. Returns true in the
+// workgroup of the sequence's last task once every task of the sequence has counted itself.
 template <typename T>
 __device__ __forceinline__ bool draw_task(DP& prm_arg, int64_t b, int task, const Job& job_arg) {
   DP& prm = uniform_params(prm_arg);
@@ -1560,8 +1584,9 @@ __device__ __forceinline__ bool draw_task(DP& prm_arg, int64_t b, int task, cons
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   if (job.kind != JOB_NONE) {                       // uniform over the workgroup
     const int64_t V = prm.V;
-    const int64_t cbeg = int64_t(task) * kTaskChunks;
-    const int64_t c1 = min<int64_t>(cbeg + kTaskChunks, prm.nch);
+    const TaskShape shp = task_shape(prm, b);
+    const int64_t cbeg = int64_t(task) * shp.chunks;
+    const int64_t c1 = min<int64_t>(cbeg + shp.chunks, prm.nch);
     const int64_t c0 = cbeg + (wave + NW / 2) % NW;
     const T* rt = static_cast<const T*>(prm.tgt) + b * prm.t_seq + int64_t(job.row) * prm.t_row;
     const bool resid = job.kind == JOB_RESID;
@@ -1610,7 +1635,7 @@ __device__ __forceinline__ bool draw_task(DP& prm_arg, int64_t b, int task, cons
     if (tid == 0) {
       double S = 0.0, D = 0.0;
       for (int i = 0; i < NW; ++i) { S += ds.sum[i][0]; D += ds.sum[i][1]; }
-      st_task(prm.part2 + b * prm.ntask + task, make_double4(mt, has_nan ? NAN : S, job.m_d, D));
+      st_task(prm.part2 + b * prm.ntask2 + task, make_double4(mt, has_nan ? NAN : S, job.m_d, D));
     }
   }
   // this workgroup's records are complete before it is counted (the count does not wait for a reply); the
@@ -1619,8 +1644,9 @@ __device__ __forceinline__ bool draw_task(DP& prm_arg, int64_t b, int task, cons
   __syncthreads();
   int32_t* done = prm.done + b * kCtrStride;
   if (tid == 0) ctr_inc(done);
-  if (task != prm.ntask - 1) return false;
-  if (!wait_count(done, prm.ntask)) {               // gave up: report the sequence as not verified
+  const int32_t nt_b = task_shape(prm, b).ntask;
+  if (task != nt_b - 1) return false;
+  if (!wait_count(done, nt_b)) {                    // gave up: report the sequence as not verified
     if (tid == 0) {
       prm.token[b] = -1;
       if (prm.flags) prm.flags[b] = SV_FLAG_NONFINITE | SV_FLAG_ID_RANGE;
@@ -1675,11 +1701,14 @@ __global__ __launch_bounds__(kDrawBlock) __attribute__((amdgpu_waves_per_eu(kWpe
     }
     return;
   }
-  // draw slot: the next draw task from the ticket counter (ticket tk: sequence tk / ntask, task tk % ntask), then that
-  // sequence's job. There are more draw slots than tasks: the XCDs that run faster start more slots and take more of
+  // draw slot: the next draw task from the ticket counter (tickets in sequence order, task order within a sequence),
+  // then that sequence's job. There are more draw slots than tasks: the XCDs that run faster start more slots and take more of
   // the tasks; a slot that finds none left ends at once.
   s_exp2tab[tid] = exp2(double(tid) * 0.00390625);   // the draw's exp2 table (kDrawBlock == 256 entries)
-  const int64_t ntot = prm.B * int64_t(prm.ntask);
+  const int64_t ntot = prm.ntot;
+  const int64_t head = (prm.B - prm.tailq) * int64_t(prm.ntask);    // tickets of the sequences with large tasks
+  auto seq_of = [&](int64_t t) { return t < head ? t / prm.ntask : prm.B - prm.tailq + (t - head) / prm.ntask2; };
+  auto task_of = [&](int64_t t) { return int(t < head ? t % prm.ntask : (t - head) % prm.ntask2); };
   if (wave == 0) {
     int32_t tk = 0;
     if (lane == 0) {
@@ -1691,7 +1720,7 @@ __global__ __launch_bounds__(kDrawBlock) __attribute__((amdgpu_waves_per_eu(kWpe
     tk = __builtin_amdgcn_readfirstlane(tk);
     Job j{};
     if (tk >= 0 && tk < ntot) {
-      if (!ld_job_sealed(job_slot(prm, tk / prm.ntask), j)) {   // gave up waiting: report it as not verified
+      if (!ld_job_sealed(job_slot(prm, seq_of(tk)), j)) {       // gave up waiting: report it as not verified
         j = Job{};
         j.kind = JOB_NONE;
         j.flags = SV_FLAG_NONFINITE | SV_FLAG_ID_RANGE;
@@ -1703,9 +1732,9 @@ __global__ __launch_bounds__(kDrawBlock) __attribute__((amdgpu_waves_per_eu(kWpe
   __syncthreads();
   const int32_t tk = __builtin_amdgcn_readfirstlane(s_draw.ticket);
   if (tk < 0 || tk >= ntot) return;
-  const int64_t bd = tk / prm.ntask;
+  const int64_t bd = seq_of(tk);
   const Job job = uniform_job(s_draw.job);
-  if (draw_task<T>(prm, bd, tk % prm.ntask, job)) {
+  if (draw_task<T>(prm, bd, task_of(tk), job)) {
     const int64_t b = bd;
     __builtin_amdgcn_s_setprio(3);
     if (tid == 0 && prm.start && job.new_start >= 0) prm.start[b] = job.new_start;
@@ -1713,7 +1742,7 @@ __global__ __launch_bounds__(kDrawBlock) __attribute__((amdgpu_waves_per_eu(kWpe
       if (tid == 0) finish(prm, b, job, -1, 0u);
     } else {
       int general = 1;
-      if (prm.nch <= kLeanChunks && prm.ntask <= 64) {
+      if (prm.nch <= kLeanChunks && task_shape(prm, b).ntask <= 64) {
         if (wave == 0) {
           const int r = pick_lean<T>(prm, b, job);
           if (lane == 0) s_flag = r;
@@ -1731,17 +1760,6 @@ __global__ __launch_bounds__(kDrawBlock) __attribute__((amdgpu_waves_per_eu(kWpe
   }
 }
 
-// Resident workgroups of the kernel on the current device (compute units x workgroups per compute unit).
-int resident_workgroups() {
-  static int cached[64] = {};
-  int dev = 0, ncu = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 1024;
-  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
-  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0) ncu = 256;
-  const int r = ncu * kWpe;          // kWpe 4-wave workgroups per compute unit at kWpe waves per SIMD
-  if (dev >= 0 && dev < 64) cached[dev] = r;
-  return r;
-}
 
 template <typename T>
 hipError_t launch_typed(const DensePlan& plan, const DenseArgs& a, hipStream_t stream) {
@@ -1757,6 +1775,7 @@ hipError_t launch_typed(const DensePlan& plan, const DenseArgs& a, hipStream_t s
   dp.accept = a.accept; dp.n_acc = a.n_acc; dp.token = a.token; dp.p_draft = a.p_draft; dp.q_draft = a.q_draft;
   dp.flags = a.flags;
   dp.n1 = plan.n1; dp.ntask = plan.ntask; dp.nch = plan.nch; dp.nslots = int32_t(plan.nslots);
+  dp.ntask2 = plan.ntask2; dp.tailq = int32_t(plan.tailq); dp.ntot = plan.ntot; dp.chunks1 = plan.chunks1;
   const int R = resident_workgroups();
   auto lag_for = [&](int64_t rounds) {          // sequences whose statistics fill `rounds` resident rounds
     if (rounds <= 0) return int64_t(plan.B);
@@ -1791,7 +1810,19 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace
 
-DensePlan make_dense_plan(int64_t B, int32_t G, int64_t V, int32_t ntens, int dtype) {
+// Resident workgroups of the kernel on the current device (compute units x workgroups per compute unit).
+int resident_workgroups() {
+  static int cached[64] = {};
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1024;
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0) ncu = 256;
+  const int r = ncu * kWpe;          // kWpe 4-wave workgroups per compute unit at kWpe waves per SIMD
+  if (dev >= 0 && dev < 64) cached[dev] = r;
+  return r;
+}
+
+DensePlan make_dense_plan(int64_t B, int32_t G, int64_t V, int32_t ntens, int dtype, int64_t resident) {
   DensePlan p;
   p.B = B; p.G = G; p.V = V; p.ntens = ntens;
   const int64_t es = dtype == SV_BF16 ? 2 : 4;
@@ -1802,20 +1833,29 @@ DensePlan make_dense_plan(int64_t B, int32_t G, int64_t V, int32_t ntens, int dt
   if (s1 < 1) s1 = 1;
   p.nseg1 = int32_t(s1);
   p.n1 = int64_t(ntens) * G * s1;
-  // draw: rows cut into chunks of kChunk elements, kTaskChunks consecutive chunks per task
+  // draw: rows cut into chunks of kChunk elements, consecutive chunks per task
   p.nch = (V + kChunk - 1) / kChunk;
-  int64_t ntask = (p.nch + kTaskChunks - 1) / kTaskChunks;
+  const int64_t R = std::max<int64_t>(1, resident);
+  int64_t chunks1 = kTaskChunks;
+  while (chunks1 < kTaskChunksMax && B * ((p.nch + chunks1 - 1) / chunks1) > kTasksPerSlot * R) chunks1 *= 2;
+  p.chunks1 = int32_t(chunks1);
+  int64_t ntask = (p.nch + chunks1 - 1) / chunks1;
   if (ntask < 1) ntask = 1;
   p.ntask = int32_t(ntask);
+  int64_t ntask2 = (p.nch + kTailChunks - 1) / kTailChunks;
+  if (ntask2 < ntask) ntask2 = ntask;
+  p.ntask2 = int32_t(ntask2);
+  p.tailq = std::max<int64_t>(1, std::min<int64_t>(B, (kTailSlots * R + p.nch - 1) / p.nch));
+  p.ntot = (B - p.tailq) * ntask + p.tailq * ntask2;
   // draw slots: the tasks plus kDrawSlackPct percent more, so that a faster XCD can take more than its share
-  p.nslots = B * ntask + std::min<int64_t>((B * ntask * kDrawSlackPct + 99) / 100, kDrawSlackMax);
+  p.nslots = p.ntot + std::min<int64_t>((p.ntot * kDrawSlackPct + 99) / 100, kDrawSlackMax);
   size_t off = 0;
   p.off_ready = off; off = align_up(off + size_t(B) * kCtrStride * sizeof(int32_t), 256);
   p.off_done = off;  off = align_up(off + size_t(B) * kCtrStride * sizeof(int32_t), 256);
   p.off_tickets = off; off = align_up(off + kCtrStride * sizeof(int32_t), 256);
   p.off_jobs = off;  off = align_up(off + size_t(B) * kJobStride, 256);
   p.off_part1 = off; off = align_up(off + size_t(ntens) * size_t(B) * G * p.nseg1 * sizeof(Partial1), 256);
-  p.off_part2 = off; off = align_up(off + size_t(B) * p.ntask * sizeof(double4), 256);
+  p.off_part2 = off; off = align_up(off + size_t(B) * p.ntask2 * sizeof(double4), 256);
   p.off_recA = off; off = align_up(off + size_t(B) * size_t(p.nch) * sizeof(double), 256);
   p.off_recD = off; off = align_up(off + size_t(B) * size_t(p.nch) * sizeof(double), 256);
   p.off_recN = off; off = align_up(off + size_t(B) * size_t(p.nch) * sizeof(int32_t), 256);

@@ -47,7 +47,11 @@ struct DensePlan {
   int32_t ntens = 0;     // 2: target + draft; 1: target only (one-hot)
   int32_t nseg1 = 1;     // statistics items (segments) per row
   int64_t n1 = 1;        // statistics items per sequence: ntens * G * nseg1
-  int32_t ntask = 1;     // draw tasks per sequence
+  int32_t ntask = 1;     // draw tasks per sequence (all but the last tailq sequences)
+  int32_t ntask2 = 1;    // draw tasks of each of the last tailq sequences (smaller tasks)
+  int32_t chunks1 = 16;  // chunks per draw task of the other sequences
+  int64_t tailq = 1;     // sequences with the smaller draw tasks
+  int64_t ntot = 1;      // draw tasks in all
   int64_t nch = 1;       // 512-element chunks per row in the draw
   int64_t nslots = 1;    // draw slots of the work queue (at least B * ntask)
   size_t off_ready = 0;  // int32 per b (one per 256 bytes): statistics items finished, + 1 once the job is published
@@ -64,7 +68,10 @@ struct DensePlan {
   size_t total = 0;
 };
 
-DensePlan make_dense_plan(int64_t B, int32_t G, int64_t V, int32_t ntens, int dtype);
+// resident: workgroups resident on the device at once (it sets the draw task sizes; the workspace size does not
+// depend on it).
+DensePlan make_dense_plan(int64_t B, int32_t G, int64_t V, int32_t ntens, int dtype, int64_t resident);
+int resident_workgroups();
 
 struct DenseArgs {
   const void* tgt; int64_t t_seq, t_row;
