@@ -65,7 +65,7 @@ constexpr int64_t kTaskChunksMax = 64;
 constexpr int64_t kTasksPerSlot = 2;
 constexpr int64_t kTailChunks = 8;
 #ifndef SV_TAIL_SLOTS
-#define SV_TAIL_SLOTS 2
+#define SV_TAIL_SLOTS 3
 #endif
 constexpr int64_t kTailSlots = SV_TAIL_SLOTS;
 #ifndef SV_SCAN_LAG_ROUNDS
@@ -1846,6 +1846,9 @@ DensePlan make_dense_plan(int64_t B, int32_t G, int64_t V, int32_t ntens, int dt
   if (ntask2 < ntask) ntask2 = ntask;
   p.ntask2 = int32_t(ntask2);
   p.tailq = std::max<int64_t>(1, std::min<int64_t>(B, (kTailSlots * R + p.nch - 1) / p.nch));
+#ifdef SV_TAILQ
+  p.tailq = std::max<int64_t>(1, std::min<int64_t>(B, SV_TAILQ));
+#endif
   p.ntot = (B - p.tailq) * ntask + p.tailq * ntask2;
   // draw slots: the tasks plus kDrawSlackPct percent more, so that a faster XCD can take more than its share
   p.nslots = p.ntot + std::min<int64_t>((p.ntot * kDrawSlackPct + 99) / 100, kDrawSlackMax);
