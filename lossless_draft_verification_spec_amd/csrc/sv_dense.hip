@@ -869,13 +869,15 @@ constexpr int kAmbMax = 4;
 // task partials of sequence b sit at b * ntask2 + task.
 struct TaskShape {
   int32_t ntask;     // tasks of the sequence
-  int32_t chunks;    // chunks per task (the last task may hold fewer)
+  int32_t chunks;    // chunks per task (a power of two; the last task may hold fewer)
+  int32_t shift;     // log2(chunks)
 };
 __device__ __forceinline__ TaskShape task_shape(DP& prm, int64_t b) {
-  return b < prm.B - prm.tailq ? TaskShape{prm.ntask, prm.chunks1} : TaskShape{prm.ntask2, int32_t(kTailChunks)};
+  const int32_t c = b < prm.B - prm.tailq ? prm.chunks1 : int32_t(kTailChunks);
+  return TaskShape{b < prm.B - prm.tailq ? prm.ntask : prm.ntask2, c, __builtin_ctz(uint32_t(c))};
 }
 // The draw task that chunk c belongs to (task t holds chunks t * chunks .. t * chunks + chunks - 1).
-__device__ __forceinline__ int task_of_chunk(int64_t c, int32_t chunks) { return int(c / chunks); }
+__device__ __forceinline__ int task_of_chunk(int64_t c, const TaskShape& shp) { return int(c >> shp.shift); }
 
 __device__ __forceinline__ double4 ld_task(const double4* p) {
   const double* d = reinterpret_cast<const double*>(p);
@@ -1224,7 +1226,7 @@ __device__ __forceinline__ void pick_seq(DP& prm_arg, int64_t b, const Job& job_
       } else {
         double f = 1.0;
         if (bonus) {                                   // the chunk's exps are relative to its task's max
-          const double mref = ld_dev(reinterpret_cast<const double*>(ps + task_of_chunk(c, shp.chunks)));
+          const double mref = ld_dev(reinterpret_cast<const double*>(ps + task_of_chunk(c, shp)));
           f = mref == -INFINITY ? 0.0 : fexp_scaled((mref - mt) * c2);
         }
         double m = f * (ld_dev(rA + c) * inv_st - ld_dev(rD + c) * inv_sd);
@@ -1371,7 +1373,8 @@ __device__ __forceinline__ int pick_lean(DP& prm, int64_t b, const Job& job) {
     if (k >= kb) continue;
     const int64_t c = int64_t(k) * 64 + lane;
     // the task's rescaling factor, from the lane that holds that task's partial (every lane takes part)
-    const double f = bonus ? __shfl(ftask, task_of_chunk(min<int64_t>(c, nch - 1), shp.chunks)) : 1.0;
+    double f = 1.0;
+    if (bonus) f = __shfl(ftask, task_of_chunk(min<int64_t>(c, nch - 1), shp));
     if (c >= nch) continue;
     if (namb[k] > kAmbMax) {
       slow = 1;
