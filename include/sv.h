@@ -75,8 +75,10 @@ extern "C" {
  * needed and (size_t)-1 for arguments the calls would reject. The workspace holds the call's work-queue counters
  * and scratch records. It must be zero-filled before its first use (for example allocated with torch.zeros or
  * cleared with hipMemset once); every call leaves its counters at zero again, so the same workspace serves any
- * number of later calls of any shape it is large enough for without being cleared again. Apart from the counters
- * its contents are meaningless after a call. It must not be shared by calls that may run concurrently.
+ * number of later calls of any shape it is large enough for without being cleared again. The counters' positions
+ * depend on the shape: when a workspace comes with a different shape than on its previous call, the call first
+ * clears the counter region of its own layout with one extra small kernel on the same stream. Apart from the
+ * counters its contents are meaningless after a call. It must not be shared by calls that may run concurrently.
  */
 size_t sv_workspace_bytes(int kind, int64_t B, int32_t gamma, int64_t V_or_k);
 

@@ -31,6 +31,8 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
+#include <unordered_map>
 
 #include "sv.h"
 #include "sv_internal.h"
@@ -1764,9 +1766,39 @@ __global__ __launch_bounds__(kDrawBlock) __attribute__((amdgpu_waves_per_eu(kWpe
 }
 
 
+// Zeroes n 16-byte words (vector stores).
+__global__ __launch_bounds__(256) void k_clear(uint4* p, int64_t n) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// The control words of a call (per-sequence counters, the draw ticket, the job slots) fill the start of the
+// workspace, [0, off_part1), at positions that depend on the call's shape, and a call returns them to zero only in
+// its own layout. When a workspace comes with a different layout than on its previous call through this library
+// (or for the first time), that region of the new layout is cleared first, by a small kernel on the same stream.
+bool control_layout_changed(const void* ws, const DensePlan& plan) {
+  static std::mutex mu;
+  static std::unordered_map<const void*, uint64_t> last;
+  uint64_t sig = 1469598103934665603ull;                        // FNV-1a over the layout's control offsets and B
+  for (uint64_t v : {uint64_t(plan.B), uint64_t(plan.off_done), uint64_t(plan.off_tickets), uint64_t(plan.off_jobs),
+                     uint64_t(plan.off_part1)}) {
+    sig = (sig ^ v) * 1099511628211ull;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = last.find(ws);
+  const bool changed = it == last.end() || it->second != sig;
+  last[ws] = sig;
+  return changed;
+}
+
 template <typename T>
 hipError_t launch_typed(const DensePlan& plan, const DenseArgs& a, hipStream_t stream) {
   char* ws = a.ws;
+  if (control_layout_changed(ws, plan)) {
+    const int64_t n16 = int64_t(plan.off_part1 / 16);            // off_part1 is a multiple of 256
+    const unsigned g = unsigned(std::min<int64_t>((n16 + 255) / 256, 1024));
+    hipLaunchKernelGGL(k_clear, dim3(g > 0 ? g : 1), dim3(256), 0, stream, reinterpret_cast<uint4*>(ws), n16);
+  }
   const double T_ = double(a.temperature);
   const float c = float(1.4426950408889634074 / T_);          // log2(e) / T
   DenseParams dp{};

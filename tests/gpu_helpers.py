@@ -44,7 +44,7 @@ def host(out):
     return res
 
 
-def run_dense(case, *, start=None, order=None, target=None, draft=None, u_accept=None, u_sample=None):
+def run_dense(case, *, start=None, order=None, target=None, draft=None, u_accept=None, u_sample=None, ws=None):
     from lossless_draft_verification_spec_amd import sv
     tgt = t_logits(case["target"], case["dtype"]) if target is None else target
     dft = t_logits(case["draft"], case["dtype"]) if draft is None else draft
@@ -53,7 +53,7 @@ def run_dense(case, *, start=None, order=None, target=None, draft=None, u_accept
     ua = t_(case["u_accept"] if u_accept is None else u_accept, torch.float32)
     us = t_(case["u_sample"] if u_sample is None else u_sample, torch.float32)
     out = sv.sv_verify_dense(tgt, dft, t_(case["draft_ids"], torch.int32), ua, us, case["temperature"],
-                             bonus=case["bonus"], start=st, order=od)
+                             bonus=case["bonus"], start=st, order=od, ws=ws)
     torch.cuda.synchronize()
     res = host(out)
     if st is not None:
@@ -61,14 +61,14 @@ def run_dense(case, *, start=None, order=None, target=None, draft=None, u_accept
     return res
 
 
-def run_onehot(case, *, start=None, order=None, target=None):
+def run_onehot(case, *, start=None, order=None, target=None, ws=None):
     from lossless_draft_verification_spec_amd import sv
     tgt = t_logits(case["target"], case["dtype"]) if target is None else target
     st = None if start is None else t_(start, torch.int32)
     od = None if order is None else t_(order, torch.int32)
     out = sv.sv_verify_onehot_draft(tgt, t_(case["draft_ids"], torch.int32), t_(case["u_accept"], torch.float32),
                                     t_(case["u_sample"], torch.float32), case["temperature"], bonus=case["bonus"],
-                                    start=st, order=od)
+                                    start=st, order=od, ws=ws)
     torch.cuda.synchronize()
     res = host(out)
     if st is not None:

@@ -197,6 +197,36 @@ def test_dense_is_deterministic():
         assert np.array_equal(a[k], b[k], equal_nan=True), k
 
 
+def test_workspace_reused_across_shapes_and_kinds():
+    """One workspace, zero-filled once, serves dense and one-hot calls of different shapes in a row: every call
+    returns the work-queue counters, the draw ticket and the job slots to their start state, so each call matches the
+    oracle and a repeated call repeats its outputs bit for bit."""
+    from lossless_draft_verification_spec_amd import sv
+    a = W.dense_case(5, 4, 50_000, dtype="bf16", sigma_t=3.0, sigma_d=1.0, seed=41)
+    b = W.onehot_case(7, 6, 20_011, dtype="bf16", temperature=0.8, seed=42)
+    c = W.dense_case(33, 2, 3_000, dtype="f32", sigma_t=2.0, sigma_d=0.3, seed=43)
+    need = int(max(sv.sv_workspace_bytes(sv.SV_KIND_DENSE, 5, 4, 50_000),
+                   sv.sv_workspace_bytes(sv.SV_KIND_ONEHOT, 7, 6, 20_011),
+                   sv.sv_workspace_bytes(sv.SV_KIND_DENSE, 33, 2, 3_000)))
+    raw = torch.zeros(need + 256, dtype=torch.uint8, device="cuda")     # zero-filled once, 256-byte aligned view
+    off = (-raw.data_ptr()) % 256
+    ws = raw[off:off + need]
+    first = None
+    for i, (case, kind) in enumerate([(a, "dense"), (b, "onehot"), (c, "dense"), (a, "dense"), (b, "onehot")]):
+        if kind == "dense":
+            g = run_dense(case, ws=ws)
+            o = oracle_dense(case)
+        else:
+            g = run_onehot(case, ws=ws)
+            o = oracle_dense(case, onehot=True)
+        log(f"workspace reuse call {i} ({kind}): {compare_decisions(g, o, f'reuse {i}')}")
+        if i == 0:
+            first = g
+        if i == 3:
+            for k in first:
+                assert np.array_equal(first[k], g[k], equal_nan=True), k
+
+
 def test_dense_block_workload_full_size():
     """The dense block workload at its full size (B=64, gamma=16, V=151936, bf16) in the benchmark's launch
     configuration; the oracle runs on every sequence."""
