@@ -59,8 +59,8 @@ def build_support(logits, dtype: str, k: int, top_p: float, temperature: float =
         raise ValueError("top_p must lie in (0, 1]")
     if not (np.isfinite(temperature) and temperature > 0):
         raise ValueError("temperature must be finite and positive")
-    T = float(temperature)
-    p_cut = float(np.float32(top_p))           # the kernel receives top_p as a float32
+    T = float(np.float32(temperature))         # both arrive as float32 values (the C call's argument types)
+    p_cut = float(np.float32(top_p))
     rows = z_all.reshape(-1, V)
     n = rows.shape[0]
     ids = np.full((n, k), -1, np.int32)

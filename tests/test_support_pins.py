@@ -88,10 +88,11 @@ def test_full_support_is_the_softmax():
     z = _random_rows(5, 4, 37)
     for T in (0.7, 1.0, 1.6):
         out = osup.build_support(z, "f32", 37, 1.0, T)
+        T32 = float(np.float32(T))                 # the temperature is a float32 argument
         for r in range(4):
             ids = out["ids"][r]
             assert int(out["count"][r]) == 37
-            ref = special.softmax(z[r].astype(np.float64) / T)[ids]
+            ref = special.softmax(z[r].astype(np.float64) / T32)[ids]
             np.testing.assert_allclose(out["probs"][r], ref, rtol=2e-7, atol=1e-30)
             full = osup.build_support(z[r:r + 1], "f32", 37, 1.0, T, renorm=False)
             np.testing.assert_allclose(full["probs"][0], ref, rtol=2e-7, atol=1e-30)
