@@ -6,8 +6,9 @@ headline value is verified draft positions per second; the roofline object repor
 bandwidth: algorithmic bytes per launch (every verified logit of both tensors, 2*B*gamma*V*2, plus the row pair each
 rejected sequence's draw reads again, or the target row of a bonus draw) over its average duration, timed with HIP
 events taken from the kernel's own dispatch on its stream, in a second timed region of the same steps (the whole-call
-figure comes from steps without the events). The other workloads (tiny dense, greedy one-hot, sparse top-64,
-masked-diffusion window with 4 chained rounds) are timed after it and reported under "workloads".
+figure comes from steps without the events). The other workloads (the dense -> top-k/top-p support -> sparse verify
+chain on the headline's logits, tiny dense, greedy one-hot, sparse top-64, masked-diffusion window with 4 chained
+rounds) are timed after it and reported under "workloads".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--cpu-seconds S] [--only NAME]
 Prints one JSON line on stdout.
@@ -151,6 +152,59 @@ def bench_dense(case, steps, warmup, torch, sv, d, profile_events=True):
     return res
 
 
+SUPPORT = "support_chain_B64_g16_V151936_k50_p095_bf16"
+
+
+def bench_support(case, steps, warmup, torch, sv, d, k=50, top_p=0.95):
+    """Dense -> sparse -> verify on the headline workload's logits: top-k / top-p supports of the target rows
+    (B x (gamma+1)) and of the draft rows (B x gamma), then the sparse verify of the drafted ids on them. The two
+    support builds are timed from their own dispatches (HIP events) in a second region of the same steps."""
+    B, G, V = case["B"], case["gamma"], case["V"]
+    rows_t, rows_d = B * (G + 1), B * G
+    ncopies = 2                                                         # 1.28 GB per step pair: no cache reuse
+    tgts = [to_dev_logits(case["target"], "bf16", torch, d).view(rows_t, V) for _ in range(ncopies)]
+    dfts = [to_dev_logits(case["draft"], "bf16", torch, d).view(rows_d, V) for _ in range(ncopies)]
+    ids = torch.from_numpy(case["draft_ids"]).to(d)
+    ua = torch.from_numpy(case["u_accept"]).to(d)
+    us = torch.from_numpy(case["u_sample"]).to(d)
+    ws_t = sv.support_workspace(rows_t, V, k, d)
+    ws_d = sv.support_workspace(rows_d, V, k, d)
+    po, qo, vo = {}, {}, {}
+    ev_t, ev_d = HipEvents(steps), HipEvents(steps)
+    state = {"timed": False}
+
+    def step(i):
+        c = i % ncopies
+        if state["timed"]:
+            sv.sv_profile_next_stats(ev_t.pairs[i][0], ev_t.pairs[i][1])
+        sv.sv_build_support(tgts[c], k, top_p, case["temperature"], True, out=po, ws=ws_t)
+        if state["timed"]:
+            sv.sv_profile_next_stats(ev_d.pairs[i][0], ev_d.pairs[i][1])
+        sv.sv_build_support(dfts[c], k, top_p, case["temperature"], True, out=qo, ws=ws_d)
+        sv.sv_verify_sparse(po["ids"].view(B, G + 1, k), po["probs"].view(B, G + 1, k), qo["ids"].view(B, G, k),
+                            qo["probs"].view(B, G, k), ids, ua, us, bonus=1, vocab_size=V, out=vo)
+
+    ms, wall = time_steps(step, steps, warmup, torch)
+    state["timed"] = True
+    time_steps(step, steps, 0, torch)
+    state["timed"] = False
+    kt = float(np.mean([ev_t.elapsed_ms(i) for i in range(steps)]))
+    kd = float(np.mean([ev_d.elapsed_ms(i) for i in range(steps)]))
+    ev_t.close()
+    ev_d.close()
+    out_row = k * 8 + 8                                                 # ids, probs, count, flags per row
+    bytes_t, bytes_d = rows_t * (V * 2 + out_row), rows_d * (V * 2 + out_row)
+    n = vo["n_accepted"].cpu().numpy()
+    return dict(ms_per_step=ms, wall_ms_per_step=wall, positions=B * G, positions_per_s=B * G / (ms * 1e-3),
+                k=k, top_p=top_p, mean_n_accepted=float(n.mean()),
+                mean_kept_target=float(po["count"].float().mean().item()),
+                mean_kept_draft=float(qo["count"].float().mean().item()),
+                support_kernel_ms_target=kt, support_kernel_ms_draft=kd,
+                support_bytes_target=bytes_t, support_bytes_draft=bytes_d,
+                support_GBps_target=bytes_t / (kt * 1e-3) / 1e9, support_GBps_draft=bytes_d / (kd * 1e-3) / 1e9,
+                support_hbm_frac=(bytes_t + bytes_d) / ((kt + kd) * 1e-3) / 1e9 / HBM_PEAK_GBPS)
+
+
 def bench_sparse(case, steps, warmup, torch, sv, d):
     B, G, k = case["B"], case["gamma"], case["k"]
     t = {key: torch.from_numpy(np.ascontiguousarray(case[key])).to(d)
@@ -224,20 +278,30 @@ def cpu_baseline(case, seconds):
                        f"numpy float64, one thread")
 
 
+KERNEL_SOURCES = ("sv_dense.hip", "sv_device.h", "sv_internal.h")    # what k_verify is compiled from
+
+
+def kernel_source_sha():
+    """sha256 over the verifier kernel's source files, in KERNEL_SOURCES order."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "lossless_draft_verification_spec_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def measured_traffic():
     """HBM bytes per launch of the verifier kernel from the committed FETCH_SIZE / WRITE_SIZE counter summary, or
     None when the kernel source has changed since the counters were taken."""
-    import hashlib
     prof = os.path.join(ROOT, "profiles", "k_verify_dense_block_traffic.txt")
-    src = os.path.join(ROOT, "lossless_draft_verification_spec_amd", "csrc", "sv_dense.hip")
     try:
         rec = None
         with open(prof) as f:
             for ln in f:
                 if ln.startswith("TRAFFIC_JSON "):
                     rec = json.loads(ln[len("TRAFFIC_JSON "):])
-        with open(src, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        sha = kernel_source_sha()
     except OSError:
         return None
     if rec is None or rec.get("source_sha256") != sha:
@@ -281,6 +345,10 @@ def main():
     log("headline", json.dumps(r))
 
     others = {}
+    if args.only in (None, SUPPORT):
+        others[SUPPORT] = bench_support(head, args.steps, args.warmup, torch, sv, d)
+        log(SUPPORT, json.dumps(others[SUPPORT]))
+        torch.cuda.empty_cache()
     names = [n for n in workloads.WORKLOADS if n != HEADLINE]
     if args.only:
         names = [n for n in names if n == args.only]

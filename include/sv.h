@@ -10,8 +10,9 @@
  * both sides before the ratio).
  *
  * Conventions shared by every entry point
- * - Every array argument is a DEVICE pointer owned by the caller. The library allocates nothing, keeps no state
- *   between calls and may be called from several host threads on different streams.
+ * - Every array argument is a DEVICE pointer owned by the caller. The library allocates nothing and may be called
+ *   from several host threads on different streams; between calls it keeps only a host-side note of the layout
+ *   each workspace was last used with (see sv_workspace_bytes).
  * - Work is enqueued on `stream` (a hipStream_t, or NULL for the null stream) of the current device; outputs are
  *   valid once that stream has reached the enqueued work. No call synchronises the host.
  * - The return value is 0 (SV_OK) or a negative SV_ERR_* code. Argument errors are detected on the host BEFORE any
@@ -87,11 +88,12 @@ const char* sv_status_string(int status);
 
 /*
  * Profiling hook (no counterpart on the pages; it lets a caller time the verifier's kernel on its own). When both
- * events are non-NULL, the next sv_verify_dense or sv_verify_onehot_draft call made on this host thread records
- * `start_event` when its kernel starts and `stop_event` when it ends (from the dispatch itself), on that call's
- * stream, and then forgets them; hipEventElapsedTime(start, stop) is that kernel's duration. The events (hipEvent_t) are created
- * and owned by the caller. Passing two NULLs clears a pending request. Returns SV_OK, or SV_ERR_NULL when exactly
- * one event is NULL. The request is per host thread, so concurrent callers on other threads are unaffected.
+ * events are non-NULL, the next sv_verify_dense, sv_verify_onehot_draft or sv_build_support call made on this host
+ * thread records `start_event` when its kernel starts and `stop_event` when it ends (from the dispatch itself), on
+ * that call's stream, and then forgets them; hipEventElapsedTime(start, stop) is that kernel's duration. The events
+ * (hipEvent_t) are created and owned by the caller. Passing two NULLs clears a pending request. Returns SV_OK, or
+ * SV_ERR_NULL when exactly one event is NULL. The request is per host thread, so concurrent callers on other
+ * threads are unaffected.
  */
 int sv_profile_next_stats(void* start_event, void* stop_event);
 
@@ -174,6 +176,40 @@ int sv_verify_sparse(const int32_t* p_ids, const float* p_probs,
                      const int32_t* spec_ids, const float* u_accept, const float* u_sample, int32_t bonus,
                      uint8_t* accept, int32_t* n_accepted, int32_t* out_token,
                      float* correction_probs, float* p_spec, float* q_spec, uint32_t* flags,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Top-k / top-p support builder: dense logit rows to the (ids, probs) supports that sv_verify_sparse takes. The
+ * sampler settings are those of the throughput test on the Uno page (section "The speedup, without the 'up to'":
+ * temperature 1, top-p 0.95, top-k 50), whose sparse verify routine (section "What 'lossless' actually has to mean")
+ * takes p and q as such supports; the temperature divides the logits first (DFlash/DFlash2 guide, section 9 Q3).
+ * The pages name the parameters only; the procedure is the usual sampler's, in this order:
+ * - top-k: the k largest logits of the row, equal logits ordered by ascending id, listed in descending order
+ *   (the order is the same at every T > 0);
+ * - top-p on the top-k distribution t_j = e_j / sum(e), e_j = exp(z_j / T - z_0 / T): slot j is kept when j = 0 or
+ *   t_0 + ... + t_{j-1} < top_p, i.e. the shortest prefix whose mass reaches top_p, the crossing slot included;
+ *   the cumulative sums and the comparison are float64;
+ * - probs of kept slots: renorm = 1, e_j over the sum of the kept e (they sum to 1); renorm = 0, the row's full
+ *   softmax probability exp(z_j / T) / sum over all V of exp(z_i / T) (they sum to the kept mass). Slots past the
+ *   kept ones keep their ids and get probability 0, so every output row is a valid support of k slots.
+ *
+ * logits       rows of V logits of `dtype`, row r at logits + r * ld elements (ld >= V; V contiguous); pointer
+ *              aligned to the element size.
+ * rows, V      1 <= rows, V <= 2^31-1.   k: 1 .. min(SV_MAX_K, V).
+ * temperature  T > 0, finite.   top_p: in (0, 1] (1: no cut beyond rounding).   renorm: 0 or 1.
+ * ids          [rows][k] int32 (required): the top-k ids in descending order.
+ * probs        [rows][k] float (required).
+ * count        [rows] int32 or NULL: kept slots (1 .. k).
+ * flags        [rows] uint32 or NULL: SV_FLAG_NONFINITE for a row with a NaN or +inf logit, or all -inf; such a
+ *              row gets ids -1, probs NaN, count 0 (so a sparse verify of it flags the sequence). 0 otherwise.
+ * workspace    >= sv_support_workspace_bytes(rows, V, k) bytes, 256-byte aligned, zero-filled before its first
+ *              use (the same contract as sv_workspace_bytes; a workspace may alternate between this call and the
+ *              verify calls).
+ */
+size_t sv_support_workspace_bytes(int64_t rows, int64_t V, int32_t k);
+int sv_build_support(const void* logits, int64_t ld, int dtype, int64_t rows, int64_t V,
+                     float temperature, int32_t k, float top_p, int32_t renorm,
+                     int32_t* ids, float* probs, int32_t* count, uint32_t* flags,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus

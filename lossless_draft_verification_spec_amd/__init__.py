@@ -5,7 +5,8 @@ The verifier itself is the HIP library ``libsv.so`` (C ABI in ``include/sv.h``);
 input generators work without the built library; using a verifier entry point without the library raises.
 """
 _BINDING = ("sv_verify_dense", "sv_verify_onehot_draft", "sv_verify_sparse", "sv_workspace_bytes",
-            "sv_status_string", "SVError", "workspace")
+            "sv_status_string", "SVError", "workspace", "sv_build_support", "sv_support_workspace_bytes",
+            "support_workspace")
 
 
 def __getattr__(name):

@@ -1,5 +1,5 @@
 // Exported C entry points of the verifier library: argument validation on the host (before any HIP call),
-// workspace sizing and launch sequencing. The kernels live in sv_dense.hip and sv_sparse.hip.
+// workspace sizing and launch sequencing. The kernels live in sv_dense.hip, sv_sparse.hip and sv_support.hip.
 
 #include <hip/hip_runtime.h>
 
@@ -47,11 +47,12 @@ int check_grid(const sv::DensePlan& p) {
   return SV_OK;
 }
 
-// Events for the next dense / one-hot call on this host thread (see sv_profile_next_stats).
+// Events for the next dense, one-hot or support call on this host thread (see sv_profile_next_stats).
 thread_local void* t_ev_start = nullptr;
 thread_local void* t_ev_stop = nullptr;
 
-void take_events(sv::DenseArgs& a) {
+template <typename Args>
+void take_events(Args& a) {
   a.ev_start = t_ev_start;
   a.ev_stop = t_ev_stop;
   t_ev_start = t_ev_stop = nullptr;
@@ -183,6 +184,38 @@ int sv_verify_sparse(const int32_t* p_ids, const float* p_probs,
   sv::SparseArgs a{p_ids, p_probs, q_ids, q_probs, B, gamma, kp, kq, vocab_size, spec_ids, u_accept, u_sample, bonus,
                    accept, n_accepted, out_token, correction_probs, p_spec, q_spec, flags};
   return sv::launch_sparse(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+size_t sv_support_workspace_bytes(int64_t rows, int64_t V, int32_t k) {
+  if (rows < 1 || rows > kMaxI32 || V < 1 || V > kMaxI32 || k < 1 || k > SV_MAX_K || k > V)
+    return static_cast<size_t>(-1);
+  return sv::make_support_plan(rows, V, k, SV_F32, 1).total;
+}
+
+int sv_build_support(const void* logits, int64_t ld, int dtype, int64_t rows, int64_t V,
+                     float temperature, int32_t k, float top_p, int32_t renorm,
+                     int32_t* ids, float* probs, int32_t* count, uint32_t* flags,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!logits || !ids || !probs) return SV_ERR_NULL;
+  if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
+  if (rows < 1 || rows > kMaxI32 || V < 1 || V > kMaxI32 || k < 1 || k > SV_MAX_K || k > V || ld < V)
+    return SV_ERR_SHAPE;
+  if (double(rows - 1) * double(ld) + double(V) > 9.0e18) return SV_ERR_SHAPE;
+  if (!std::isfinite(temperature) || !(temperature > 0.f)) return SV_ERR_TEMP;
+  if (!(top_p > 0.f && top_p <= 1.f)) return SV_ERR_ARG;
+  if (renorm != 0 && renorm != 1) return SV_ERR_ARG;
+  if (!aligned(logits, dtype == SV_BF16 ? 2 : 4)) return SV_ERR_ALIGN;
+  const void* ptrs[] = {ids, probs, count, flags};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, 4)) return SV_ERR_ALIGN;
+  const sv::SupportPlan plan = sv::make_support_plan(rows, V, k, dtype, sv::resident_workgroups());
+  if (double(plan.items) > double(kMaxI32)) return SV_ERR_SHAPE;
+  const int st = check_workspace(workspace, workspace_bytes, plan.total);
+  if (st != SV_OK) return st;
+  sv::SupportArgs a{logits, ld, dtype, temperature, top_p, renorm, ids, probs, count, flags,
+                    static_cast<char*>(workspace)};
+  take_events(a);
+  return sv::launch_support(plan, a, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
 }  // extern "C"

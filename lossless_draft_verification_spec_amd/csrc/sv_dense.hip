@@ -35,6 +35,7 @@
 #include <unordered_map>
 
 #include "sv.h"
+#include "sv_device.h"
 #include "sv_internal.h"
 
 namespace sv {
@@ -97,89 +98,9 @@ struct alignas(16) Partial1 {
 };
 
 // ----------------------------------------------------------------------------------------------------------------
-// element access
+// helpers that depend on the job record
 // ----------------------------------------------------------------------------------------------------------------
 
-// Loads through the global address space. The logit rows are always global memory; saying so keeps the loads
-// global_load instructions (not flat ones) wherever the compiler cannot see where a pointer came from.
-#define SV_GLOBAL __attribute__((address_space(1)))
-template <typename V>
-__device__ __forceinline__ V gload(const V* p) {
-  return *(const SV_GLOBAL V*)(p);
-}
-
-template <typename T> struct Vec;
-template <> struct Vec<float> {
-  static constexpr int kEPV = 4;                                  // elements per 16-byte vector
-  __device__ static __forceinline__ void unpack(const uint4& w, float* v) {
-    v[0] = __uint_as_float(w.x); v[1] = __uint_as_float(w.y);
-    v[2] = __uint_as_float(w.z); v[3] = __uint_as_float(w.w);
-  }
-  __device__ static __forceinline__ float load1(const float* p) { return gload(p); }
-};
-template <> struct Vec<uint16_t> {
-  static constexpr int kEPV = 8;
-  __device__ static __forceinline__ void unpack(const uint4& w, float* v) {
-    v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xFFFF0000u);
-    v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xFFFF0000u);
-    v[4] = __uint_as_float(w.z << 16); v[5] = __uint_as_float(w.z & 0xFFFF0000u);
-    v[6] = __uint_as_float(w.w << 16); v[7] = __uint_as_float(w.w & 0xFFFF0000u);
-  }
-  __device__ static __forceinline__ float load1(const uint16_t* p) { return __uint_as_float(uint32_t(gload(p)) << 16); }
-};
-
-__device__ __forceinline__ float ex2f(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Element i of a row of V logits, -inf for i >= V. The load address is clamped into the row and the value selected
-// afterwards, so a run of such loads issues without a branch (and a wait) per element.
-template <typename T>
-__device__ __forceinline__ float elem_or_ninf(const T* row, int64_t i, int64_t V) {
-  const float z = Vec<T>::load1(row + (i < V ? i : V - 1));
-  return i < V ? z : -INFINITY;
-}
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint4 gload4(const uint4* p) {
-  const u32x4 r = *(const SV_GLOBAL u32x4*)(p);
-  return make_uint4(r.x, r.y, r.z, r.w);
-}
-
-// ----------------------------------------------------------------------------------------------------------------
-// wave-level reductions and scans through DPP: data-parallel-primitive moves between the lanes of a row of 16 inside
-// the VALU (a few cycles each, where a cross-lane shuffle is an LDS round trip); rows are combined with readlane.
-// All 64 lanes must be active. The operation order is fixed, so results are bitwise reproducible and identical in
-// every lane.
-// ----------------------------------------------------------------------------------------------------------------
-
-constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
-constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
-constexpr int kDppHalfMirror = 0x141;  // row_half_mirror: lane i <- lane 7 - i within each 8
-constexpr int kDppMirror = 0x140;      // row_mirror: lane i <- lane 15 - i within each row
-constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;   // row_shr:n
-constexpr int kDppBcast15 = 0x142;     // row_bcast:15: lane 15 of the previous row
-constexpr int kDppBcast31 = 0x143;     // row_bcast:31: lane 31
-
-// v moved by the DPP control CTRL; lanes outside ROWS, or whose source lies outside the row, get `old`.
-template <int CTRL, int ROWS = 0xF>
-__device__ __forceinline__ int dpp_i(int old, int v) {
-  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWS, 0xF, false);
-}
-template <int CTRL, int ROWS = 0xF>
-__device__ __forceinline__ float dpp_f(float old, float v) {
-  return __int_as_float(dpp_i<CTRL, ROWS>(__float_as_int(old), __float_as_int(v)));
-}
-template <int CTRL, int ROWS = 0xF>
-__device__ __forceinline__ double dpp_d(double old, double v) {
-  return __hiloint2double(dpp_i<CTRL, ROWS>(__double2hiint(old), __double2hiint(v)),
-                          dpp_i<CTRL, ROWS>(__double2loint(old), __double2loint(v)));
-}
-// v moved by CTRL where every lane's source lies inside its row and every row takes part (no `old` operand needed).
-template <int CTRL>
-__device__ __forceinline__ double dpp_full_d(double v) {
-  return __hiloint2double(__builtin_amdgcn_mov_dpp(__double2hiint(v), CTRL, 0xF, 0xF, true),
-                          __builtin_amdgcn_mov_dpp(__double2loint(v), CTRL, 0xF, 0xF, true));
-}
 // The job's fields are the same in every lane (read from shared memory after a barrier): moved to scalar registers,
 // so that branches on them are uniform.
 __device__ __forceinline__ Job uniform_job(const Job& j) {
@@ -191,112 +112,6 @@ __device__ __forceinline__ Job uniform_job(const Job& j) {
   return r;
 }
 
-__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
-  const uint64_t u = uint64_t(v);
-  return int64_t((uint64_t(__builtin_amdgcn_readfirstlane(uint32_t(u >> 32))) << 32) |
-                 __builtin_amdgcn_readfirstlane(uint32_t(u)));
-}
-__device__ __forceinline__ double readlane_d(double v, int l) {
-  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
-                          __builtin_amdgcn_readlane(__double2loint(v), l));
-}
-__device__ __forceinline__ float readlane_f(float v, int l) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
-
-__device__ __forceinline__ double wave_sum(double v) {
-  v += dpp_full_d<kDppXor1>(v);
-  v += dpp_full_d<kDppXor2>(v);
-  v += dpp_full_d<kDppHalfMirror>(v);
-  v += dpp_full_d<kDppMirror>(v);
-  return (readlane_d(v, 0) + readlane_d(v, 16)) + (readlane_d(v, 32) + readlane_d(v, 48));
-}
-
-__device__ __forceinline__ double wave_max_d(double v) {
-  v = fmax(v, dpp_d<kDppXor1>(v, v));
-  v = fmax(v, dpp_d<kDppXor2>(v, v));
-  v = fmax(v, dpp_d<kDppHalfMirror>(v, v));
-  v = fmax(v, dpp_d<kDppMirror>(v, v));
-  return fmax(fmax(readlane_d(v, 0), readlane_d(v, 16)), fmax(readlane_d(v, 32), readlane_d(v, 48)));
-}
-
-__device__ __forceinline__ float wave_max_f(float v) {
-  v = fmaxf(v, dpp_f<kDppXor1>(v, v));
-  v = fmaxf(v, dpp_f<kDppXor2>(v, v));
-  v = fmaxf(v, dpp_f<kDppHalfMirror>(v, v));
-  v = fmaxf(v, dpp_f<kDppMirror>(v, v));
-  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
-}
-
-__device__ __forceinline__ int wave_min_i(int v) {
-  v = min(v, dpp_i<kDppXor1>(v, v));
-  v = min(v, dpp_i<kDppXor2>(v, v));
-  v = min(v, dpp_i<kDppHalfMirror>(v, v));
-  v = min(v, dpp_i<kDppMirror>(v, v));
-  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
-             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
-}
-
-// Inclusive running sum over the lanes in lane order (Hillis-Steele inside each row, then row carries).
-__device__ __forceinline__ double wave_incl_scan(double v) {
-  v += dpp_d<kDppShr1>(0.0, v);
-  v += dpp_d<kDppShr2>(0.0, v);
-  v += dpp_d<kDppShr4>(0.0, v);
-  v += dpp_d<kDppShr8>(0.0, v);
-  v += dpp_d<kDppBcast15, 0xA>(0.0, v);
-  v += dpp_d<kDppBcast31, 0xC>(0.0, v);
-  return v;
-}
-
-// ----------------------------------------------------------------------------------------------------------------
-// block reductions (fixed order, so results are bitwise reproducible)
-// ----------------------------------------------------------------------------------------------------------------
-
-template <int BLOCK>
-__device__ __forceinline__ float block_max(float v, float* sh) {
-  v = wave_max_f(v);
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  __syncthreads();
-  if (l == 0) sh[w] = v;
-  __syncthreads();
-  float r = sh[0];
-#pragma unroll
-  for (int i = 1; i < BLOCK / 64; ++i) r = fmaxf(r, sh[i]);
-  return r;
-}
-
-template <int BLOCK>
-__device__ __forceinline__ double block_sum(double v, double* sh) {
-  v = wave_sum(v);
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  __syncthreads();
-  if (l == 0) sh[w] = v;
-  __syncthreads();
-  double r = sh[0];
-#pragma unroll
-  for (int i = 1; i < BLOCK / 64; ++i) r += sh[i];
-  return r;
-}
-
-// ----------------------------------------------------------------------------------------------------------------
-// passing records between workgroups of one kernel
-// ----------------------------------------------------------------------------------------------------------------
-// Each XCD has its own write-back L2, so a plain store from one workgroup may not be visible to a workgroup on
-// another XCD before the kernel ends. Records handed over inside a kernel are stored and loaded at device scope
-// (written through to, and read from, the level where all XCDs agree); the writer waits for its stores to complete
-// and then counts itself on a per-sequence counter (a system-scope atomic, performed where all XCDs agree); the
-// workgroup that brings the count to its total reads the records. Nobody waits on a counter.
-template <typename V>
-__device__ __forceinline__ void st_dev(V* p, V v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <typename V>
-__device__ __forceinline__ V ld_dev(const V* p) {
-  return __hip_atomic_load(const_cast<V*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int32_t ctr_add(int32_t* p) {
-  return __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
 
 // ----------------------------------------------------------------------------------------------------------------
 // 1. row statistics
@@ -381,15 +196,6 @@ __device__ __forceinline__ void absorb(Run& st, const float* v, float c) {
 #pragma unroll
     for (int k = 0; k + w < N; k += 2 * w) t[k] += t[k + w];
   st.s += t[0];
-}
-
-template <bool NT>
-__device__ __forceinline__ uint4 load_vec(const uint4* p) {
-  const SV_GLOBAL u32x4* q = (const SV_GLOBAL u32x4*)(p);
-  u32x4 r;
-  if constexpr (NT) r = __builtin_nontemporal_load(q);
-  else r = *q;
-  return make_uint4(r.x, r.y, r.z, r.w);
 }
 
 // One work item: segment `seg` of one row. Returns without writing when the row's slot lies before start.
@@ -1772,32 +1578,18 @@ __global__ __launch_bounds__(256) void k_clear(uint4* p, int64_t n) {
     p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
-// The control words of a call (per-sequence counters, the draw ticket, the job slots) fill the start of the
-// workspace, [0, off_part1), at positions that depend on the call's shape, and a call returns them to zero only in
-// its own layout. When a workspace comes with a different layout than on its previous call through this library
-// (or for the first time), that region of the new layout is cleared first, by a small kernel on the same stream.
-bool control_layout_changed(const void* ws, const DensePlan& plan) {
-  static std::mutex mu;
-  static std::unordered_map<const void*, uint64_t> last;
-  uint64_t sig = 1469598103934665603ull;                        // FNV-1a over the layout's control offsets and B
-  for (uint64_t v : {uint64_t(plan.B), uint64_t(plan.off_done), uint64_t(plan.off_tickets), uint64_t(plan.off_jobs),
-                     uint64_t(plan.off_part1)}) {
-    sig = (sig ^ v) * 1099511628211ull;
-  }
-  std::lock_guard<std::mutex> lock(mu);
-  auto it = last.find(ws);
-  const bool changed = it == last.end() || it->second != sig;
-  last[ws] = sig;
-  return changed;
-}
-
 template <typename T>
 hipError_t launch_typed(const DensePlan& plan, const DenseArgs& a, hipStream_t stream) {
   char* ws = a.ws;
-  if (control_layout_changed(ws, plan)) {
-    const int64_t n16 = int64_t(plan.off_part1 / 16);            // off_part1 is a multiple of 256
-    const unsigned g = unsigned(std::min<int64_t>((n16 + 255) / 256, 1024));
-    hipLaunchKernelGGL(k_clear, dim3(g > 0 ? g : 1), dim3(256), 0, stream, reinterpret_cast<uint4*>(ws), n16);
+  // the control words (per-sequence counters, the draw ticket, the job slots) fill [0, off_part1) at positions that
+  // depend on the shape; the signature covers the offsets that place them
+  uint64_t sig = kLayoutDense;
+  for (uint64_t v : {uint64_t(plan.B), uint64_t(plan.off_done), uint64_t(plan.off_tickets), uint64_t(plan.off_jobs),
+                     uint64_t(plan.off_part1)})
+    sig = layout_mix(sig, v);
+  if (workspace_layout_changed(ws, sig)) {
+    const hipError_t e = clear_control(ws, plan.off_part1, stream);
+    if (e != hipSuccess) return e;
   }
   const double T_ = double(a.temperature);
   const float c = float(1.4426950408889634074 / T_);          // log2(e) / T
@@ -1844,6 +1636,28 @@ hipError_t launch_typed(const DensePlan& plan, const DenseArgs& a, hipStream_t s
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace
+
+// A call's control words (counters that every call returns to zero) sit at positions that depend on its shape and
+// kind, and a call returns them to zero only in its own layout. The library remembers, per workspace pointer, the
+// layout signature of the last call that used it; when a workspace comes with another signature (or for the first
+// time), the caller clears the new layout's control region first (clear_control), on the same stream.
+bool workspace_layout_changed(const void* ws, uint64_t sig) {
+  static std::mutex mu;
+  static std::unordered_map<const void*, uint64_t> last;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = last.find(ws);
+  const bool changed = it == last.end() || it->second != sig;
+  last[ws] = sig;
+  return changed;
+}
+
+hipError_t clear_control(char* ws, size_t bytes, hipStream_t stream) {
+  const int64_t n16 = int64_t(bytes / 16);                       // control regions are multiples of 256 bytes
+  if (n16 <= 0) return hipSuccess;
+  const unsigned g = unsigned(std::min<int64_t>((n16 + 255) / 256, 1024));
+  hipLaunchKernelGGL(k_clear, dim3(g), dim3(256), 0, stream, reinterpret_cast<uint4*>(ws), n16);
+  return hipGetLastError();
+}
 
 // Resident workgroups of the kernel on the current device (compute units x workgroups per compute unit).
 int resident_workgroups() {

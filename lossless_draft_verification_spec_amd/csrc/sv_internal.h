@@ -73,6 +73,13 @@ struct DensePlan {
 DensePlan make_dense_plan(int64_t B, int32_t G, int64_t V, int32_t ntens, int dtype, int64_t resident);
 int resident_workgroups();
 
+// Workspace layout bookkeeping shared by the calls that keep control words in a workspace (see sv_dense.hip).
+constexpr uint64_t kLayoutDense = 0xcbf29ce484222325ull;     // FNV-1a offset basis, one per kind of layout
+constexpr uint64_t kLayoutSupport = 0x84222325cbf29ce4ull;
+inline uint64_t layout_mix(uint64_t sig, uint64_t v) { return (sig ^ v) * 1099511628211ull; }
+bool workspace_layout_changed(const void* ws, uint64_t sig);
+hipError_t clear_control(char* ws, size_t bytes, hipStream_t stream);   // zeroes [ws, ws + bytes), bytes % 16 == 0
+
 struct DenseArgs {
   const void* tgt; int64_t t_seq, t_row;
   const void* dft; int64_t d_seq, d_row;     // dft == nullptr: one-hot drafts
@@ -99,5 +106,37 @@ struct SparseArgs {
 };
 
 hipError_t launch_sparse(const SparseArgs& a, hipStream_t stream);
+
+// Top-k / top-p support builder (sv_support.hip): sizes and workspace layout of one call.
+struct SupportPlan {
+  int64_t rows = 0;
+  int64_t V = 0;
+  int32_t k = 0;
+  int64_t head_rows = 0;   // rows taken whole, one workgroup each (full resident rounds)
+  int32_t nseg = 1;        // segments of each later row
+  int32_t nlay = 1;        // segment records per row in the workspace
+  int64_t items = 0;       // workgroups of the launch
+  int64_t attach = 0;      // segments of the later rows that ride on whole-row items (0: they are items)
+  size_t off_ctr = 0;      // int32 per row (one per 256 bytes): segments finished, returned to 0 by the row's merge
+  size_t ctr_bytes = 0;    // the control region [0, ctr_bytes)
+  size_t off_keys = 0;     // per (row, segment): up to k uint64 keys
+  size_t off_part = 0;     // per (row, segment): the segment's statistics
+  size_t total = 0;
+};
+
+// resident: workgroups resident on the device at once (it sets which rows are cut into segments; the workspace size
+// depends on neither it nor the dtype).
+SupportPlan make_support_plan(int64_t rows, int64_t V, int32_t k, int dtype, int64_t resident);
+
+struct SupportArgs {
+  const void* logits; int64_t ld; int dtype;
+  float temperature; float top_p; int32_t renorm;
+  int32_t* ids; float* probs; int32_t* count; uint32_t* flags;
+  char* ws;
+  void* ev_start = nullptr;   // optional hipEvent_t pair recorded from the kernel's dispatch
+  void* ev_stop = nullptr;
+};
+
+hipError_t launch_support(const SupportPlan& plan, const SupportArgs& a, hipStream_t stream);
 
 }  // namespace sv

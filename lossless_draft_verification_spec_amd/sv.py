@@ -21,7 +21,7 @@ SV_FLAG_NONFINITE, SV_FLAG_ID_RANGE, SV_FLAG_EMPTY_RESIDUAL, SV_FLAG_Q_ZERO = 1,
 SV_MAX_GAMMA, SV_MAX_K = 1024, 256
 
 EXPORTS = ("sv_workspace_bytes", "sv_status_string", "sv_profile_next_stats", "sv_verify_dense",
-           "sv_verify_onehot_draft", "sv_verify_sparse")
+           "sv_verify_onehot_draft", "sv_verify_sparse", "sv_support_workspace_bytes", "sv_build_support")
 
 
 def _load() -> ctypes.CDLL:
@@ -43,6 +43,10 @@ def _load() -> ctypes.CDLL:
     lib.sv_verify_onehot_draft.restype = ctypes.c_int
     lib.sv_verify_sparse.argtypes = [P, P, P, P, I64, I32, I32, I32, I64, P, P, P, I32, P, P, P, P, P, P, P, P, SZ, P]
     lib.sv_verify_sparse.restype = ctypes.c_int
+    lib.sv_support_workspace_bytes.argtypes = [I64, I64, I32]
+    lib.sv_support_workspace_bytes.restype = SZ
+    lib.sv_build_support.argtypes = [P, I64, ctypes.c_int, I64, I64, F, I32, F, I32, P, P, P, P, P, SZ, P]
+    lib.sv_build_support.restype = ctypes.c_int
     return lib
 
 
@@ -57,6 +61,10 @@ class SVError(RuntimeError):
 
 def sv_workspace_bytes(kind: int, B: int, gamma: int, V_or_k: int) -> int:
     return int(LIB.sv_workspace_bytes(kind, B, gamma, V_or_k))
+
+
+def sv_support_workspace_bytes(rows: int, V: int, k: int) -> int:
+    return int(LIB.sv_support_workspace_bytes(rows, V, k))
 
 
 def sv_status_string(status: int) -> str:
@@ -104,8 +112,7 @@ def _logits_layout(t, name, rows, B, device):
     return seq, row
 
 
-def workspace(kind: int, B: int, gamma: int, V_or_k: int, device) -> torch.Tensor | None:
-    n = sv_workspace_bytes(kind, B, gamma, V_or_k)
+def _zeroed_workspace(n: int, device) -> torch.Tensor | None:
     if n == (1 << 64) - 1:
         raise SVError(-2)
     if n == 0:
@@ -113,6 +120,14 @@ def workspace(kind: int, B: int, gamma: int, V_or_k: int, device) -> torch.Tenso
     ws = torch.zeros(n + 256, dtype=torch.uint8, device=device)   # control words must start at zero
     off = (-ws.data_ptr()) % 256
     return ws[off:off + n]
+
+
+def workspace(kind: int, B: int, gamma: int, V_or_k: int, device) -> torch.Tensor | None:
+    return _zeroed_workspace(sv_workspace_bytes(kind, B, gamma, V_or_k), device)
+
+
+def support_workspace(rows: int, V: int, k: int, device) -> torch.Tensor | None:
+    return _zeroed_workspace(sv_support_workspace_bytes(rows, V, k), device)
 
 
 def _dtype_code(t):
@@ -223,6 +238,41 @@ def sv_verify_sparse(p_ids, p_probs, q_ids, q_probs, spec_ids, u_accept, u_sampl
                               _ptr(o["n_accepted"]), _ptr(o["out_token"]), _ptr(o.get("correction_probs")),
                               _ptr(o.get("p_spec")), _ptr(o.get("q_spec")), _ptr(o.get("flags")), None, 0,
                               _stream(stream))
+    if st != SV_OK:
+        raise SVError(st)
+    return o
+
+
+def sv_build_support(logits, k, top_p, temperature=1.0, renorm=True, *, out=None, ws=None, stream=None):
+    """Top-k / top-p supports of logit rows (see ``sv_build_support`` in include/sv.h). logits [..., V] float32 or
+    bfloat16: a contiguous tensor, or a 2-D tensor whose rows may be strided. Returns a dict: ids [..., k] int32,
+    probs [..., k] float32, count [...] int32, flags [...] int32 (the uint32 bits)."""
+    dev = logits.device
+    V = logits.shape[-1]
+    lead = tuple(logits.shape[:-1])
+    if logits.dim() == 2 and logits.stride(-1) == 1:
+        rows = logits.shape[0]
+        ld = logits.stride(0) if rows > 1 else V
+    elif logits.is_contiguous():
+        rows = 1
+        for d in lead:
+            rows *= d
+        ld = V
+    else:
+        raise ValueError("logits must be contiguous, or 2-D with a contiguous vocabulary axis")
+    o = {} if out is None else out
+    spec = {"ids": (lead + (k,), torch.int32), "probs": (lead + (k,), torch.float32), "count": (lead, torch.int32),
+            "flags": (lead, torch.int32)}
+    for n, (shape, dt) in spec.items():
+        if n not in o:
+            o[n] = torch.empty(shape, dtype=dt, device=dev)
+        else:
+            _need(o[n], n, dt, shape, dev)
+    if ws is None:
+        ws = support_workspace(rows, V, k, dev)
+    st = LIB.sv_build_support(_ptr(logits), ld, _dtype_code(logits), rows, V, float(temperature), int(k),
+                              float(top_p), 1 if renorm else 0, _ptr(o["ids"]), _ptr(o["probs"]), _ptr(o["count"]),
+                              _ptr(o["flags"]), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
     if st != SV_OK:
         raise SVError(st)
     return o

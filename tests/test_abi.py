@@ -23,7 +23,8 @@ def declared_functions():
 def test_exports_match_header():
     names = declared_functions()
     assert set(names) == {"sv_workspace_bytes", "sv_status_string", "sv_profile_next_stats", "sv_verify_dense",
-                          "sv_verify_onehot_draft", "sv_verify_sparse"}
+                          "sv_verify_onehot_draft", "sv_verify_sparse", "sv_support_workspace_bytes",
+                          "sv_build_support"}
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (sv_[a-z_]+)\b", out))
     assert set(names) <= exported
@@ -129,6 +130,41 @@ def test_sparse_rejects_bad_arguments(kw, code):
     st = sv.LIB.sv_verify_sparse(a["pi"], a["pp"], a["qi"], a["qp"], a["B"], a["G"], a["kp"], a["kq"], a["vocab"],
                                  a["spec"], a["ua"], a["us"], a["bonus"], a["accept"], a["n"], a["tok"], a["corr"],
                                  a["ps"], a["qs"], a["flags"], None, 0, None)
+    assert st == code
+
+
+def test_support_workspace_sizes():
+    from lossless_draft_verification_spec_amd import sv
+    bad = (1 << 64) - 1
+    for (rows, V, k) in [(1, 1024, 50), (1088, 151936, 50), (17408, 151936, 64), (5, 37, 37), (2, 300000, 256)]:
+        n = sv.sv_support_workspace_bytes(rows, V, k)
+        assert 0 < n < 256 << 20 and n % 256 == 0
+        assert n >= rows * 256                     # one counter line per row
+    assert sv.sv_support_workspace_bytes(0, 100, 5) == bad
+    assert sv.sv_support_workspace_bytes(4, 0, 1) == bad
+    assert sv.sv_support_workspace_bytes(4, 100, 0) == bad
+    assert sv.sv_support_workspace_bytes(4, 100, 101) == bad           # k > V
+    assert sv.sv_support_workspace_bytes(4, 1000, sv.SV_MAX_K + 1) == bad
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(logits=None), -1), (dict(ids=None), -1), (dict(probs=None), -1),
+    (dict(dtype=3), -3),
+    (dict(rows=0), -2), (dict(V=0), -2), (dict(k=0), -2), (dict(k=257, V=1000), -2), (dict(k=129), -2),
+    (dict(ld=127), -2), (dict(V=1 << 31, ld=1 << 31), -2),
+    (dict(T=0.0), -4), (dict(T=float("nan")), -4),
+    (dict(top_p=0.0), -8), (dict(top_p=1.5), -8), (dict(top_p=float("nan")), -8), (dict(renorm=2), -8),
+    (dict(logits=A + 2), -5), (dict(logits=A + 1, dtype=1), -5), (dict(ids=A + 2), -5), (dict(count=A + 1), -5),
+    (dict(ws=A + 16), -5), (dict(ws=None), -6), (dict(ws_bytes=16), -6),
+])
+def test_support_rejects_bad_arguments(kw, code):
+    from lossless_draft_verification_spec_amd import sv
+    a = dict(logits=A, ld=128, dtype=0, rows=3, V=128, T=1.0, k=8, top_p=0.9, renorm=1, ids=A, probs=A, count=A,
+             flags=A, ws=A, ws_bytes=1 << 30)
+    a.update(kw)
+    st = sv.LIB.sv_build_support(a["logits"], a["ld"], a["dtype"], a["rows"], a["V"], a["T"], a["k"], a["top_p"],
+                                 a["renorm"], a["ids"], a["probs"], a["count"], a["flags"], a["ws"], a["ws_bytes"],
+                                 None)
     assert st == code
 
 
