@@ -8,8 +8,9 @@ from .verify import (FLAG_EMPTY_RESIDUAL, FLAG_ID_RANGE, FLAG_NONFINITE, FLAG_Q_
                      log_softmax_at, residual, softmax, verify_dense, verify_onehot, verify_sparse, verify_windows,
                      widen)
 from .support import build_support, topk_order
+from .greedy import first_argmax, verify_greedy
 
 __all__ = ["FLAG_EMPTY_RESIDUAL", "FLAG_ID_RANGE", "FLAG_NONFINITE", "FLAG_Q_ZERO", "FATAL", "accept_test",
            "accept_test_exact",
            "inverse_cdf", "log_softmax_at", "residual", "softmax", "verify_dense", "verify_onehot", "verify_sparse",
-           "verify_windows", "widen", "build_support", "topk_order"]
+           "verify_windows", "widen", "build_support", "topk_order", "first_argmax", "verify_greedy"]
