@@ -205,6 +205,45 @@ def bench_support(case, steps, warmup, torch, sv, d, k=50, top_p=0.95):
                 support_hbm_frac=(bytes_t + bytes_d) / ((kt + kd) * 1e-3) / 1e9 / HBM_PEAK_GBPS)
 
 
+GREEDY = "greedy_block_B64_g16_V151936_bf16"
+
+
+def bench_greedy(steps, warmup, torch, sv, d):
+    """Greedy (T = 0) verification of the block workload's shape: B = 64, gamma = 16, V = 151936, bf16 target with
+    the Zipf bias; drafts equal the target argmax with probability 0.85. Every target row (gamma + 1 per sequence)
+    is read once; the kernel is timed from its own dispatches in a second region of the same steps."""
+    from lossless_draft_verification_spec_amd import workloads
+    case = workloads.greedy_case(64, 16, 151936, seed=0)
+    B, G, V = case["B"], case["gamma"], case["V"]
+    ncopies = 3                                                         # 0.99 GB: no reuse in the 256 MB cache
+    tgts = [to_dev_logits(case["target"], "bf16", torch, d) for _ in range(ncopies)]
+    ids = torch.from_numpy(case["draft_ids"]).to(d)
+    ws = sv.workspace(sv.SV_KIND_GREEDY, B, G, V, d)
+    out = {}
+    ev = HipEvents(steps)
+    state = {"timed": False}
+
+    def step(i):
+        if state["timed"]:
+            sv.sv_profile_next_stats(ev.pairs[i][0], ev.pairs[i][1])
+        sv.sv_verify_greedy(tgts[i % ncopies], ids, bonus=1, out=out, ws=ws)
+
+    ms, wall = time_steps(step, steps, warmup, torch)
+    state["timed"] = True
+    time_steps(step, steps, 0, torch)
+    state["timed"] = False
+    km = float(np.mean([ev.elapsed_ms(i) for i in range(steps)]))
+    ev.close()
+    # every target row once, the draft ids, and accept / n / token / flags written
+    nbytes = B * (G + 1) * V * 2 + B * G * 4 + B * G + B * 12
+    n = out["n_accepted"].cpu().numpy()
+    del tgts
+    return dict(ms_per_step=ms, wall_ms_per_step=wall, positions=B * G, positions_per_s=B * G / (ms * 1e-3),
+                mean_n_accepted=float(n.mean()), kernel_ms=km, kernel_bytes=nbytes,
+                kernel_GBps=nbytes / (km * 1e-3) / 1e9, kernel_hbm_frac=nbytes / (km * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                input_copies=ncopies)
+
+
 def bench_sparse(case, steps, warmup, torch, sv, d):
     B, G, k = case["B"], case["gamma"], case["k"]
     t = {key: torch.from_numpy(np.ascontiguousarray(case[key])).to(d)
@@ -348,6 +387,10 @@ def main():
     if args.only in (None, SUPPORT):
         others[SUPPORT] = bench_support(head, args.steps, args.warmup, torch, sv, d)
         log(SUPPORT, json.dumps(others[SUPPORT]))
+        torch.cuda.empty_cache()
+    if args.only in (None, GREEDY):
+        others[GREEDY] = bench_greedy(args.steps, args.warmup, torch, sv, d)
+        log(GREEDY, json.dumps(others[GREEDY]))
         torch.cuda.empty_cache()
     names = [n for n in workloads.WORKLOADS if n != HEADLINE]
     if args.only:

@@ -55,6 +55,7 @@ extern "C" {
 #define SV_KIND_DENSE  0
 #define SV_KIND_ONEHOT 1
 #define SV_KIND_SPARSE 2
+#define SV_KIND_GREEDY 3
 
 /* ---- per-sequence flags ------------------------------------------------------------------------------------- */
 #define SV_FLAG_NONFINITE      1u  /* NaN or +inf logit (or a row all -inf) in a row that was read; for sparse, a
@@ -71,8 +72,8 @@ extern "C" {
 #define SV_MAX_K     256         /* support size of a sparse row (kp, kq)                                          */
 
 /*
- * Bytes of device workspace a call of `kind` needs for B sequences of gamma drafts over V_or_k (V for dense and
- * one-hot, the p-support size kp for sparse). Depends only on these arguments. Returns 0 when no workspace is
+ * Bytes of device workspace a call of `kind` needs for B sequences of gamma drafts over V_or_k (V for dense,
+ * one-hot and greedy, the p-support size kp for sparse). Depends only on these arguments. Returns 0 when no workspace is
  * needed and (size_t)-1 for arguments the calls would reject. The workspace holds the call's work-queue counters
  * and scratch records. It must be zero-filled before its first use (for example allocated with torch.zeros or
  * cleared with hipMemset once); every call leaves its counters at zero again, so the same workspace serves any
@@ -88,7 +89,8 @@ const char* sv_status_string(int status);
 
 /*
  * Profiling hook (no counterpart on the pages; it lets a caller time the verifier's kernel on its own). When both
- * events are non-NULL, the next sv_verify_dense, sv_verify_onehot_draft or sv_build_support call made on this host
+ * events are non-NULL, the next sv_verify_dense, sv_verify_onehot_draft, sv_verify_greedy or sv_build_support call
+ * made on this host
  * thread records `start_event` when its kernel starts and `stop_event` when it ends (from the dispatch itself), on
  * that call's stream, and then forgets them; hipEventElapsedTime(start, stop) is that kernel's duration. The events
  * (hipEvent_t) are created and owned by the caller. Passing two NULLs clears a pending request. Returns SV_OK, or
@@ -210,6 +212,45 @@ size_t sv_support_workspace_bytes(int64_t rows, int64_t V, int32_t k);
 int sv_build_support(const void* logits, int64_t ld, int dtype, int64_t rows, int64_t V,
                      float temperature, int32_t k, float top_p, int32_t renorm,
                      int32_t* ids, float* probs, int32_t* count, uint32_t* flags,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Greedy verification at temperature 0 (DFlash/DFlash2 guide, section 4.4: under greedy decoding a drafted token is
+ * kept exactly when it is the target's most likely token; the block is cut at the first one that is not). The
+ * target's choice at a row is the argmax of its logits, equal maxima going to the lowest id. Slots start[b] ..
+ * gamma-1 are checked in `order`; at the first mismatching slot k the target's argmax there is emitted; when every
+ * checked draft matches and bonus = 1, the argmax of target row gamma is emitted (section 2: up to gamma + 1 tokens
+ * per cycle). No draft logits, uniforms or temperature are involved: every output is an integer decision that the
+ * logits fix exactly.
+ *
+ * target_logits  [B][gamma + bonus][V] of `dtype` at target_logits[b*t_seq + r*t_row + i]; pointer aligned to the
+ *                element size (rows need no further alignment; strides >= 1; V contiguous). Every row of a slot
+ *                >= start is read, and row gamma whenever the sequence is live (bonus = 1), even if unused.
+ * dtype          SV_F32 or SV_BF16.
+ * B, gamma, V    1 <= B <= 2^31-1, 1 <= gamma <= SV_MAX_GAMMA, 1 <= V <= 2^31-1.
+ * draft_ids      [B][gamma] int32, the drafted token of each storage row.
+ * bonus          0 or 1 (with 0 the target needs only gamma rows and out_token is -1 after a full match).
+ * start          [B] int32 or NULL (= all 0), updated to min(gamma, k + 1) as for sv_verify_dense; a sequence with
+ *                start[b] == gamma is finished (nothing read, n = 0, out_token = -1).
+ * order          [B][gamma] int32 or NULL (= identity): slot s checks storage row order[b][s].
+ * accept         [B][gamma] uint8 or NULL: 1 where a checked row's draft equals its argmax (0 for rows before start).
+ * n_accepted     [B] int32 (required): matches from start up to the first mismatch; -1 for a fault.
+ * out_token      [B] int32 (required): the argmax at the first mismatch, the bonus argmax, or -1.
+ * flags          [B] uint32 or NULL: SV_FLAG_ID_RANGE (a draft id outside [0, V) in a checked slot, order not a
+ *                permutation, start outside [0, gamma]) and SV_FLAG_NONFINITE (a NaN or +inf logit, or a row all
+ *                -inf, in a checked row; in row gamma only when the bonus is taken from it). Either one in a
+ *                checked slot makes the sequence fail: n = -1, out_token = -1, accept 0, start unchanged; a bad bonus
+ *                row only sets the flag and leaves out_token = -1.
+ * workspace      >= sv_workspace_bytes(SV_KIND_GREEDY, B, gamma, V) bytes of device memory, 256-byte aligned,
+ *                zero-filled before its first use (same contract as the other calls).
+ * Errors: SV_ERR_NULL, SV_ERR_DTYPE, SV_ERR_SHAPE, SV_ERR_ARG (bonus), SV_ERR_ALIGN, SV_ERR_WORKSPACE, SV_ERR_HIP,
+ * all returned before anything is launched except SV_ERR_HIP.
+ */
+int sv_verify_greedy(const void* target_logits, int64_t t_seq, int64_t t_row,
+                     int dtype, int64_t B, int32_t gamma, int64_t V,
+                     const int32_t* draft_ids, int32_t bonus,
+                     int32_t* start, const int32_t* order,
+                     uint8_t* accept, int32_t* n_accepted, int32_t* out_token, uint32_t* flags,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus

@@ -8,6 +8,7 @@
 #include <limits>
 
 #include "sv.h"
+#include "sv_greedy.h"
 #include "sv_internal.h"
 
 namespace {
@@ -81,6 +82,9 @@ size_t sv_workspace_bytes(int kind, int64_t B, int32_t gamma, int64_t V_or_k) {
     case SV_KIND_SPARSE:
       if (V_or_k > SV_MAX_K) return bad;
       return 0;
+    case SV_KIND_GREEDY:
+      if (V_or_k > kMaxI32) return bad;
+      return sv::greedy_workspace_bytes(B, gamma, V_or_k);
     default:
       return bad;
   }
@@ -216,6 +220,33 @@ int sv_build_support(const void* logits, int64_t ld, int dtype, int64_t rows, in
                     static_cast<char*>(workspace)};
   take_events(a);
   return sv::launch_support(plan, a, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+int sv_verify_greedy(const void* target_logits, int64_t t_seq, int64_t t_row,
+                     int dtype, int64_t B, int32_t gamma, int64_t V,
+                     const int32_t* draft_ids, int32_t bonus,
+                     int32_t* start, const int32_t* order,
+                     uint8_t* accept, int32_t* n_accepted, int32_t* out_token, uint32_t* flags,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!target_logits || !draft_ids || !n_accepted || !out_token) return SV_ERR_NULL;
+  if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
+  if (B < 1 || B > kMaxI32 || gamma < 1 || gamma > SV_MAX_GAMMA || V < 1 || V > kMaxI32) return SV_ERR_SHAPE;
+  if (t_seq < 1 || t_row < 1) return SV_ERR_SHAPE;
+  if (bonus != 0 && bonus != 1) return SV_ERR_ARG;
+  if (double(B - 1) * double(t_seq) + double(gamma + bonus - 1) * double(t_row) + double(V) > 9.0e18)
+    return SV_ERR_SHAPE;
+  if (!aligned(target_logits, dtype == SV_BF16 ? 2 : 4)) return SV_ERR_ALIGN;
+  const void* ptrs[] = {draft_ids, start, order, n_accepted, out_token, flags};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, 4)) return SV_ERR_ALIGN;
+  const sv::GreedyPlan plan = sv::make_greedy_plan(B, gamma, V, bonus, dtype);
+  if (double(plan.items) > double(kMaxI32)) return SV_ERR_SHAPE;
+  const int st = check_workspace(workspace, workspace_bytes, plan.total);
+  if (st != SV_OK) return st;
+  sv::GreedyArgs a{target_logits, t_seq, t_row, dtype, bonus, draft_ids, start, order, accept, n_accepted, out_token,
+                   flags, static_cast<char*>(workspace)};
+  take_events(a);
+  return sv::launch_greedy(plan, a, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
 }  // extern "C"

@@ -16,12 +16,13 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsv.so")
 
 SV_OK = 0
 SV_F32, SV_BF16 = 0, 1
-SV_KIND_DENSE, SV_KIND_ONEHOT, SV_KIND_SPARSE = 0, 1, 2
+SV_KIND_DENSE, SV_KIND_ONEHOT, SV_KIND_SPARSE, SV_KIND_GREEDY = 0, 1, 2, 3
 SV_FLAG_NONFINITE, SV_FLAG_ID_RANGE, SV_FLAG_EMPTY_RESIDUAL, SV_FLAG_Q_ZERO = 1, 2, 4, 8
 SV_MAX_GAMMA, SV_MAX_K = 1024, 256
 
 EXPORTS = ("sv_workspace_bytes", "sv_status_string", "sv_profile_next_stats", "sv_verify_dense",
-           "sv_verify_onehot_draft", "sv_verify_sparse", "sv_support_workspace_bytes", "sv_build_support")
+           "sv_verify_onehot_draft", "sv_verify_sparse", "sv_support_workspace_bytes", "sv_build_support",
+           "sv_verify_greedy")
 
 
 def _load() -> ctypes.CDLL:
@@ -47,6 +48,8 @@ def _load() -> ctypes.CDLL:
     lib.sv_support_workspace_bytes.restype = SZ
     lib.sv_build_support.argtypes = [P, I64, ctypes.c_int, I64, I64, F, I32, F, I32, P, P, P, P, P, SZ, P]
     lib.sv_build_support.restype = ctypes.c_int
+    lib.sv_verify_greedy.argtypes = [P, I64, I64, ctypes.c_int, I64, I32, I64, P, I32, P, P, P, P, P, P, P, SZ, P]
+    lib.sv_verify_greedy.restype = ctypes.c_int
     return lib
 
 
@@ -206,6 +209,32 @@ def sv_verify_onehot_draft(target, draft_ids, u_accept, u_sample, temperature, b
                                     _ptr(order), _ptr(o.get("accept")), _ptr(o["n_accepted"]), _ptr(o["out_token"]),
                                     _ptr(o.get("p_draft")), _ptr(o.get("flags")), _ptr(ws),
                                     0 if ws is None else ws.numel(), _stream(stream))
+    if st != SV_OK:
+        raise SVError(st)
+    return o
+
+
+def sv_verify_greedy(target, draft_ids, bonus=1, start=None, order=None, *, out=None, ws=None, stream=None,
+                     outputs=("accept", "n_accepted", "out_token", "flags")):
+    """Greedy verification at temperature 0 (see ``sv_verify_greedy`` in include/sv.h): a draft is kept when it is
+    the argmax of its target row. target [B, gamma+bonus, V] float32 or bfloat16 (vocabulary axis contiguous);
+    draft_ids int32 [B, gamma]; start int32 [B] (updated in place) or None; order int32 [B, gamma] or None."""
+    B, G = draft_ids.shape
+    dev = target.device
+    V = target.shape[-1]
+    t_seq, t_row = _logits_layout(target, "target", G + bonus, B, dev)
+    _need(draft_ids, "draft_ids", torch.int32, (B, G), dev)
+    if start is not None:
+        _need(start, "start", torch.int32, (B,), dev)
+    if order is not None:
+        _need(order, "order", torch.int32, (B, G), dev)
+    o = _outputs(B, G, dev, out, outputs)
+    if ws is None:
+        ws = workspace(SV_KIND_GREEDY, B, G, V, dev)
+    st = LIB.sv_verify_greedy(_ptr(target), t_seq, t_row, _dtype_code(target), B, G, V, _ptr(draft_ids), int(bonus),
+                              _ptr(start), _ptr(order), _ptr(o.get("accept")), _ptr(o["n_accepted"]),
+                              _ptr(o["out_token"]), _ptr(o.get("flags")), _ptr(ws), 0 if ws is None else ws.numel(),
+                              _stream(stream))
     if st != SV_OK:
         raise SVError(st)
     return o

@@ -189,6 +189,26 @@ def onehot_case(B: int, gamma: int, V: int, *, dtype: str = DTYPE_BF16, sigma_t:
                 u_accept=uniforms(r_a, (B, gamma)), u_sample=uniforms(r_s, (B, gamma + 1)))
 
 
+def greedy_case(B: int, gamma: int, V: int, *, dtype: str = DTYPE_BF16, sigma_t: float = 3.0, zipf: float = 1.1,
+                agree: float = 0.85, sigma_x: float = 1.5, bonus: int = 1, seed: int = 0) -> dict:
+    """Greedy verification inputs: the target of ``dense_case`` (N(0, sigma_t^2) plus the Zipf bias); each draft id
+    is, with probability ``agree``, the largest target logit of its row (lowest index on ties), and otherwise the
+    largest of target + N(0, sigma_x^2). No draft logits, uniforms or temperature."""
+    r_t, r_n, r_a = _streams(seed, 3)
+    zt = _normal_f32(r_t, (B, gamma + bonus, V), sigma_t)
+    if zipf:
+        zt += (-zipf * np.log1p(np.arange(V, dtype=np.float64))).astype(np.float32)
+    zt_store = f32_to_bf16_bits(zt) if dtype == DTYPE_BF16 else zt
+    zt_eff = bf16_bits_to_f32(zt_store) if dtype == DTYPE_BF16 else zt
+    noisy = _normal_f32(r_n, (B, gamma, V), sigma_x)
+    keep = uniforms(r_a, (B, gamma)) < agree
+    noisy[keep] = 0.0
+    noisy += zt_eff[:, :gamma]
+    ids = np.argmax(noisy, axis=-1).astype(np.int32)
+    del noisy
+    return dict(kind="greedy", dtype=dtype, B=B, gamma=gamma, V=V, bonus=bonus, target=zt_store, draft_ids=ids)
+
+
 # ----------------------------------------------------------------------------------------------------------------------
 # Sparse (top-k support) inputs
 # ----------------------------------------------------------------------------------------------------------------------
