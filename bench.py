@@ -238,10 +238,12 @@ def bench_greedy(steps, warmup, torch, sv, d):
     nbytes = B * (G + 1) * V * 2 + B * G * 4 + B * G + B * 12
     n = out["n_accepted"].cpu().numpy()
     del tgts
+    gbps = nbytes / (km * 1e-3) / 1e9
     return dict(ms_per_step=ms, wall_ms_per_step=wall, positions=B * G, positions_per_s=B * G / (ms * 1e-3),
-                mean_n_accepted=float(n.mean()), kernel_ms=km, kernel_bytes=nbytes,
-                kernel_GBps=nbytes / (km * 1e-3) / 1e9, kernel_hbm_frac=nbytes / (km * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                input_copies=ncopies)
+                mean_n_accepted=float(n.mean()), kernel_ms=km, kernel_bytes=nbytes, kernel_GBps=gbps,
+                kernel_hbm_frac=gbps / HBM_PEAK_GBPS, input_copies=ncopies,
+                roofline={"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                          "frac": gbps / HBM_PEAK_GBPS, "traffic": greedy_traffic(), "kernel": "k_greedy"})
 
 
 def bench_sparse(case, steps, warmup, torch, sv, d):
@@ -328,6 +330,30 @@ def kernel_source_sha():
         with open(os.path.join(ROOT, "lossless_draft_verification_spec_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+GREEDY_SOURCES = ("sv_greedy.hip", "sv_greedy.h", "sv_device.h", "sv_internal.h")   # what k_greedy is built from
+
+
+def greedy_traffic():
+    """HBM bytes per launch of k_greedy on the greedy block workload from the committed counter summary, or None when
+    its sources have changed since the counters were taken."""
+    import hashlib
+    h = hashlib.sha256()
+    try:
+        for name in GREEDY_SOURCES:
+            with open(os.path.join(ROOT, "lossless_draft_verification_spec_amd", "csrc", name), "rb") as f:
+                h.update(f.read())
+        rec = None
+        with open(os.path.join(ROOT, "profiles", "k_greedy_block_traffic.txt")) as f:
+            for ln in f:
+                if ln.startswith("TRAFFIC_JSON "):
+                    rec = json.loads(ln[len("TRAFFIC_JSON "):])
+    except OSError:
+        return None
+    if rec is None or rec.get("source_sha256") != h.hexdigest():
+        return None
+    return int(rec["target"]["traffic_bytes"])
 
 
 def measured_traffic():
