@@ -246,6 +246,49 @@ def bench_greedy(steps, warmup, torch, sv, d):
                           "frac": gbps / HBM_PEAK_GBPS, "traffic": greedy_traffic(), "kernel": "k_greedy"})
 
 
+COMMIT = "commit_block_B256_W4_V151936_bf16"
+
+
+def bench_commit(steps, warmup, torch, sv, d):
+    """Confidence-threshold commit of masked-diffusion blocks: B = 256 blocks of W = 4 slots over V = 151936, bf16,
+    three quarters of the slots still masked, tau = 0.9. Only masked slots are read; the kernel is timed from its own
+    dispatches in a second region of the same steps."""
+    from lossless_draft_verification_spec_amd import workloads
+    case = workloads.commit_case(256, 4, 151936, seed=0)
+    B, Wn, V = case["B"], case["W"], case["V"]
+    ncopies = 4                                                         # 1.24 GB: no reuse in the 256 MB cache
+    zs = [to_dev_logits(case["logits"], "bf16", torch, d) for _ in range(ncopies)]
+    masked = torch.from_numpy(case["masked"]).to(d)
+    ws = sv.workspace(sv.SV_KIND_GREEDY, B, Wn, V, d)
+    out = {}
+    ev = HipEvents(steps)
+    state = {"timed": False}
+
+    def step(i):
+        if state["timed"]:
+            sv.sv_profile_next_stats(ev.pairs[i][0], ev.pairs[i][1])
+        sv.sv_confidence_commit(zs[i % ncopies], case["tau"], masked, out=out, ws=ws)
+
+    ms, wall = time_steps(step, steps, warmup, torch)
+    state["timed"] = True
+    time_steps(step, steps, 0, torch)
+    state["timed"] = False
+    km = float(np.mean([ev.elapsed_ms(i) for i in range(steps)]))
+    ev.close()
+    nm = int(case["masked"].sum())
+    # every masked row once, the mask, and commit / token / confidence per slot and the count and flags per block
+    nbytes = nm * V * 2 + B * Wn + B * Wn * 9 + B * 8
+    gbps = nbytes / (km * 1e-3) / 1e9
+    del zs
+    return dict(ms_per_step=ms, wall_ms_per_step=wall, slots=B * Wn, masked_slots=nm,
+                committed=int(out["n_commit"].sum().item()), kernel_ms=km, kernel_bytes=nbytes, kernel_GBps=gbps,
+                kernel_hbm_frac=gbps / HBM_PEAK_GBPS,
+                roofline={"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                          "frac": gbps / HBM_PEAK_GBPS,
+                          "traffic": greedy_traffic("k_greedy_commit_block_traffic.txt", "masked"),
+                          "kernel": "k_greedy (commit mode)"})
+
+
 def bench_sparse(case, steps, warmup, torch, sv, d):
     B, G, k = case["B"], case["gamma"], case["k"]
     t = {key: torch.from_numpy(np.ascontiguousarray(case[key])).to(d)
@@ -335,9 +378,9 @@ def kernel_source_sha():
 GREEDY_SOURCES = ("sv_greedy.hip", "sv_greedy.h", "sv_device.h", "sv_internal.h")   # what k_greedy is built from
 
 
-def greedy_traffic():
-    """HBM bytes per launch of k_greedy on the greedy block workload from the committed counter summary, or None when
-    its sources have changed since the counters were taken."""
+def greedy_traffic(profile="k_greedy_block_traffic.txt", key="target"):
+    """HBM bytes per launch of k_greedy (greedy verification, or commit mode with the commit profile) from the
+    committed counter summary, or None when its sources have changed since the counters were taken."""
     import hashlib
     h = hashlib.sha256()
     try:
@@ -345,7 +388,7 @@ def greedy_traffic():
             with open(os.path.join(ROOT, "lossless_draft_verification_spec_amd", "csrc", name), "rb") as f:
                 h.update(f.read())
         rec = None
-        with open(os.path.join(ROOT, "profiles", "k_greedy_block_traffic.txt")) as f:
+        with open(os.path.join(ROOT, "profiles", profile)) as f:
             for ln in f:
                 if ln.startswith("TRAFFIC_JSON "):
                     rec = json.loads(ln[len("TRAFFIC_JSON "):])
@@ -353,7 +396,7 @@ def greedy_traffic():
         return None
     if rec is None or rec.get("source_sha256") != h.hexdigest():
         return None
-    return int(rec["target"]["traffic_bytes"])
+    return int(rec[key]["traffic_bytes"])
 
 
 def measured_traffic():
@@ -417,6 +460,10 @@ def main():
     if args.only in (None, GREEDY):
         others[GREEDY] = bench_greedy(args.steps, args.warmup, torch, sv, d)
         log(GREEDY, json.dumps(others[GREEDY]))
+        torch.cuda.empty_cache()
+    if args.only in (None, COMMIT):
+        others[COMMIT] = bench_commit(args.steps, args.warmup, torch, sv, d)
+        log(COMMIT, json.dumps(others[COMMIT]))
         torch.cuda.empty_cache()
     names = [n for n in workloads.WORKLOADS if n != HEADLINE]
     if args.only:

@@ -89,8 +89,8 @@ const char* sv_status_string(int status);
 
 /*
  * Profiling hook (no counterpart on the pages; it lets a caller time the verifier's kernel on its own). When both
- * events are non-NULL, the next sv_verify_dense, sv_verify_onehot_draft, sv_verify_greedy or sv_build_support call
- * made on this host
+ * events are non-NULL, the next sv_verify_dense, sv_verify_onehot_draft, sv_verify_greedy, sv_confidence_commit or
+ * sv_build_support call made on this host
  * thread records `start_event` when its kernel starts and `stop_event` when it ends (from the dispatch itself), on
  * that call's stream, and then forgets them; hipEventElapsedTime(start, stop) is that kernel's duration. The events
  * (hipEvent_t) are created and owned by the caller. Passing two NULLs clears a pending request. Returns SV_OK, or
@@ -252,6 +252,35 @@ int sv_verify_greedy(const void* target_logits, int64_t t_seq, int64_t t_row,
                      int32_t* start, const int32_t* order,
                      uint8_t* accept, int32_t* n_accepted, int32_t* out_token, uint32_t* flags,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Confidence-threshold commit of block diffusion (SDAR-style block diffusion page, section 5 "Decoding timeline":
+ * each pass gives a distribution over the vocabulary at every masked slot of the block; slots whose confidence
+ * reaches tau are committed, at least the most confident one, so every pass makes progress). This is the decoding
+ * rule of a masked-diffusion pass, not a verifier: it is lossy by design.
+ * Per masked slot j of block b: token = argmax of the logits (equal maxima to the lowest id) and confidence = its
+ * softmax probability 1 / sum_i exp(z_i - max) (temperature 1), merged in float64. Committed: the masked slots with
+ * confidence >= tau; if there are none, the single most confident masked slot (equal confidences: the lowest j).
+ *
+ * logits      [B][W][V] of `dtype` at logits[b*l_seq + j*l_row + i]; pointer aligned to the element size, rows need
+ *             no further alignment; only masked slots are read.
+ * B, W, V     1 <= B <= 2^31-1, 1 <= W <= SV_MAX_GAMMA, 1 <= V <= 2^31-1.
+ * masked      [B][W] uint8 or NULL (= every slot masked): nonzero = the slot is still masked.
+ * tau         in [0, 1] (float; compared with the float64 confidence), else SV_ERR_ARG.
+ * commit      [B][W] uint8 or NULL: 1 for a committed slot.
+ * token       [B][W] int32 (required): the committed token, -1 elsewhere.
+ * confidence  [B][W] float or NULL: the confidence of each masked slot (rounded to float), NaN elsewhere.
+ * n_commit    [B] int32 (required): committed slots (0 when none is masked), -1 for a fault.
+ * flags       [B] uint32 or NULL: SV_FLAG_NONFINITE for a NaN or +inf logit, or a row all -inf, in a masked slot;
+ *             such a block commits nothing (token -1, confidence NaN).
+ * workspace   >= sv_workspace_bytes(SV_KIND_GREEDY, B, W, V) bytes, 256-byte aligned, zero-filled before its first
+ *             use (same contract as the other calls; it may alternate with sv_verify_greedy and the others).
+ * Errors: SV_ERR_NULL, SV_ERR_DTYPE, SV_ERR_SHAPE, SV_ERR_ARG, SV_ERR_ALIGN, SV_ERR_WORKSPACE, SV_ERR_HIP.
+ */
+int sv_confidence_commit(const void* logits, int64_t l_seq, int64_t l_row, int dtype, int64_t B, int32_t W,
+                         int64_t V, const uint8_t* masked, float tau, uint8_t* commit, int32_t* token,
+                         float* confidence, int32_t* n_commit, uint32_t* flags,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -6,7 +6,8 @@ input generators work without the built library; using a verifier entry point wi
 """
 _BINDING = ("sv_verify_dense", "sv_verify_onehot_draft", "sv_verify_sparse", "sv_workspace_bytes",
             "sv_status_string", "SVError", "workspace", "sv_build_support", "sv_support_workspace_bytes",
-            "support_workspace", "sv_verify_greedy")
+            "support_workspace", "sv_verify_greedy",
+            "sv_confidence_commit")
 
 
 def __getattr__(name):

@@ -249,4 +249,33 @@ int sv_verify_greedy(const void* target_logits, int64_t t_seq, int64_t t_row,
   return sv::launch_greedy(plan, a, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
+int sv_confidence_commit(const void* logits, int64_t l_seq, int64_t l_row, int dtype, int64_t B, int32_t W,
+                         int64_t V, const uint8_t* masked, float tau, uint8_t* commit, int32_t* token,
+                         float* confidence, int32_t* n_commit, uint32_t* flags,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (!logits || !token || !n_commit) return SV_ERR_NULL;
+  if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
+  if (B < 1 || B > kMaxI32 || W < 1 || W > SV_MAX_GAMMA || V < 1 || V > kMaxI32) return SV_ERR_SHAPE;
+  if (l_seq < 1 || l_row < 1) return SV_ERR_SHAPE;
+  if (double(B - 1) * double(l_seq) + double(W - 1) * double(l_row) + double(V) > 9.0e18) return SV_ERR_SHAPE;
+  if (!(tau >= 0.f && tau <= 1.f)) return SV_ERR_ARG;
+  if (!aligned(logits, dtype == SV_BF16 ? 2 : 4)) return SV_ERR_ALIGN;
+  const void* ptrs[] = {token, confidence, n_commit, flags};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, 4)) return SV_ERR_ALIGN;
+  const sv::GreedyPlan plan = sv::make_greedy_plan(B, W, V, 0, dtype);
+  if (double(plan.items) > double(kMaxI32)) return SV_ERR_SHAPE;
+  const int st = check_workspace(workspace, workspace_bytes, plan.total);
+  if (st != SV_OK) return st;
+  sv::GreedyArgs a{logits, l_seq, l_row, dtype, 0, nullptr, nullptr, nullptr, nullptr, n_commit, token, flags,
+                   static_cast<char*>(workspace)};
+  a.conf_mode = true;
+  a.masked = masked;
+  a.tau = tau;
+  a.commit = commit;
+  a.conf = confidence;
+  take_events(a);
+  return sv::launch_greedy(plan, a, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
 }  // extern "C"

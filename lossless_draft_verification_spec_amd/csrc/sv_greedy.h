@@ -28,6 +28,7 @@ struct GreedyPlan {
   int64_t items = 0;       // workgroups of the launch: B * R * S
   size_t ctr_bytes = 0;    // the control region [0, ctr_bytes): int32 per sequence, returned to 0 by its merge
   size_t off_part = 0;     // uint64 key per (sequence, row, segment)
+  size_t off_part2 = 0;    // float2 (segment maximum, sum of exp(z - maximum)) per (sequence, row, segment)
   size_t total = 0;
 };
 
@@ -42,6 +43,9 @@ struct GreedyArgs {
   int32_t* start; const int32_t* order;
   uint8_t* accept; int32_t* n_acc; int32_t* token; uint32_t* flags;
   char* ws;
+  // confidence-threshold commit: gamma = W slots, bonus 0, n_acc = committed count, token [B][W]
+  bool conf_mode = false;
+  const uint8_t* masked = nullptr; float tau = 0.f; uint8_t* commit = nullptr; float* conf = nullptr;
   void* ev_start = nullptr;   // optional hipEvent_t pair recorded from the kernel's dispatch
   void* ev_stop = nullptr;
 };

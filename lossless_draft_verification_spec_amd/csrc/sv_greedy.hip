@@ -47,6 +47,7 @@ constexpr int kGrU = SV_GR_U;                               // 16-byte vectors p
 constexpr int64_t kGrChunkVec = int64_t(kGrBlock) * kGrU;   // vectors per chunk (16 KB)
 constexpr uint64_t kFaultKey = ~0ull;                       // a segment holding a NaN or +inf
 constexpr uint32_t kOrdNegInf = 0x007FFFFFu;                // ord_bits(-inf)
+constexpr float kLog2e = 1.4426950408889634f;
 
 struct GreedyParams {
   const void* tgt;
@@ -64,6 +65,12 @@ struct GreedyParams {
   uint32_t* flags;
   int32_t* ctr;                // per sequence: workgroups finished
   uint64_t* part;              // per (sequence, row, segment): the segment's key
+  // confidence-threshold commit (CONF kernels): W = G slots, no bonus row
+  const uint8_t* masked;       // [B][W] or null (all masked)
+  double tau;
+  uint8_t* commit;             // [B][W] or null
+  float* conf;                 // [B][W] or null
+  float2* part2;               // per (sequence, row, segment): (segment maximum, sum of exp(z - maximum))
 };
 
 struct GrShared {
@@ -73,8 +80,13 @@ struct GrShared {
   int32_t last;                // this workgroup merges the sequence
   int32_t kmin;                // first mismatching slot
   uint32_t fl;                 // the sequence's flags
+  float wsum[kGrWaves];
   uint32_t seen[SV_MAX_GAMMA / 32];
   uint64_t rowkey[SV_MAX_GAMMA + 1];
+  double rowconf[SV_MAX_GAMMA];   // CONF merge: the slot's confidence
+  uint64_t best;                  // CONF merge: the largest confidence (its bits)
+  int32_t bestj;
+  int32_t any;
 };
 
 // Order-preserving code of a float's bits (larger float, larger code), -0 taken as +0 so that equal values tie.
@@ -108,9 +120,9 @@ __device__ __forceinline__ void load_chunk(uint4 (&w)[kGrU], const uint4* vp, in
 // Folds one chunk into the thread's running (maximum m, lowest index mi holding it). The chunk maximum is
 // NaN-propagating, so a NaN or +inf sets `bad`; only a chunk whose maximum beats m is searched for its first
 // element equal to that maximum (elements are visited last to first, so the final match is the lowest index).
-template <typename T>
+template <typename T, bool CONF>
 __device__ __forceinline__ void fold_chunk(const uint4 (&w)[kGrU], int c, int64_t nv, int t, int64_t elem0, float& m,
-                                          int64_t& mi, bool& bad) {
+                                          int64_t& mi, bool& bad, float& sum) {
   constexpr int E = Vec<T>::kEPV;
   const int64_t base = int64_t(c) * kGrChunkVec + t;
   const bool full = int64_t(c + 1) * kGrChunkVec <= nv;
@@ -141,8 +153,19 @@ __device__ __forceinline__ void fold_chunk(const uint4 (&w)[kGrU], int c, int64_
 #pragma unroll
       for (int e = E - 1; e >= 0; --e)
         if (v[u][e] == cm) pos = u * kGrBlock * E + e;
+    if constexpr (CONF) sum *= ex2f((m - cm) * kLog2e);   // m = -inf the first time: the empty sum stays 0
     m = cm;
     mi = elem0 + pos;
+  }
+  if constexpr (CONF) {                    // sum of exp(z - m) with m the running maximum (masked-off lanes: -inf)
+    if (m > -INFINITY) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int u = 0; u < kGrU; ++u)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc += ex2f((v[u][e] - m) * kLog2e);
+      sum += acc;
+    }
   }
 }
 
@@ -174,9 +197,10 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
   return best;
 }
 
-// The key of logits [e0, e1) of one row (see the file comment). Every thread of the workgroup calls it.
-template <typename T>
-__device__ uint64_t segment_key(const T* row, int64_t e0, int64_t e1, GrShared& sh) {
+// The key of logits [e0, e1) of one row (see the file comment). Every thread of the workgroup calls it. CONF: also
+// the segment's sum of exp(z - M), M its maximum, in `ssum`.
+template <typename T, bool CONF>
+__device__ uint64_t segment_key(const T* row, int64_t e0, int64_t e1, GrShared& sh, float& ssum) {
   constexpr int E = Vec<T>::kEPV;
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63;
@@ -205,12 +229,14 @@ __device__ uint64_t segment_key(const T* row, int64_t e0, int64_t e1, GrShared& 
   float m = -INFINITY;
   int64_t mi = -1;
   bool bad = false;
+  float sum = 0.0f;
   uint4 nxt[kGrU];
   for (int c = 0; c < nch; c += 2) {
     load_chunk(nxt, vp, c + 1, nv, t);
-    fold_chunk<T>(cur, c, nv, t, v0 + (int64_t(c) * kGrChunkVec + t) * E, m, mi, bad);
+    fold_chunk<T, CONF>(cur, c, nv, t, v0 + (int64_t(c) * kGrChunkVec + t) * E, m, mi, bad, sum);
     load_chunk(cur, vp, c + 2, nv, t);
-    if (c + 1 < nch) fold_chunk<T>(nxt, c + 1, nv, t, v0 + (int64_t(c + 1) * kGrChunkVec + t) * E, m, mi, bad);
+    if (c + 1 < nch)
+      fold_chunk<T, CONF>(nxt, c + 1, nv, t, v0 + (int64_t(c + 1) * kGrChunkVec + t) * E, m, mi, bad, sum);
   }
 
   // Workgroup maximum key and fault test.
@@ -233,7 +259,23 @@ __device__ uint64_t segment_key(const T* row, int64_t e0, int64_t e1, GrShared& 
     best = sh.wkey[w] > best ? sh.wkey[w] : best;
     anyf |= sh.wfault[w];
   }
-  return anyf ? kFaultKey : best;
+  if (anyf) return kFaultKey;
+  if constexpr (CONF) {
+    // the workgroup's sum, every thread's sum rescaled to the segment maximum (taken from the key)
+    const uint32_t hb = uint32_t(best >> 32);
+    const float M = __uint_as_float((hb & 0x80000000u) ? (hb & 0x7FFFFFFFu) : ~hb);
+    float mine = sum > 0.0f ? sum * ex2f((m - M) * kLog2e) : 0.0f;
+    if (has_s && sval > -INFINITY) mine += ex2f((sval - M) * kLog2e);
+    const float ws = float(wave_sum(double(mine)));
+    __syncthreads();
+    if (lane == 0) sh.wsum[wave] = ws;
+    __syncthreads();
+    float tot = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kGrWaves; ++w) tot += sh.wsum[w];
+    ssum = tot;
+  }
+  return best;
 }
 
 __device__ __forceinline__ bool key_fault(uint64_t k) { return k == kFaultKey || uint32_t(k >> 32) == kOrdNegInf; }
@@ -313,7 +355,81 @@ __device__ void resolve(const GreedyParams& p, int64_t b, int32_t st, GrShared& 
   }
 }
 
-template <typename T>
+// Confidence-threshold commit, the last workgroup of a block: per masked slot the merged argmax and confidence
+// 1 / sum exp(z - max) (float64 merge of the segment sums), then commit the slots at or above tau, or else the single
+// most confident one (lowest slot on ties).
+__device__ void resolve_conf(const GreedyParams& p, int64_t b, GrShared& sh) {
+  const int t = threadIdx.x;
+  const int W = p.G, S = p.S;
+  for (int i = t; i < W; i += kGrBlock) sh.rowkey[i] = 0;
+  if (t == 0) {
+    sh.fl = 0;
+    sh.best = 0;
+    sh.bestj = W;
+    sh.any = 0;
+  }
+  __syncthreads();
+  const uint64_t* part = p.part + b * W * S;
+  const float2* part2 = p.part2 + b * W * S;
+  const uint8_t* msk = p.masked ? p.masked + b * W : nullptr;
+  for (int i = t; i < W * S; i += kGrBlock)
+    if (!msk || msk[i / S]) atomicMax(reinterpret_cast<unsigned long long*>(&sh.rowkey[i / S]),
+                                      static_cast<unsigned long long>(ld_dev(part + i)));
+  __syncthreads();
+  for (int j = t; j < W; j += kGrBlock) {
+    double c = -1.0;
+    if (!msk || msk[j]) {
+      const uint64_t k = sh.rowkey[j];
+      if (key_fault(k)) {
+        atomicOr(&sh.fl, SV_FLAG_NONFINITE);
+      } else {
+        const uint32_t hb = uint32_t(k >> 32);
+        const double M = double(__uint_as_float((hb & 0x80000000u) ? (hb & 0x7FFFFFFFu) : ~hb));
+        double acc = 0.0;
+        for (int s = 0; s < S; ++s) {
+          const float2 q = make_float2(ld_dev(&part2[j * S + s].x), ld_dev(&part2[j * S + s].y));
+          if (q.y > 0.0f) acc += double(q.y) * exp(double(q.x) - M);
+        }
+        c = 1.0 / acc;
+        if (c >= p.tau) atomicOr(&sh.any, 1);
+        atomicMax(reinterpret_cast<unsigned long long*>(&sh.best), static_cast<unsigned long long>(__double_as_longlong(c)));
+      }
+    }
+    sh.rowconf[j] = c;
+  }
+  __syncthreads();
+  const bool fatal = sh.fl != 0;
+  const bool any = sh.any != 0;
+  const double best = __longlong_as_double(static_cast<long long>(sh.best));
+  if (!fatal && !any)
+    for (int j = t; j < W; j += kGrBlock)
+      if (sh.rowconf[j] >= 0.0 && sh.rowconf[j] == best) atomicMin(&sh.bestj, j);
+  __syncthreads();
+  int cnt = 0;
+  for (int j = t; j < W; j += kGrBlock) {
+    const double c = sh.rowconf[j];
+    const bool read = c >= 0.0;
+    const bool take = !fatal && read && (any ? c >= p.tau : j == sh.bestj);
+    cnt += take;
+    if (p.commit) p.commit[b * W + j] = take;
+    p.token[b * W + j] = take ? key_index(sh.rowkey[j]) : -1;
+    if (p.conf) p.conf[b * W + j] = read && !fatal ? float(c) : NAN;
+  }
+  // block count of commits
+  const int wc = int(wave_sum(double(cnt)));
+  __syncthreads();
+  if ((t & 63) == 0) sh.wsum[t >> 6] = float(wc);
+  __syncthreads();
+  if (t == 0) {
+    int n = 0;
+    for (int w = 0; w < kGrWaves; ++w) n += int(sh.wsum[w]);
+    p.n_acc[b] = fatal ? -1 : n;
+    if (p.flags) p.flags[b] = sh.fl;
+    st_dev(p.ctr + b, int32_t(0));          // ready for the next call
+  }
+}
+
+template <typename T, bool CONF>
 __global__ __launch_bounds__(kGrBlock) void k_greedy(GreedyParams p) {
   __shared__ GrShared sh;
   const int t = threadIdx.x;
@@ -323,11 +439,13 @@ __global__ __launch_bounds__(kGrBlock) void k_greedy(GreedyParams p) {
   const int r = int(br % p.R);
   const int64_t b = br / p.R;
   const int G = p.G;
-  const int32_t st = p.start ? p.start[b] : 0;
+  const int32_t st = (!CONF && p.start) ? p.start[b] : 0;
 
-  // Is this row verified (or the bonus row of a live sequence)?
+  // Is this row verified (or the bonus row of a live sequence; CONF: a masked slot)?
   bool read;
-  if (st < 0 || st >= G) {
+  if constexpr (CONF) {
+    read = !p.masked || p.masked[b * G + r] != 0;
+  } else if (st < 0 || st >= G) {
     read = false;
   } else if (r == G || st == 0) {
     read = true;
@@ -343,23 +461,35 @@ __global__ __launch_bounds__(kGrBlock) void k_greedy(GreedyParams p) {
   }
 
   uint64_t key = 0;
+  float ssum = 0.0f, smax = -INFINITY;
   if (read) {
     const T* row = static_cast<const T*>(p.tgt) + b * p.t_seq + int64_t(r) * p.t_row;
     const int64_t e0 = int64_t(s) * p.seg_elems;
     const int64_t e1 = min(p.V, e0 + p.seg_elems);
-    key = segment_key<T>(row, e0, e1, sh);
+    key = segment_key<T, CONF>(row, e0, e1, sh, ssum);
+    if (CONF && key != kFaultKey) {
+      const uint32_t hb = uint32_t(key >> 32);
+      smax = __uint_as_float((hb & 0x80000000u) ? (hb & 0x7FFFFFFFu) : ~hb);
+    }
   }
   // The key is a device-scope store, complete (waitcnt) before the counter counts it; the merging workgroup reads
   // the keys with device-scope loads issued after it has seen the count. No release or acquire fence: at agent
   // scope those write back and invalidate the whole L2, which would cost far more than the pass itself.
   if (t == 0) {
-    if (read) st_dev(p.part + item, key);
+    if (read) {
+      st_dev(p.part + item, key);
+      if (CONF) {
+        st_dev(&p.part2[item].x, smax);
+        st_dev(&p.part2[item].y, ssum);
+      }
+    }
     __builtin_amdgcn_s_waitcnt(0);
     sh.last = ctr_add(p.ctr + b) == p.R * p.S - 1;
   }
   __syncthreads();
   if (!sh.last) return;
-  resolve(p, b, st, sh);
+  if constexpr (CONF) resolve_conf(p, b, sh);
+  else resolve(p, b, st, sh);
 }
 
 }  // namespace
@@ -379,7 +509,8 @@ GreedyPlan make_greedy_plan(int64_t B, int32_t G, int64_t V, int32_t bonus, int 
   pl.items = rows * pl.S;
   pl.ctr_bytes = size_t((B * 4 + 255) / 256 * 256);
   pl.off_part = pl.ctr_bytes;
-  pl.total = pl.off_part + size_t(pl.items) * 8;
+  pl.off_part2 = pl.off_part + size_t(pl.items) * 8;
+  pl.total = pl.off_part2 + size_t(pl.items) * 8;
   return pl;
 }
 
@@ -401,9 +532,12 @@ hipError_t launch_greedy(const GreedyPlan& plan, const GreedyArgs& a, hipStream_
   p.G = plan.G; p.R = plan.R; p.S = plan.S; p.bonus = a.bonus;
   p.ids = a.ids; p.start = a.start; p.order = a.order;
   p.accept = a.accept; p.n_acc = a.n_acc; p.token = a.token; p.flags = a.flags;
+  p.masked = a.masked; p.tau = double(a.tau); p.commit = a.commit; p.conf = a.conf;
   p.ctr = reinterpret_cast<int32_t*>(a.ws);
   p.part = reinterpret_cast<uint64_t*>(a.ws + plan.off_part);
-  auto kern = a.dtype == SV_BF16 ? k_greedy<uint16_t> : k_greedy<float>;
+  p.part2 = reinterpret_cast<float2*>(a.ws + plan.off_part2);
+  auto kern = a.conf_mode ? (a.dtype == SV_BF16 ? k_greedy<uint16_t, true> : k_greedy<float, true>)
+                          : (a.dtype == SV_BF16 ? k_greedy<uint16_t, false> : k_greedy<float, false>);
   const unsigned grid = unsigned(plan.items);
   if (a.ev_start) {
     hipExtLaunchKernelGGL(kern, dim3(grid), dim3(kGrBlock), 0, stream, static_cast<hipEvent_t>(a.ev_start),

@@ -22,7 +22,7 @@ SV_MAX_GAMMA, SV_MAX_K = 1024, 256
 
 EXPORTS = ("sv_workspace_bytes", "sv_status_string", "sv_profile_next_stats", "sv_verify_dense",
            "sv_verify_onehot_draft", "sv_verify_sparse", "sv_support_workspace_bytes", "sv_build_support",
-           "sv_verify_greedy")
+           "sv_verify_greedy", "sv_confidence_commit")
 
 
 def _load() -> ctypes.CDLL:
@@ -50,6 +50,8 @@ def _load() -> ctypes.CDLL:
     lib.sv_build_support.restype = ctypes.c_int
     lib.sv_verify_greedy.argtypes = [P, I64, I64, ctypes.c_int, I64, I32, I64, P, I32, P, P, P, P, P, P, P, SZ, P]
     lib.sv_verify_greedy.restype = ctypes.c_int
+    lib.sv_confidence_commit.argtypes = [P, I64, I64, ctypes.c_int, I64, I32, I64, P, F, P, P, P, P, P, P, SZ, P]
+    lib.sv_confidence_commit.restype = ctypes.c_int
     return lib
 
 
@@ -235,6 +237,31 @@ def sv_verify_greedy(target, draft_ids, bonus=1, start=None, order=None, *, out=
                               _ptr(start), _ptr(order), _ptr(o.get("accept")), _ptr(o["n_accepted"]),
                               _ptr(o["out_token"]), _ptr(o.get("flags")), _ptr(ws), 0 if ws is None else ws.numel(),
                               _stream(stream))
+    if st != SV_OK:
+        raise SVError(st)
+    return o
+
+
+def sv_confidence_commit(logits, tau, masked=None, *, out=None, ws=None, stream=None):
+    """Confidence-threshold commit (see ``sv_confidence_commit`` in include/sv.h). logits [B, W, V] float32 or
+    bfloat16 (vocabulary axis contiguous); masked uint8 [B, W] or None. Returns commit, token, confidence, n_commit,
+    flags."""
+    B, W, V = logits.shape
+    dev = logits.device
+    l_seq, l_row = _logits_layout(logits, "logits", W, B, dev)
+    if masked is not None:
+        _need(masked, "masked", torch.uint8, (B, W), dev)
+    o = {} if out is None else out
+    for name, shape, dt in (("commit", (B, W), torch.uint8), ("token", (B, W), torch.int32),
+                            ("confidence", (B, W), torch.float32), ("n_commit", (B,), torch.int32),
+                            ("flags", (B,), torch.int32)):
+        if name not in o:
+            o[name] = torch.empty(shape, dtype=dt, device=dev)
+    if ws is None:
+        ws = workspace(SV_KIND_GREEDY, B, W, V, dev)
+    st = LIB.sv_confidence_commit(_ptr(logits), l_seq, l_row, _dtype_code(logits), B, W, V, _ptr(masked), float(tau),
+                                  _ptr(o["commit"]), _ptr(o["token"]), _ptr(o["confidence"]), _ptr(o["n_commit"]),
+                                  _ptr(o["flags"]), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
     if st != SV_OK:
         raise SVError(st)
     return o

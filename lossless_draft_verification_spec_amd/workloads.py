@@ -209,6 +209,23 @@ def greedy_case(B: int, gamma: int, V: int, *, dtype: str = DTYPE_BF16, sigma_t:
     return dict(kind="greedy", dtype=dtype, B=B, gamma=gamma, V=V, bonus=bonus, target=zt_store, draft_ids=ids)
 
 
+def commit_case(B: int, W: int, V: int, *, dtype: str = DTYPE_BF16, sigma: float = 3.0, zipf: float = 1.1,
+                peak: float = 14.0, p_masked: float = 0.75, tau: float = 0.9, seed: int = 0) -> dict:
+    """Masked-diffusion block inputs: logits N(0, sigma^2) plus the Zipf bias, plus a spike of height U(0, peak) at one
+    uniform id per slot (so that slot confidences spread over (0, 1)); each slot still masked with probability
+    ``p_masked``."""
+    r_z, r_h, r_i, r_m = _streams(seed, 4)
+    z = _normal_f32(r_z, (B, W, V), sigma)
+    if zipf:
+        z += (-zipf * np.log1p(np.arange(V, dtype=np.float64))).astype(np.float32)
+    h = uniforms(r_h, (B, W)) * np.float32(peak)
+    at = (uniforms(r_i, (B, W)) * V).astype(np.int64)
+    np.put_along_axis(z, at[..., None], np.take_along_axis(z, at[..., None], axis=-1) + h[..., None], axis=-1)
+    masked = (uniforms(r_m, (B, W)) < p_masked).astype(np.uint8)
+    zs = f32_to_bf16_bits(z) if dtype == DTYPE_BF16 else z
+    return dict(kind="commit", dtype=dtype, B=B, W=W, V=V, logits=zs, masked=masked, tau=float(np.float32(tau)))
+
+
 # ----------------------------------------------------------------------------------------------------------------------
 # Sparse (top-k support) inputs
 # ----------------------------------------------------------------------------------------------------------------------

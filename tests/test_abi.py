@@ -24,7 +24,7 @@ def test_exports_match_header():
     names = declared_functions()
     assert set(names) == {"sv_workspace_bytes", "sv_status_string", "sv_profile_next_stats", "sv_verify_dense",
                           "sv_verify_onehot_draft", "sv_verify_sparse", "sv_support_workspace_bytes",
-                          "sv_build_support", "sv_verify_greedy"}
+                          "sv_build_support", "sv_verify_greedy", "sv_confidence_commit"}
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (sv_[a-z_]+)\b", out))
     assert set(names) <= exported
@@ -214,4 +214,22 @@ def test_greedy_rejects_bad_arguments(kw, code):
     st = sv.LIB.sv_verify_greedy(a["tgt"], a["t_seq"], a["t_row"], a["dtype"], a["B"], a["G"], a["V"], a["ids"],
                                  a["bonus"], a["start"], a["order"], a["accept"], a["n"], a["tok"], a["flags"],
                                  a["ws"], a["ws_bytes"], None)
+    assert st == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(logits=None), -1), (dict(tok=None), -1), (dict(n=None), -1), (dict(dtype=7), -3),
+    (dict(B=0), -2), (dict(W=0), -2), (dict(W=1025), -2), (dict(V=0), -2), (dict(l_row=0), -2),
+    (dict(tau=-0.1), -8), (dict(tau=1.5), -8), (dict(tau=float("nan")), -8),
+    (dict(logits=A + 1, dtype=1), -5), (dict(tok=A + 2), -5), (dict(conf=A + 1), -5), (dict(ws=A + 8), -5),
+    (dict(ws=None), -6), (dict(ws_bytes=8), -6),
+])
+def test_commit_rejects_bad_arguments(kw, code):
+    from lossless_draft_verification_spec_amd import sv
+    a = dict(logits=A, l_seq=4 * 64, l_row=64, dtype=0, B=3, W=4, V=64, masked=A, tau=0.9, commit=A, tok=A, conf=A,
+             n=A, flags=A, ws=A, ws_bytes=1 << 30)
+    a.update(kw)
+    st = sv.LIB.sv_confidence_commit(a["logits"], a["l_seq"], a["l_row"], a["dtype"], a["B"], a["W"], a["V"],
+                                     a["masked"], a["tau"], a["commit"], a["tok"], a["conf"], a["n"], a["flags"],
+                                     a["ws"], a["ws_bytes"], None)
     assert st == code
