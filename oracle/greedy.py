@@ -6,7 +6,7 @@ The HIP library never calls it, and it imports nothing from the HIP package: the
 What it follows (pages cited by title and section):
 - DFlash/DFlash2 guide, section 4.4 "Mathematical Losslessness Guarantee": under greedy decoding (T = 0) a drafted
   token is accepted exactly when it is the target's most likely token at its position (the formula itself is lost
-  in the page's text; the prose around it and the serving example of section 8, whose sampling parameters set
+  in the page's text; the prose around it and the serving example of section 7, whose sampling parameters set
   temperature 0 and call it the greedy verification mode, leave this as the only reading). The block is truncated
   at the first rejected position, as in the sampled case.
 - DFlash/DFlash2 guide, section 2 "Speculative Decoding Speedup Formulation": a cycle yields between 1 and gamma + 1
