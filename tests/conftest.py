@@ -9,3 +9,8 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long-running CPU test")
+    # a planted mistake for tests/test_planted_mistakes.py: the session runs the pins against a mistaken oracle
+    name = os.environ.get("ORACLE_PLANT")
+    if name:
+        import planted
+        planted.plant(name)

@@ -545,6 +545,28 @@ def test_golden_sparse(case):
         np.testing.assert_allclose(res["correction_probs"][0], case["correction_probs"], rtol=1e-15)
 
 
+def window_golden_inputs(case):
+    zt = np.log(np.array(case["p"])).astype(np.float32)[None]
+    zd = np.log(np.array(case["q"])).astype(np.float32)[None]
+    ua = np.array([[r["u_accept"]] for r in case["rounds"]], np.float32)
+    us = np.array([[r["u_sample"]] for r in case["rounds"]], np.float32)
+    return zt, zd, np.array([case["draft_ids"]], np.int32), ua, us, np.array([case["order"]], np.int32)
+
+
+@pytest.mark.parametrize("case", _golden()["window"], ids=lambda c: c["name"][:40])
+def test_golden_window_rounds(case):
+    zt, zd, ids, ua, us, order = window_golden_inputs(case)
+    res = oracle.verify_windows(zt, zd, ids, ua, us, case["T"], order=order)
+    assert len(res) == len(case["rounds"])
+    for r, (got, want) in enumerate(zip(res, case["rounds"])):
+        np.testing.assert_array_equal(got["accept"][0], want["accept"], err_msg=f"round {r}")
+        assert got["n_accepted"][0] == want["n_accepted"], f"round {r}"
+        assert got["out_token"][0] == want["out_token"], f"round {r}"
+        assert got["start_out"][0] == want["start_out"], f"round {r}"
+        np.testing.assert_allclose(got["p_draft"][0], want["p_draft"], rtol=1e-6, atol=1e-12)
+        np.testing.assert_allclose(got["q_draft"][0], want["q_draft"], rtol=1e-6, atol=1e-12)
+
+
 # ----------------------------------------------------------------------------------------------------------------------
 # The pins catch plausible mistakes (planted in the oracle, on the CPU)
 # ----------------------------------------------------------------------------------------------------------------------
