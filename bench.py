@@ -2,22 +2,30 @@
 
 One step = one full verification call (statistics, accept/first-reject scan, float64 draw: one kernel launch) over the
 dense block workload: B=64 sequences, gamma=16 drafts, V=151936, bf16 target and draft logits (synthetic, seeded). The
-headline value is verified draft positions per second; the roofline object reports the verifier kernel's achieved HBM
+headline value is verified draft positions per second. The roofline object reports the verifier kernel's achieved HBM
 bandwidth: algorithmic bytes per launch (every verified logit of both tensors, 2*B*gamma*V*2, plus the row pair each
-rejected sequence's draw reads again, or the target row of a bonus draw) over its average duration, timed with HIP
-events taken from the kernel's own dispatch on its stream, in a second timed region of the same steps (the whole-call
-figure comes from steps without the events). The other workloads (the dense -> top-k/top-p support -> sparse verify
-chain on the headline's logits, tiny dense, greedy one-hot, sparse top-64, masked-diffusion window with 4 chained
-rounds) are timed after it and reported under "workloads".
+rejected sequence's draw reads again, or the target row of a bonus draw) over the average launch duration, taken
+from HIP events on the launch stream around the K timed steps (each step is exactly one launch, so this average
+includes the gap between back-to-back launches: it bounds the kernel's own duration from above).
+
+The other workloads are timed after it, each in its own region of back-to-back launches of one kernel, and reported
+under "workloads": the dense -> top-k/top-p support -> sparse verify chain on the headline's logits (each of its three
+kernels alone, then the whole chain), tiny dense, greedy one-hot, sparse top-64, the masked-diffusion window (per
+round, from events between the rounds of each chained step, and the whole 4-round chain), greedy verification at
+T = 0, the confidence-threshold commit, and tree verification.
+
+The CPU baseline is the float64 oracle as it stands, timed before the GPU is touched on bounded samples of the
+headline workload: once in this process (one thread) and once over a pool of worker processes on the host cores this
+process may run on (at most 16).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--cpu-seconds S] [--only NAME]
-Prints one JSON line on stdout.
+Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
 
 import argparse
-import ctypes
 import json
+import multiprocessing as mp
 import os
 import sys
 import time
@@ -31,36 +39,11 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0
 HEADLINE = "dense_block_B64_g16_V151936_bf16"
 METRIC = "verified draft positions/sec + achieved HBM GB/s (% of peak), dense B x gamma x V"
+CPU_POOL_MAX = 16
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
-
-
-class HipEvents:
-    """hipEvent_t pairs from the process's HIP runtime (the one torch loaded)."""
-
-    def __init__(self, n):
-        self.hip = ctypes.CDLL("libamdhip64.so.7")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
-        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
-        self.pairs = []
-        for _ in range(n):
-            a, b = ctypes.c_void_p(), ctypes.c_void_p()
-            assert self.hip.hipEventCreate(ctypes.byref(a)) == 0 and self.hip.hipEventCreate(ctypes.byref(b)) == 0
-            self.pairs.append((a, b))
-
-    def elapsed_ms(self, i):
-        ms = ctypes.c_float()
-        st = self.hip.hipEventElapsedTime(ctypes.byref(ms), self.pairs[i][0], self.pairs[i][1])
-        assert st == 0, f"hipEventElapsedTime failed: {st}"
-        return ms.value
-
-    def close(self):
-        for a, b in self.pairs:
-            self.hip.hipEventDestroy(a)
-            self.hip.hipEventDestroy(b)
 
 
 def to_dev_logits(x, dtype, torch, d):
@@ -68,7 +51,9 @@ def to_dev_logits(x, dtype, torch, d):
     return (t.view(torch.bfloat16) if dtype == "bf16" else t).to(d)
 
 
-def time_steps(fn, steps, warmup, torch):
+def time_region(fn, steps, warmup, torch):
+    """Average ms per step over `steps` back-to-back calls of fn(i), from events on the current stream (the stream
+    every call launches on), after `warmup` untimed calls. Also returns the host wall time per step."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -79,12 +64,26 @@ def time_steps(fn, steps, warmup, torch):
         fn(i)
     e1.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return e0.elapsed_time(e1) / steps, wall / steps * 1e3
+    return e0.elapsed_time(e1) / steps, (time.perf_counter() - t0) * 1e3 / steps
 
 
-def bench_dense(case, steps, warmup, torch, sv, d, profile_events=True):
-    """Dense or one-hot workload: returns timing and byte accounting."""
+def hbm(nbytes, ms):
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return gbps, gbps / HBM_PEAK_GBPS
+
+
+def roofline(nbytes, ms, kernel, traffic=None):
+    gbps, frac = hbm(nbytes, ms)
+    return {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": frac,
+            "traffic": traffic, "kernel": kernel, "kernel_ms": ms, "bytes_per_launch": nbytes}
+
+
+# ----------------------------------------------------------------------------------------------------------------------
+# dense / one-hot
+# ----------------------------------------------------------------------------------------------------------------------
+
+def bench_dense(case, steps, warmup, torch, sv, d, traffic=None):
+    """Dense or one-hot workload: one launch of k_verify per step."""
     onehot = case["kind"] == "onehot"
     B, G, V = case["B"], case["gamma"], case["V"]
     s = 2 if case["dtype"] == "bf16" else 4
@@ -98,42 +97,16 @@ def bench_dense(case, steps, warmup, torch, sv, d, profile_events=True):
     kind = sv.SV_KIND_ONEHOT if onehot else sv.SV_KIND_DENSE
     ws = sv.workspace(kind, B, G, V, d)
     out = {}
-    ev = HipEvents(steps) if profile_events else None
-    state = {"timed": False}
 
     def step(i):
         c = i % ncopies
-        if state["timed"] and ev is not None:
-            sv.sv_profile_next_stats(ev.pairs[i][0], ev.pairs[i][1])
         if onehot:
             sv.sv_verify_onehot_draft(tgts[c], ids, ua, us, case["temperature"], bonus=case["bonus"], out=out, ws=ws)
         else:
             sv.sv_verify_dense(tgts[c], dfts[c], ids, ua, us, case["temperature"], bonus=case["bonus"], out=out,
                                ws=ws)
 
-    def region(profiled):
-        state["timed"] = profiled
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        e0.record()
-        for i in range(steps):
-            step(i)
-        e1.record()
-        torch.cuda.synchronize()
-        state["timed"] = False
-        return e0.elapsed_time(e1) / steps, (time.perf_counter() - t0) * 1e3 / steps
-
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    # The whole-call figure comes from steps with no event hook; a second region of the same steps records the
-    # kernel's own start/stop events on every launch.
-    ms, wall_ms = region(False)
-    stats_ms = None
-    if ev is not None:
-        ms_profiled, _ = region(True)
-        stats_ms = float(np.mean([ev.elapsed_ms(i) for i in range(steps)]))
-        ev.close()
+    ms, wall_ms = time_region(step, steps, warmup, torch)
     n = out["n_accepted"].cpu().numpy()
     tok = out["out_token"].cpu().numpy()
     draws = int((tok >= 0).sum())
@@ -142,23 +115,24 @@ def bench_dense(case, steps, warmup, torch, sv, d, profile_events=True):
     bonus_draws = draws - resid
     draw_bytes = resid * (1 if onehot else 2) * V * s + bonus_draws * V * s
     total_bytes = verified_bytes + draw_bytes
-    res = dict(ms_per_step=ms, wall_ms_per_step=wall_ms, positions=B * G, positions_per_s=B * G / (ms * 1e-3),
-               algorithmic_bytes=total_bytes, hbm_GBps=total_bytes / (ms * 1e-3) / 1e9,
-               hbm_frac=total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, mean_n_accepted=float(n.mean()),
-               input_copies=ncopies)
-    if stats_ms is not None:
-        res.update(ms_per_step_with_kernel_events=ms_profiled, kernel_ms=stats_ms, kernel_bytes=total_bytes,
-                   kernel_GBps=total_bytes / (stats_ms * 1e-3) / 1e9)
-    return res
+    gbps, frac = hbm(total_bytes, ms)
+    return dict(ms_per_step=ms, wall_ms_per_step=wall_ms, positions=B * G, positions_per_s=B * G / (ms * 1e-3),
+                algorithmic_bytes=total_bytes, hbm_GBps=gbps, hbm_frac=frac, mean_n_accepted=float(n.mean()),
+                residual_draws=resid, bonus_draws=bonus_draws, input_copies=ncopies,
+                roofline=roofline(total_bytes, ms, "k_verify<bf16>" if s == 2 else "k_verify<f32>", traffic))
 
+
+# ----------------------------------------------------------------------------------------------------------------------
+# dense -> support -> sparse chain
+# ----------------------------------------------------------------------------------------------------------------------
 
 SUPPORT = "support_chain_B64_g16_V151936_k50_p095_bf16"
 
 
 def bench_support(case, steps, warmup, torch, sv, d, k=50, top_p=0.95):
     """Dense -> sparse -> verify on the headline workload's logits: top-k / top-p supports of the target rows
-    (B x (gamma+1)) and of the draft rows (B x gamma), then the sparse verify of the drafted ids on them. The two
-    support builds are timed from their own dispatches (HIP events) in a second region of the same steps."""
+    (B x (gamma+1)) and of the draft rows (B x gamma), then the sparse verify of the drafted ids on them. Each of the
+    three kernels is timed alone in its own region, then the whole chain."""
     B, G, V = case["B"], case["gamma"], case["V"]
     rows_t, rows_d = B * (G + 1), B * G
     ncopies = 2                                                         # 1.28 GB per step pair: no cache reuse
@@ -170,40 +144,44 @@ def bench_support(case, steps, warmup, torch, sv, d, k=50, top_p=0.95):
     ws_t = sv.support_workspace(rows_t, V, k, d)
     ws_d = sv.support_workspace(rows_d, V, k, d)
     po, qo, vo = {}, {}, {}
-    ev_t, ev_d = HipEvents(steps), HipEvents(steps)
-    state = {"timed": False}
 
-    def step(i):
-        c = i % ncopies
-        if state["timed"]:
-            sv.sv_profile_next_stats(ev_t.pairs[i][0], ev_t.pairs[i][1])
-        sv.sv_build_support(tgts[c], k, top_p, case["temperature"], True, out=po, ws=ws_t)
-        if state["timed"]:
-            sv.sv_profile_next_stats(ev_d.pairs[i][0], ev_d.pairs[i][1])
-        sv.sv_build_support(dfts[c], k, top_p, case["temperature"], True, out=qo, ws=ws_d)
+    def sup_t(i):
+        sv.sv_build_support(tgts[i % ncopies], k, top_p, case["temperature"], True, out=po, ws=ws_t)
+
+    def sup_d(i):
+        sv.sv_build_support(dfts[i % ncopies], k, top_p, case["temperature"], True, out=qo, ws=ws_d)
+
+    def verify(i):
         sv.sv_verify_sparse(po["ids"].view(B, G + 1, k), po["probs"].view(B, G + 1, k), qo["ids"].view(B, G, k),
                             qo["probs"].view(B, G, k), ids, ua, us, bonus=1, vocab_size=V, out=vo)
 
-    ms, wall = time_steps(step, steps, warmup, torch)
-    state["timed"] = True
-    time_steps(step, steps, 0, torch)
-    state["timed"] = False
-    kt = float(np.mean([ev_t.elapsed_ms(i) for i in range(steps)]))
-    kd = float(np.mean([ev_d.elapsed_ms(i) for i in range(steps)]))
-    ev_t.close()
-    ev_d.close()
+    def chain(i):
+        sup_t(i)
+        sup_d(i)
+        verify(i)
+
+    kt, _ = time_region(sup_t, steps, warmup, torch)
+    kd, _ = time_region(sup_d, steps, warmup, torch)
+    kv, _ = time_region(verify, steps, warmup, torch)
+    ms, wall = time_region(chain, steps, warmup, torch)
     out_row = k * 8 + 8                                                 # ids, probs, count, flags per row
     bytes_t, bytes_d = rows_t * (V * 2 + out_row), rows_d * (V * 2 + out_row)
     n = vo["n_accepted"].cpu().numpy()
+    gt, ft = hbm(bytes_t, kt)
+    gd, fd = hbm(bytes_d, kd)
     return dict(ms_per_step=ms, wall_ms_per_step=wall, positions=B * G, positions_per_s=B * G / (ms * 1e-3),
                 k=k, top_p=top_p, mean_n_accepted=float(n.mean()),
                 mean_kept_target=float(po["count"].float().mean().item()),
                 mean_kept_draft=float(qo["count"].float().mean().item()),
-                support_kernel_ms_target=kt, support_kernel_ms_draft=kd,
+                support_ms_target=kt, support_ms_draft=kd, sparse_ms=kv,
                 support_bytes_target=bytes_t, support_bytes_draft=bytes_d,
-                support_GBps_target=bytes_t / (kt * 1e-3) / 1e9, support_GBps_draft=bytes_d / (kd * 1e-3) / 1e9,
-                support_hbm_frac=(bytes_t + bytes_d) / ((kt + kd) * 1e-3) / 1e9 / HBM_PEAK_GBPS)
+                support_GBps_target=gt, support_GBps_draft=gd, support_frac_target=ft, support_frac_draft=fd,
+                roofline=roofline(bytes_t, kt, "k_support<bf16> (target rows)"))
 
+
+# ----------------------------------------------------------------------------------------------------------------------
+# greedy, commit
+# ----------------------------------------------------------------------------------------------------------------------
 
 GREEDY = "greedy_block_B64_g16_V151936_bf16"
 
@@ -211,7 +189,7 @@ GREEDY = "greedy_block_B64_g16_V151936_bf16"
 def bench_greedy(steps, warmup, torch, sv, d):
     """Greedy (T = 0) verification of the block workload's shape: B = 64, gamma = 16, V = 151936, bf16 target with
     the Zipf bias; drafts equal the target argmax with probability 0.85. Every target row (gamma + 1 per sequence)
-    is read once; the kernel is timed from its own dispatches in a second region of the same steps."""
+    is read once; one launch of k_greedy per step."""
     from lossless_draft_verification_spec_amd import workloads
     case = workloads.greedy_case(64, 16, 151936, seed=0)
     B, G, V = case["B"], case["gamma"], case["V"]
@@ -220,30 +198,19 @@ def bench_greedy(steps, warmup, torch, sv, d):
     ids = torch.from_numpy(case["draft_ids"]).to(d)
     ws = sv.workspace(sv.SV_KIND_GREEDY, B, G, V, d)
     out = {}
-    ev = HipEvents(steps)
-    state = {"timed": False}
 
     def step(i):
-        if state["timed"]:
-            sv.sv_profile_next_stats(ev.pairs[i][0], ev.pairs[i][1])
         sv.sv_verify_greedy(tgts[i % ncopies], ids, bonus=1, out=out, ws=ws)
 
-    ms, wall = time_steps(step, steps, warmup, torch)
-    state["timed"] = True
-    time_steps(step, steps, 0, torch)
-    state["timed"] = False
-    km = float(np.mean([ev.elapsed_ms(i) for i in range(steps)]))
-    ev.close()
+    ms, wall = time_region(step, steps, warmup, torch)
     # every target row once, the draft ids, and accept / n / token / flags written
     nbytes = B * (G + 1) * V * 2 + B * G * 4 + B * G + B * 12
     n = out["n_accepted"].cpu().numpy()
     del tgts
-    gbps = nbytes / (km * 1e-3) / 1e9
+    gbps, frac = hbm(nbytes, ms)
     return dict(ms_per_step=ms, wall_ms_per_step=wall, positions=B * G, positions_per_s=B * G / (ms * 1e-3),
-                mean_n_accepted=float(n.mean()), kernel_ms=km, kernel_bytes=nbytes, kernel_GBps=gbps,
-                kernel_hbm_frac=gbps / HBM_PEAK_GBPS, input_copies=ncopies,
-                roofline={"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                          "frac": gbps / HBM_PEAK_GBPS, "traffic": greedy_traffic(), "kernel": "k_greedy"})
+                mean_n_accepted=float(n.mean()), algorithmic_bytes=nbytes, hbm_GBps=gbps, hbm_frac=frac,
+                input_copies=ncopies, roofline=roofline(nbytes, ms, "k_greedy<bf16>"))
 
 
 COMMIT = "commit_block_B256_W4_V151936_bf16"
@@ -251,8 +218,7 @@ COMMIT = "commit_block_B256_W4_V151936_bf16"
 
 def bench_commit(steps, warmup, torch, sv, d):
     """Confidence-threshold commit of masked-diffusion blocks: B = 256 blocks of W = 4 slots over V = 151936, bf16,
-    three quarters of the slots still masked, tau = 0.9. Only masked slots are read; the kernel is timed from its own
-    dispatches in a second region of the same steps."""
+    three quarters of the slots still masked, tau = 0.9. Only masked slots are read; one launch per step."""
     from lossless_draft_verification_spec_amd import workloads
     case = workloads.commit_case(256, 4, 151936, seed=0)
     B, Wn, V = case["B"], case["W"], case["V"]
@@ -261,36 +227,27 @@ def bench_commit(steps, warmup, torch, sv, d):
     masked = torch.from_numpy(case["masked"]).to(d)
     ws = sv.workspace(sv.SV_KIND_GREEDY, B, Wn, V, d)
     out = {}
-    ev = HipEvents(steps)
-    state = {"timed": False}
 
     def step(i):
-        if state["timed"]:
-            sv.sv_profile_next_stats(ev.pairs[i][0], ev.pairs[i][1])
         sv.sv_confidence_commit(zs[i % ncopies], case["tau"], masked, out=out, ws=ws)
 
-    ms, wall = time_steps(step, steps, warmup, torch)
-    state["timed"] = True
-    time_steps(step, steps, 0, torch)
-    state["timed"] = False
-    km = float(np.mean([ev.elapsed_ms(i) for i in range(steps)]))
-    ev.close()
+    ms, wall = time_region(step, steps, warmup, torch)
     nm = int(case["masked"].sum())
     # every masked row once, the mask, and commit / token / confidence per slot and the count and flags per block
     nbytes = nm * V * 2 + B * Wn + B * Wn * 9 + B * 8
-    gbps = nbytes / (km * 1e-3) / 1e9
     del zs
+    gbps, frac = hbm(nbytes, ms)
     return dict(ms_per_step=ms, wall_ms_per_step=wall, slots=B * Wn, masked_slots=nm,
-                committed=int(out["n_commit"].sum().item()), kernel_ms=km, kernel_bytes=nbytes, kernel_GBps=gbps,
-                kernel_hbm_frac=gbps / HBM_PEAK_GBPS,
-                roofline={"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                          "frac": gbps / HBM_PEAK_GBPS,
-                          "traffic": greedy_traffic("k_greedy_commit_block_traffic.txt", "masked"),
-                          "kernel": "k_greedy (commit mode)"})
+                committed=int(out["n_commit"].sum().item()), algorithmic_bytes=nbytes, hbm_GBps=gbps,
+                hbm_frac=frac, roofline=roofline(nbytes, ms, "k_greedy<bf16> (commit mode)"))
 
+
+# ----------------------------------------------------------------------------------------------------------------------
+# sparse, windows
+# ----------------------------------------------------------------------------------------------------------------------
 
 def bench_sparse(case, steps, warmup, torch, sv, d):
-    B, G, k = case["B"], case["gamma"], case["k"]
+    B, G = case["B"], case["gamma"]
     t = {key: torch.from_numpy(np.ascontiguousarray(case[key])).to(d)
          for key in ("p_ids", "p_probs", "q_ids", "q_probs", "spec_ids", "u_accept", "u_sample")}
     out = {}
@@ -299,14 +256,17 @@ def bench_sparse(case, steps, warmup, torch, sv, d):
         sv.sv_verify_sparse(t["p_ids"], t["p_probs"], t["q_ids"], t["q_probs"], t["spec_ids"], t["u_accept"],
                             t["u_sample"], bonus=1, vocab_size=case["V"], out=out)
 
-    ms, wall = time_steps(step, steps, warmup, torch)
+    ms, wall = time_region(step, steps, warmup, torch)
     in_bytes = sum(int(v.numel() * v.element_size()) for v in t.values())
     out_bytes = sum(int(v.numel() * v.element_size()) for v in out.values())
+    gbps, frac = hbm(in_bytes + out_bytes, ms)
     return dict(ms_per_step=ms, wall_ms_per_step=wall, positions=B * G, positions_per_s=B * G / (ms * 1e-3),
-                algorithmic_bytes=in_bytes + out_bytes, hbm_GBps=(in_bytes + out_bytes) / (ms * 1e-3) / 1e9)
+                algorithmic_bytes=in_bytes + out_bytes, hbm_GBps=gbps, hbm_frac=frac)
 
 
 def bench_window(case, steps, warmup, torch, sv, d):
+    """The masked-diffusion window: every step runs the 4 chained rounds from start = 0. Events recorded between the
+    rounds of each step give each round's time; the chain's time is the whole step."""
     B, W, V, R = case["B"], case["gamma"], case["V"], case["rounds"]
     tgt = to_dev_logits(case["target"], "f32", torch, d)
     dft = to_dev_logits(case["draft"], "f32", torch, d)
@@ -318,103 +278,158 @@ def bench_window(case, steps, warmup, torch, sv, d):
     start = torch.zeros(B, dtype=torch.int32, device=d)
     zero = torch.zeros(B, dtype=torch.int32, device=d)
     outs = [dict() for _ in range(R)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(R + 1)] for _ in range(steps)]
+    state = {"timed": False}
 
     def step(i):
         start.copy_(zero)
         for r in range(R):
+            if state["timed"]:
+                evs[i][r].record()
             sv.sv_verify_dense(tgt, dft, ids, ua[r], us[r], case["temperature"], bonus=0, start=start, order=order,
                                out=outs[r], ws=ws)
+        if state["timed"]:
+            evs[i][R].record()
 
-    ms, wall = time_steps(step, steps, warmup, torch)
-    # verified positions and bytes of the chain, replayed once with the starts observed per round
+    ms, wall = time_region(step, steps, warmup, torch)
+    state["timed"] = True
+    time_region(step, steps, 0, torch)
+    round_ms = [float(np.mean([evs[i][r].elapsed_time(evs[i][r + 1]) for i in range(steps)])) for r in range(R)]
+    # verified positions and bytes of each round, replayed once with the starts observed per round
     start.zero_()
-    positions, total_bytes = 0, 0
+    rounds = []
     for r in range(R):
         st = start.cpu().numpy()
         verified = int(np.sum(W - st))
         sv.sv_verify_dense(tgt, dft, ids, ua[r], us[r], case["temperature"], bonus=0, start=start, order=order,
                            out=outs[r], ws=ws)
         tok = outs[r]["out_token"].cpu().numpy()
-        positions += verified
-        total_bytes += 2 * verified * V * 4 + int((tok >= 0).sum()) * 2 * V * 4
+        nbytes = 2 * verified * V * 4 + int((tok >= 0).sum()) * 2 * V * 4
+        gbps, frac = hbm(nbytes, round_ms[r])
+        rounds.append(dict(round=r, ms=round_ms[r], positions=verified, positions_per_s=verified / (round_ms[r] * 1e-3),
+                           algorithmic_bytes=nbytes, logits=2 * verified * V, hbm_GBps=gbps, hbm_frac=frac))
     torch.cuda.synchronize()
-    return dict(ms_per_step=ms, wall_ms_per_step=wall, rounds=R, positions=positions,
-                positions_per_s=positions / (ms * 1e-3), algorithmic_bytes=total_bytes,
-                hbm_GBps=total_bytes / (ms * 1e-3) / 1e9, hbm_frac=total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS)
+    positions = sum(x["positions"] for x in rounds)
+    total_bytes = sum(x["algorithmic_bytes"] for x in rounds)
+    gbps, frac = hbm(total_bytes, ms)
+    return dict(ms_per_step=ms, wall_ms_per_step=wall, rounds=rounds, positions=positions,
+                positions_per_s=positions / (ms * 1e-3), algorithmic_bytes=total_bytes, hbm_GBps=gbps, hbm_frac=frac,
+                roofline=roofline(rounds[0]["algorithmic_bytes"], rounds[0]["ms"], "k_verify<f32> (round 0)"))
+
+
+# ----------------------------------------------------------------------------------------------------------------------
+# tree verification
+# ----------------------------------------------------------------------------------------------------------------------
+
+TREE = "tree_B64_N16_V151936_bf16"
+
+
+def bench_tree(steps, warmup, torch, sv, d):
+    from lossless_draft_verification_spec_amd import workloads
+    case = workloads.make(TREE)
+    B, N, V = case["B"], case["N"], case["V"]
+    ncopies = 3
+    tgts = [to_dev_logits(case["target"], "bf16", torch, d) for _ in range(ncopies)]
+    par = torch.from_numpy(case["parent"]).to(d)
+    tok = torch.from_numpy(case["token"]).to(d)
+    ua = torch.from_numpy(case["u_accept"]).to(d)
+    us = torch.from_numpy(case["u_sample"]).to(d)
+    ws = sv.workspace(sv.SV_KIND_TREE, B, N, V, d)
+    out = {}
+
+    def step(i):
+        sv.sv_verify_tree(tgts[i % ncopies], par, tok, ua, us, case["temperature"], out=out, ws=ws)
+
+    ms, wall = time_region(step, steps, warmup, torch)
+    n = out["n_accepted"].cpu().numpy()
+    # every node row once; the stop node's row once more for the draw
+    nbytes = B * N * V * 2 + int((out["out_token"].cpu().numpy() >= 0).sum()) * V * 2
+    gbps, frac = hbm(nbytes, ms)
+    del tgts
+    return dict(ms_per_step=ms, wall_ms_per_step=wall, sequences=B, nodes=N, mean_accepted_path=float(n.mean()),
+                algorithmic_bytes=nbytes, hbm_GBps=gbps, hbm_frac=frac, roofline=roofline(nbytes, ms, "k_tree<bf16>"))
+
+
+# ----------------------------------------------------------------------------------------------------------------------
+# CPU baseline (the oracle as it stands)
+# ----------------------------------------------------------------------------------------------------------------------
+
+_POOL_CASE = None
+
+
+def _oracle_slice(b0):
+    import oracle
+    c = _POOL_CASE
+    sl = slice(b0, b0 + 4)
+    oracle.verify_dense(c["target"][sl], c["draft"][sl], c["draft_ids"][sl], c["u_accept"][sl], c["u_sample"][sl],
+                        c["temperature"], dtype=c["dtype"])
+    return c["draft_ids"][sl].shape[0]
 
 
 def cpu_baseline(case, seconds):
-    """The float64 oracle, as it stands, on a bounded sample of the headline workload (whole sequences)."""
+    """The float64 oracle on bounded samples of the headline workload (4 whole sequences per task): one thread in
+    this process for about `seconds`, then a pool of worker processes, one per usable core (at most 16), for about as
+    long. Runs before the GPU is touched, so the workers are plain CPU processes."""
+    global _POOL_CASE
     import oracle
     B, G = case["B"], case["gamma"]
     t0 = time.perf_counter()
-    done = 0
-    b = 0
+    done, b = 0, 0
     while time.perf_counter() - t0 < seconds:
         sl = slice(b % B, b % B + 4)
         oracle.verify_dense(case["target"][sl], case["draft"][sl], case["draft_ids"][sl], case["u_accept"][sl],
                             case["u_sample"][sl], case["temperature"], dtype=case["dtype"])
         done += case["draft_ids"][sl].shape[0]
         b += 4
-    dt = time.perf_counter() - t0
-    return dict(value=done * G / dt, unit="positions/s", cores=1, kind="oracle",
-                sample=f"{done} of the {B} sequences x {G} drafts (4 at a time, wrapping) in {dt:.1f} s, "
-                       f"numpy float64, one thread")
+    dt1 = time.perf_counter() - t0
+    rate1 = done * G / dt1
+    cores = min(CPU_POOL_MAX, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count())
+    _POOL_CASE = case
+    per_task = dt1 / max(1, done // 4)
+    ntask = max(cores, int(round(seconds / per_task)) * cores)
+    starts = [(4 * i) % B for i in range(ntask)]
+    with mp.get_context("fork").Pool(cores) as pool:
+        pool.map(_oracle_slice, [0] * cores)                   # workers started and warm
+        t0 = time.perf_counter()
+        seqs = sum(pool.map(_oracle_slice, starts, chunksize=1))
+        dtp = time.perf_counter() - t0
+    _POOL_CASE = None
+    ratep = seqs * G / dtp
+    log(f"cpu oracle: {rate1:.0f} positions/s on 1 thread, {ratep:.0f} on {cores} processes")
+    return dict(value=ratep, unit="positions/s", cores=cores, kind="oracle",
+                sample=f"{seqs} sequences x {G} drafts of the headline workload (4 per task, wrapping over its {B}) "
+                       f"on a pool of {cores} worker processes in {dtp:.1f} s; numpy float64",
+                single_thread=dict(value=rate1, cores=1, sample=f"{done} sequences in {dt1:.1f} s, one thread"))
 
 
-KERNEL_SOURCES = ("sv_dense.hip", "sv_device.h", "sv_internal.h")    # what k_verify is compiled from
+# ----------------------------------------------------------------------------------------------------------------------
+# measured HBM traffic from committed counter summaries
+# ----------------------------------------------------------------------------------------------------------------------
 
-
-def kernel_source_sha():
-    """sha256 over the verifier kernel's source files, in KERNEL_SOURCES order."""
+def _sources_sha(names):
     import hashlib
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in names:
         with open(os.path.join(ROOT, "lossless_draft_verification_spec_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-GREEDY_SOURCES = ("sv_greedy.hip", "sv_greedy.h", "sv_device.h", "sv_internal.h")   # what k_greedy is built from
-
-
-def greedy_traffic(profile="k_greedy_block_traffic.txt", key="target"):
-    """HBM bytes per launch of k_greedy (greedy verification, or commit mode with the commit profile) from the
-    committed counter summary, or None when its sources have changed since the counters were taken."""
-    import hashlib
-    h = hashlib.sha256()
+def profile_traffic(profile, key):
+    """HBM bytes per launch from a committed FETCH_SIZE / WRITE_SIZE summary (line 'TRAFFIC_JSON {...}' holding
+    source_files, source_sha256 and per-workload traffic_bytes), or None when the kernel's sources have changed since
+    the counters were taken."""
     try:
-        for name in GREEDY_SOURCES:
-            with open(os.path.join(ROOT, "lossless_draft_verification_spec_amd", "csrc", name), "rb") as f:
-                h.update(f.read())
         rec = None
         with open(os.path.join(ROOT, "profiles", profile)) as f:
             for ln in f:
                 if ln.startswith("TRAFFIC_JSON "):
                     rec = json.loads(ln[len("TRAFFIC_JSON "):])
-    except OSError:
+        if rec is None or rec.get("source_sha256") != _sources_sha(rec["source_files"]):
+            return None
+        return int(rec["workloads"][key]["traffic_bytes"])
+    except (OSError, KeyError, ValueError):
         return None
-    if rec is None or rec.get("source_sha256") != h.hexdigest():
-        return None
-    return int(rec[key]["traffic_bytes"])
-
-
-def measured_traffic():
-    """HBM bytes per launch of the verifier kernel from the committed FETCH_SIZE / WRITE_SIZE counter summary, or
-    None when the kernel source has changed since the counters were taken."""
-    prof = os.path.join(ROOT, "profiles", "k_verify_dense_block_traffic.txt")
-    try:
-        rec = None
-        with open(prof) as f:
-            for ln in f:
-                if ln.startswith("TRAFFIC_JSON "):
-                    rec = json.loads(ln[len("TRAFFIC_JSON "):])
-        sha = kernel_source_sha()
-    except OSError:
-        return None
-    if rec is None or rec.get("source_sha256") != sha:
-        return None
-    return int(rec["traffic_bytes"])
 
 
 def main():
@@ -423,7 +438,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--only", default=None,
                     help="time only this workload besides the headline ('headline': the headline alone)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -434,8 +449,13 @@ def main():
               f"exchange, so the per-GPU figure is the one this run measures.", file=sys.stderr)
         sys.exit(2)
 
+    from lossless_draft_verification_spec_amd import workloads
+    log("generating", HEADLINE)
+    head = workloads.make(HEADLINE)
+    cpu = None if args.no_cpu else cpu_baseline(head, args.cpu_seconds)
+
     import torch
-    from lossless_draft_verification_spec_amd import sv, workloads
+    from lossless_draft_verification_spec_amd import sv
 
     d = torch.device("cuda", 0)
     if args.calibrate_copy:
@@ -447,32 +467,31 @@ def main():
         log("calibration copy: 3 x 1 GiB")
         del src, dst
         torch.cuda.empty_cache()
-    log("generating", HEADLINE)
-    head = workloads.make(HEADLINE)
-    r = bench_dense(head, args.steps, args.warmup, torch, sv, d)
+    r = bench_dense(head, args.steps, args.warmup, torch, sv, d,
+                    traffic=profile_traffic("k_verify_traffic.txt", HEADLINE))
     log("headline", json.dumps(r))
 
     others = {}
-    if args.only in (None, SUPPORT):
-        others[SUPPORT] = bench_support(head, args.steps, args.warmup, torch, sv, d)
-        log(SUPPORT, json.dumps(others[SUPPORT]))
-        torch.cuda.empty_cache()
-    if args.only in (None, GREEDY):
-        others[GREEDY] = bench_greedy(args.steps, args.warmup, torch, sv, d)
-        log(GREEDY, json.dumps(others[GREEDY]))
-        torch.cuda.empty_cache()
-    if args.only in (None, COMMIT):
-        others[COMMIT] = bench_commit(args.steps, args.warmup, torch, sv, d)
-        log(COMMIT, json.dumps(others[COMMIT]))
-        torch.cuda.empty_cache()
-    names = [n for n in workloads.WORKLOADS if n != HEADLINE]
+    legs = [(SUPPORT, lambda: bench_support(head, args.steps, args.warmup, torch, sv, d)),
+            (GREEDY, lambda: bench_greedy(args.steps, args.warmup, torch, sv, d)),
+            (COMMIT, lambda: bench_commit(args.steps, args.warmup, torch, sv, d))]
+    if hasattr(sv, "sv_verify_tree"):
+        legs.append((TREE, lambda: bench_tree(args.steps, args.warmup, torch, sv, d)))
+    for name, fn in legs:
+        if args.only in (None, name):
+            others[name] = fn()
+            log(name, json.dumps(others[name]))
+            torch.cuda.empty_cache()
+    del head
+    names = [n for n in workloads.WORKLOADS if n != HEADLINE and n != TREE]
     if args.only:
         names = [n for n in names if n == args.only]
     for name in names:
         log("generating", name)
         c = workloads.make(name)
         if c["kind"] in ("dense", "onehot"):
-            others[name] = bench_dense(c, args.steps, args.warmup, torch, sv, d)
+            others[name] = bench_dense(c, args.steps, args.warmup, torch, sv, d,
+                                       traffic=profile_traffic("k_verify_traffic.txt", name))
         elif c["kind"] == "sparse":
             others[name] = bench_sparse(c, args.steps, args.warmup, torch, sv, d)
         else:
@@ -481,7 +500,6 @@ def main():
         del c
         torch.cuda.empty_cache()
 
-    cpu = None if args.no_cpu else cpu_baseline(head, args.cpu_seconds)
     line = {
         "metric": METRIC, "value": r["positions_per_s"], "unit": "positions/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": r["ms_per_step"], "higher_is_better": True, "scaling": "weak",
@@ -489,10 +507,7 @@ def main():
         "config": {"workload": HEADLINE, "B": 64, "gamma": 16, "V": 151936, "logits": "bf16", "temperature": 1.0,
                    "bonus": 1},
         "hbm_GBps": r["hbm_GBps"], "hbm_frac_of_peak": r["hbm_frac"],
-        "roofline": {"bound": "hbm", "achieved": r.get("kernel_GBps"), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": (r["kernel_GBps"] / HBM_PEAK_GBPS) if r.get("kernel_GBps") else None,
-                     "traffic": measured_traffic(), "kernel": "k_verify (statistics, scan and draw)",
-                     "traffic_unit": "B/launch", "kernel_ms": r.get("kernel_ms"), "kernel_bytes": r.get("kernel_bytes")},
+        "roofline": r["roofline"],
         "cpu_baseline": cpu,
         "workloads": {HEADLINE: r, **others},
     }

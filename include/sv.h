@@ -10,9 +10,9 @@
  * both sides before the ratio).
  *
  * Conventions shared by every entry point
- * - Every array argument is a DEVICE pointer owned by the caller. The library allocates nothing and may be called
- *   from several host threads on different streams; between calls it keeps only a host-side note of the layout
- *   each workspace was last used with (see sv_workspace_bytes).
+ * - Every array argument is a DEVICE pointer owned by the caller. The library allocates nothing, keeps no state of
+ *   its own between calls (what a call leaves for the next one lives in the caller's workspace, see
+ *   sv_workspace_bytes) and may be called from several host threads on different streams.
  * - Work is enqueued on `stream` (a hipStream_t, or NULL for the null stream) of the current device; outputs are
  *   valid once that stream has reached the enqueued work. No call synchronises the host.
  * - The return value is 0 (SV_OK) or a negative SV_ERR_* code. Argument errors are detected on the host BEFORE any
@@ -66,6 +66,9 @@ extern "C" {
                                       start outside [0, gamma]. Fatal for the sequence.                          */
 #define SV_FLAG_EMPTY_RESIDUAL 4u  /* the residual had zero mass and the draw used p instead. Informational.      */
 #define SV_FLAG_Q_ZERO         8u  /* q was exactly 0 at a verified draft (ratio 0, rejected). Informational.     */
+#define SV_FLAG_INTERNAL      16u  /* a hand-off between the workgroups of the call failed its check or timed out
+                                      (workspace shared by concurrent calls, or overwritten during the call): the
+                                      sequence was not verified (n_accepted = -1, out_token = -1). Fatal.         */
 
 /* ---- limits ------------------------------------------------------------------------------------------------- */
 #define SV_MAX_GAMMA 1024        /* drafted positions per sequence                                                */
@@ -75,29 +78,19 @@ extern "C" {
  * Bytes of device workspace a call of `kind` needs for B sequences of gamma drafts over V_or_k (V for dense,
  * one-hot and greedy, the p-support size kp for sparse). Depends only on these arguments. Returns 0 when no workspace is
  * needed and (size_t)-1 for arguments the calls would reject. The workspace holds the call's work-queue counters
- * and scratch records. It must be zero-filled before its first use (for example allocated with torch.zeros or
- * cleared with hipMemset once); every call leaves its counters at zero again, so the same workspace serves any
- * number of later calls of any shape it is large enough for without being cleared again. The counters' positions
- * depend on the shape: when a workspace comes with a different shape than on its previous call, the call first
- * clears the counter region of its own layout with one extra small kernel on the same stream. Apart from the
- * counters its contents are meaningless after a call. It must not be shared by calls that may run concurrently.
+ * and scratch records; its first 256 bytes are a header naming the layout of those counters. Its initial contents
+ * do not matter: the first workgroup of every call compares the header with the call's layout and, when they
+ * differ (first use, another kind or shape of call, or an earlier call that stopped early), zeroes the counters
+ * inside the same launch before any other workgroup uses them. Every call leaves its counters at zero, so the same
+ * workspace serves any number of later calls of any kind and shape it is large enough for. Apart from the header
+ * and the counters its contents are meaningless after a call. It must not be shared by calls that may run
+ * concurrently (they would race on the counters; a sequence whose hand-off then fails its checks is flagged
+ * SV_FLAG_INTERNAL).
  */
 size_t sv_workspace_bytes(int kind, int64_t B, int32_t gamma, int64_t V_or_k);
 
 /* Static text for a status code. */
 const char* sv_status_string(int status);
-
-/*
- * Profiling hook (no counterpart on the pages; it lets a caller time the verifier's kernel on its own). When both
- * events are non-NULL, the next sv_verify_dense, sv_verify_onehot_draft, sv_verify_greedy, sv_confidence_commit or
- * sv_build_support call made on this host
- * thread records `start_event` when its kernel starts and `stop_event` when it ends (from the dispatch itself), on
- * that call's stream, and then forgets them; hipEventElapsedTime(start, stop) is that kernel's duration. The events
- * (hipEvent_t) are created and owned by the caller. Passing two NULLs clears a pending request. Returns SV_OK, or
- * SV_ERR_NULL when exactly one event is NULL. The request is per host thread, so concurrent callers on other
- * threads are unaffected.
- */
-int sv_profile_next_stats(void* start_event, void* stop_event);
 
 /*
  * Dense verification: p and q from full logit rows.
@@ -204,9 +197,8 @@ int sv_verify_sparse(const int32_t* p_ids, const float* p_probs,
  * count        [rows] int32 or NULL: kept slots (1 .. k).
  * flags        [rows] uint32 or NULL: SV_FLAG_NONFINITE for a row with a NaN or +inf logit, or all -inf; such a
  *              row gets ids -1, probs NaN, count 0 (so a sparse verify of it flags the sequence). 0 otherwise.
- * workspace    >= sv_support_workspace_bytes(rows, V, k) bytes, 256-byte aligned, zero-filled before its first
- *              use (the same contract as sv_workspace_bytes; a workspace may alternate between this call and the
- *              verify calls).
+ * workspace    >= sv_support_workspace_bytes(rows, V, k) bytes, 256-byte aligned, any initial contents (the same
+ *              contract as sv_workspace_bytes; a workspace may alternate between this call and the verify calls).
  */
 size_t sv_support_workspace_bytes(int64_t rows, int64_t V, int32_t k);
 int sv_build_support(const void* logits, int64_t ld, int dtype, int64_t rows, int64_t V,
@@ -242,7 +234,7 @@ int sv_build_support(const void* logits, int64_t ld, int dtype, int64_t rows, in
  *                checked slot makes the sequence fail: n = -1, out_token = -1, accept 0, start unchanged; a bad bonus
  *                row only sets the flag and leaves out_token = -1.
  * workspace      >= sv_workspace_bytes(SV_KIND_GREEDY, B, gamma, V) bytes of device memory, 256-byte aligned,
- *                zero-filled before its first use (same contract as the other calls).
+ *                any initial contents (same contract as the other calls).
  * Errors: SV_ERR_NULL, SV_ERR_DTYPE, SV_ERR_SHAPE, SV_ERR_ARG (bonus), SV_ERR_ALIGN, SV_ERR_WORKSPACE, SV_ERR_HIP,
  * all returned before anything is launched except SV_ERR_HIP.
  */
@@ -273,8 +265,8 @@ int sv_verify_greedy(const void* target_logits, int64_t t_seq, int64_t t_row,
  * n_commit    [B] int32 (required): committed slots (0 when none is masked), -1 for a fault.
  * flags       [B] uint32 or NULL: SV_FLAG_NONFINITE for a NaN or +inf logit, or a row all -inf, in a masked slot;
  *             such a block commits nothing (token -1, confidence NaN).
- * workspace   >= sv_workspace_bytes(SV_KIND_GREEDY, B, W, V) bytes, 256-byte aligned, zero-filled before its first
- *             use (same contract as the other calls; it may alternate with sv_verify_greedy and the others).
+ * workspace   >= sv_workspace_bytes(SV_KIND_GREEDY, B, W, V) bytes, 256-byte aligned, any initial contents (same
+ *             contract as the other calls; it may alternate with sv_verify_greedy and the others).
  * Errors: SV_ERR_NULL, SV_ERR_DTYPE, SV_ERR_SHAPE, SV_ERR_ARG, SV_ERR_ALIGN, SV_ERR_WORKSPACE, SV_ERR_HIP.
  */
 int sv_confidence_commit(const void* logits, int64_t l_seq, int64_t l_row, int dtype, int64_t B, int32_t W,

@@ -48,17 +48,6 @@ int check_grid(const sv::DensePlan& p) {
   return SV_OK;
 }
 
-// Events for the next dense, one-hot or support call on this host thread (see sv_profile_next_stats).
-thread_local void* t_ev_start = nullptr;
-thread_local void* t_ev_stop = nullptr;
-
-template <typename Args>
-void take_events(Args& a) {
-  a.ev_start = t_ev_start;
-  a.ev_stop = t_ev_stop;
-  t_ev_start = t_ev_stop = nullptr;
-}
-
 int check_workspace(void* ws, size_t bytes, size_t need) {
   if (need == 0) return SV_OK;
   if (!ws) return SV_ERR_WORKSPACE;
@@ -88,13 +77,6 @@ size_t sv_workspace_bytes(int kind, int64_t B, int32_t gamma, int64_t V_or_k) {
     default:
       return bad;
   }
-}
-
-int sv_profile_next_stats(void* start_event, void* stop_event) {
-  if ((start_event == nullptr) != (stop_event == nullptr)) return SV_ERR_NULL;
-  t_ev_start = start_event;
-  t_ev_stop = stop_event;
-  return SV_OK;
 }
 
 const char* sv_status_string(int status) {
@@ -138,7 +120,6 @@ int sv_verify_dense(const void* target_logits, int64_t t_seq, int64_t t_row,
   sv::DenseArgs a{target_logits, t_seq, t_row, draft_logits, d_seq, d_row, dtype, draft_ids, u_accept, u_sample,
                   temperature, bonus, start, order, accept, n_accepted, out_token, p_draft, q_draft, flags,
                   static_cast<char*>(workspace)};
-  take_events(a);
   return sv::launch_dense(plan, a, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
@@ -161,7 +142,6 @@ int sv_verify_onehot_draft(const void* target_logits, int64_t t_seq, int64_t t_r
   sv::DenseArgs a{target_logits, t_seq, t_row, nullptr, 0, 0, dtype, draft_ids, u_accept, u_sample,
                   temperature, bonus, start, order, accept, n_accepted, out_token, p_draft, nullptr, flags,
                   static_cast<char*>(workspace)};
-  take_events(a);
   return sv::launch_dense(plan, a, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
@@ -218,7 +198,6 @@ int sv_build_support(const void* logits, int64_t ld, int dtype, int64_t rows, in
   if (st != SV_OK) return st;
   sv::SupportArgs a{logits, ld, dtype, temperature, top_p, renorm, ids, probs, count, flags,
                     static_cast<char*>(workspace)};
-  take_events(a);
   return sv::launch_support(plan, a, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
@@ -245,7 +224,6 @@ int sv_verify_greedy(const void* target_logits, int64_t t_seq, int64_t t_row,
   if (st != SV_OK) return st;
   sv::GreedyArgs a{target_logits, t_seq, t_row, dtype, bonus, draft_ids, start, order, accept, n_accepted, out_token,
                    flags, static_cast<char*>(workspace)};
-  take_events(a);
   return sv::launch_greedy(plan, a, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
@@ -274,7 +252,6 @@ int sv_confidence_commit(const void* logits, int64_t l_seq, int64_t l_row, int d
   a.tau = tau;
   a.commit = commit;
   a.conf = confidence;
-  take_events(a);
   return sv::launch_greedy(plan, a, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 

@@ -23,7 +23,6 @@
 // The float64 draw exists because a token boundary of the residual CDF often lies within 1e-7 of t at these
 // vocabulary sizes; float32 sums would pick a neighbouring token far more often than the float64 reference does.
 
-#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -31,34 +30,21 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
-#include <mutex>
-#include <unordered_map>
 
 #include "sv.h"
 #include "sv_device.h"
 #include "sv_internal.h"
+#include "sv_wshdr.h"
 
 namespace sv {
 namespace {
 
 constexpr int kStatsBlock = 256;
-#ifndef SV_UNROLL
-#define SV_UNROLL 4
-#endif
-constexpr int kUnroll = SV_UNROLL;   // 16-byte vectors per thread per group
-#ifndef SV_STATS_NT
-#define SV_STATS_NT 1
-#endif
-constexpr bool kNonTemporal = SV_STATS_NT != 0;   // streaming loads that bypass cache retention
-#ifndef SV_WPE
-#define SV_WPE 4
-#endif
-constexpr int kWpe = SV_WPE;        // waves per SIMD the kernel is compiled for
+constexpr int kUnroll = 4;          // 16-byte vectors per thread per group
+constexpr bool kNonTemporal = true; // streaming loads that bypass cache retention
+constexpr int kWpe = 4;             // waves per SIMD the kernel is compiled for
 constexpr int kDrawBlock = 256;     // threads per workgroup, both kinds of item
-#ifndef SV_ITEM_BYTES
-#define SV_ITEM_BYTES 1048576
-#endif
-constexpr int64_t kItemBytes = SV_ITEM_BYTES;   // target bytes of logits per statistics item
+constexpr int64_t kItemBytes = 1048576;   // target bytes of logits per statistics item
 // Draw task sizes, in chunks. Most sequences take tasks of kTaskChunks, doubled (up to kTaskChunksMax) while the launch
 // would hold more than kTasksPerSlot tasks per resident workgroup (a task costs ~4 us of hand-off and set-up besides
 // its float64 work); the last sequences, whose draws end the launch, take tasks of kTailChunks: as many sequences as
@@ -67,29 +53,14 @@ constexpr int64_t kTaskChunks = 16;
 constexpr int64_t kTaskChunksMax = 64;
 constexpr int64_t kTasksPerSlot = 2;
 constexpr int64_t kTailChunks = 8;
-#ifndef SV_TAIL_SLOTS
-#define SV_TAIL_SLOTS 3
-#endif
-constexpr int64_t kTailSlots = SV_TAIL_SLOTS;
-#ifndef SV_SCAN_LAG_ROUNDS
-#define SV_SCAN_LAG_ROUNDS 1
-#endif
-constexpr int kScanLagRounds = SV_SCAN_LAG_ROUNDS;  // resident rounds of statistics items between a sequence's
-                                                    // statistics and its scan
-#ifndef SV_DRAW_SLACK_PCT
-#define SV_DRAW_SLACK_PCT 25
-#endif
-#ifndef SV_DRAW_SLACK_MAX
-#define SV_DRAW_SLACK_MAX 256
-#endif
-constexpr int64_t kDrawSlackPct = SV_DRAW_SLACK_PCT;  // draw slots beyond the draw tasks, in percent of them ...
-constexpr int64_t kDrawSlackMax = SV_DRAW_SLACK_MAX;  // ... and at most this many
-constexpr int kCtrStride = 64;                  // int32 slots between per-sequence counters (one 256-byte line each)
-#ifndef SV_SLEEP
-#define SV_SLEEP 16
-#endif
-constexpr int32_t kSpinCap = 1 << 20;           // polls before a draw task stops waiting for its job (never reached
-                                                // when the hardware dispatches as documented)
+constexpr int64_t kTailSlots = 3;
+constexpr int kScanLagRounds = 1;   // resident rounds of statistics items between a sequence's statistics and its scan
+constexpr int64_t kDrawSlackPct = 25;   // draw slots beyond the draw tasks, in percent of them ...
+constexpr int64_t kDrawSlackMax = 256;  // ... and at most this many
+constexpr int kCtrStride = 64;          // int32 slots between per-sequence counters (one 256-byte line each)
+constexpr int kSleep = 16;              // s_sleep units between polls of a wait
+constexpr int32_t kSpinCap = kWsSpinCap;   // polls before a wait gives up (never reached when the hardware
+                                           // dispatches workgroups in index order, as documented)
 
 struct alignas(16) Partial1 {
   float m;        // exact max of the segment's logits (raw, before the temperature)
@@ -147,6 +118,9 @@ struct DenseParams {
   int32_t* recN;             // per (b, chunk)
   double2* recU;             // per (b, chunk, kAmbMax)
   double* masses;            // per (b, chunk): chunk masses, written by the pick when the chunks exceed one tile
+  char* ws;                  // the workspace: its header (the control layout at zero) leads the control words
+  uint64_t sig;              // this call's control layout
+  int64_t ctl_end;           // control words fill [kWsHeaderBytes, ctl_end)
 };
 
 // The parameters are read in place from the kernel-argument segment (constant address space) by every function,
@@ -930,6 +904,7 @@ __shared__ PickShared s_pick;     // at file scope: reached with LDS instruction
 __device__ __forceinline__ void finish(DP& prm, int64_t b, const Job& job, int32_t tok, uint32_t extra) {
   prm.token[b] = tok;
   if (prm.flags) prm.flags[b] = job.flags | extra;
+  if (job.flags & SV_FLAG_INTERNAL) prm.n_acc[b] = -1;
 }
 
 // The exact search inside chunk cstar by the whole workgroup (thread tid holds kPT consecutive elements): the first
@@ -1317,7 +1292,7 @@ __device__ __forceinline__ bool ld_job_sealed(const uint32_t* slot, Job& j) {
     const bool sealed = (__builtin_amdgcn_readlane(w, 3) & __builtin_amdgcn_readlane(w, 7) &
                          __builtin_amdgcn_readlane(w, 11) & __builtin_amdgcn_readlane(w, 15)) != 0u;
     if (sealed || ++polls >= kSpinCap) break;
-    __builtin_amdgcn_s_sleep(SV_SLEEP);
+    __builtin_amdgcn_s_sleep(kSleep);
   }
   uint32_t* d = reinterpret_cast<uint32_t*>(&j);
 #pragma unroll
@@ -1369,18 +1344,31 @@ __device__ __forceinline__ void ctr_inc(int32_t* p) {
 }
 
 // Waits (thread 0 polls, the others hold at the barrier) until the counter reaches `target`. Returns false when it
-// gave up after kSpinCap polls, which only happens if the hardware broke the dispatch order.
-__device__ __forceinline__ bool wait_count(const int32_t* ctr, int32_t target) {
+// gave up after kSpinCap polls, which only happens if the hardware broke the dispatch order; the workspace is then
+// marked so that the next call clears its control words.
+// With sig != 0 the header is confirmed first (the counter is a control word).
+__device__ __forceinline__ bool wait_count(const int32_t* ctr, int32_t target, char* ws, uint64_t sig = 0) {
   if (threadIdx.x == 0) {
     int32_t polls = 0;
-    while (ld_ctr(ctr) < target && polls < kSpinCap) {
-      __builtin_amdgcn_s_sleep(SV_SLEEP);
+    if (sig != 0 && !ws_seen_clean(ws, sig) && !ws_ready(ws, sig)) polls = kSpinCap;
+    while (polls < kSpinCap && ld_ctr(ctr) < target) {
+      __builtin_amdgcn_s_sleep(kSleep);
       ++polls;
     }
     s_flag = polls < kSpinCap;
+    if (!s_flag) ws_mark_dirty(ws);
   }
   __syncthreads();
   return s_flag != 0;
+}
+
+// The job of a sequence that could not be verified because a hand-off inside the launch failed: nothing is drawn.
+__device__ __forceinline__ Job internal_fault_job() {
+  Job j{};
+  j.kind = JOB_NONE;
+  j.flags = SV_FLAG_INTERNAL;
+  j.new_start = -1;
+  return j;
 }
 
 // Draw task `task` of sequence b, once its job is published: the float64 masses of the task's chunks of the draw
@@ -1457,10 +1445,11 @@ __device__ __forceinline__ bool draw_task(DP& prm_arg, int64_t b, int task, cons
   if (tid == 0) ctr_inc(done);
   const int32_t nt_b = task_shape(prm, b).ntask;
   if (task != nt_b - 1) return false;
-  if (!wait_count(done, nt_b)) {                    // gave up: report the sequence as not verified
+  if (!wait_count(done, nt_b, prm.ws)) {            // gave up: report the sequence as not verified
     if (tid == 0) {
       prm.token[b] = -1;
-      if (prm.flags) prm.flags[b] = SV_FLAG_NONFINITE | SV_FLAG_ID_RANGE;
+      prm.n_acc[b] = -1;
+      if (prm.flags) prm.flags[b] = SV_FLAG_INTERNAL;
     }
     return false;
   }
@@ -1486,27 +1475,31 @@ __global__ __launch_bounds__(kDrawBlock) __attribute__((amdgpu_waves_per_eu(kWpe
   const ItemRef it = decode_item(blockIdx.x, uint32_t(prm.B), uint32_t(prm.n1), uint32_t(prm.lag1));
   const int64_t b = it.b;
   int32_t* ready = prm.ready + b * kCtrStride;
+  // workgroup 0 (a statistics item) makes sure the control words are at zero for this call's layout; every other
+  // workgroup sees the header name this layout as clean before it touches a control word
+  if (blockIdx.x == 0) ws_claim(prm.ws, prm.sig, size_t(prm.ctl_end), &s_flag);
   if (it.kind == ITEM_STATS) {
+    const bool seen = blockIdx.x == 0 || ws_seen_clean(prm.ws, prm.sig);   // read while the segment streams
     stats_item<T, kStatsBlock, kUnroll, kNonTemporal>(prm, b, it.sub, sh_f, sh_d);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0) ctr_inc(ready);
+    if (tid == 0) {
+      if (seen || ws_ready(prm.ws, prm.sig)) ctr_inc(ready);
+      else ws_mark_dirty(prm.ws);                    // not counted: the scan gives up and flags the sequence
+    }
     return;
   }
   if (it.kind == ITEM_SCAN) {
     // the scan and the pick are short serial chains on the critical path: their waves get issue priority over the
     // streaming and float64 waves that share their SIMDs
     __builtin_amdgcn_s_setprio(3);
-    const bool ok = wait_count(ready, prm.n1);
+    const bool ok = wait_count(ready, prm.n1, prm.ws, prm.sig);
     if (wave == 0) {
       Job j;
       if (ok) {
         j = seq_scan(prm, b, true, seen);
       } else {                                       // gave up waiting: report the sequence as not verified
-        j = Job{};
-        j.kind = JOB_NONE;
-        j.flags = SV_FLAG_NONFINITE | SV_FLAG_ID_RANGE;
-        j.new_start = -1;
+        j = internal_fault_job();
       }
       st_job(job_slot(prm, b), j);                   // published: the draw tasks take it once sealed
     }
@@ -1523,19 +1516,25 @@ __global__ __launch_bounds__(kDrawBlock) __attribute__((amdgpu_waves_per_eu(kWpe
   if (wave == 0) {
     int32_t tk = 0;
     if (lane == 0) {
-      tk = __hip_atomic_fetch_add(prm.tickets, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      // the slot that takes the last ticket of this call returns the counter to zero for the next call (every other
-      // slot has taken its ticket already)
-      if (tk == prm.nslots - 1) st_dev(prm.tickets, 0);
+      if (ws_seen_clean(prm.ws, prm.sig) || ws_ready(prm.ws, prm.sig)) {
+        tk = __hip_atomic_fetch_add(prm.tickets, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // the slot that takes the last ticket of this call returns the counter to zero for the next call (every
+        // other slot has taken its ticket already)
+        if (tk == prm.nslots - 1) st_dev(prm.tickets, 0);
+      } else {
+        tk = -1;                                     // no ticket: the sequences' last tasks give up and flag them
+        ws_mark_dirty(prm.ws);
+      }
     }
     tk = __builtin_amdgcn_readfirstlane(tk);
     Job j{};
     if (tk >= 0 && tk < ntot) {
-      if (!ld_job_sealed(job_slot(prm, seq_of(tk)), j)) {       // gave up waiting: report it as not verified
-        j = Job{};
-        j.kind = JOB_NONE;
-        j.flags = SV_FLAG_NONFINITE | SV_FLAG_ID_RANGE;
-        j.new_start = -1;
+      const bool sealed = ld_job_sealed(job_slot(prm, seq_of(tk)), j);
+      // every field that becomes an address or an index is checked first: a job that gave up waiting or does not
+      // fit this call is not drawn from, and its sequence is reported as not verified
+      if (!sealed || !job_valid(j, prm.G, prm.V, prm.bonus, prm.dft != nullptr)) {
+        if (!sealed && lane == 0) ws_mark_dirty(prm.ws);
+        j = internal_fault_job();
       }
     }
     if (lane == 0) { s_draw.job = j; s_draw.ticket = tk; }
@@ -1572,25 +1571,9 @@ __global__ __launch_bounds__(kDrawBlock) __attribute__((amdgpu_waves_per_eu(kWpe
 }
 
 
-// Zeroes n 16-byte words (vector stores).
-__global__ __launch_bounds__(256) void k_clear(uint4* p, int64_t n) {
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
-    p[i] = make_uint4(0u, 0u, 0u, 0u);
-}
-
 template <typename T>
 hipError_t launch_typed(const DensePlan& plan, const DenseArgs& a, hipStream_t stream) {
   char* ws = a.ws;
-  // the control words (per-sequence counters, the draw ticket, the job slots) fill [0, off_part1) at positions that
-  // depend on the shape; the signature covers the offsets that place them
-  uint64_t sig = kLayoutDense;
-  for (uint64_t v : {uint64_t(plan.B), uint64_t(plan.off_done), uint64_t(plan.off_tickets), uint64_t(plan.off_jobs),
-                     uint64_t(plan.off_part1)})
-    sig = layout_mix(sig, v);
-  if (workspace_layout_changed(ws, sig)) {
-    const hipError_t e = clear_control(ws, plan.off_part1, stream);
-    if (e != hipSuccess) return e;
-  }
   const double T_ = double(a.temperature);
   const float c = float(1.4426950408889634074 / T_);          // log2(e) / T
   DenseParams dp{};
@@ -1622,14 +1605,13 @@ hipError_t launch_typed(const DensePlan& plan, const DenseArgs& a, hipStream_t s
   dp.recN = reinterpret_cast<int32_t*>(ws + plan.off_recN);
   dp.recU = reinterpret_cast<double2*>(ws + plan.off_recU);
   dp.masses = reinterpret_cast<double*>(ws + plan.off_masses);
+  // the control words (per-sequence counters, the draw ticket, the job slots) sit at positions set by B alone
+  dp.ws = ws;
+  dp.sig = ws_signature(kLayoutDense, uint64_t(plan.B));
+  dp.ctl_end = int64_t(plan.off_part1);
   const unsigned grid = unsigned(dp.n_items);
   auto kern = k_verify<T>;
-  if (a.ev_start) {      // events taken from the dispatch packet itself: no marker packets around the kernel
-    hipExtLaunchKernelGGL(kern, dim3(grid), dim3(kDrawBlock), 0, stream, static_cast<hipEvent_t>(a.ev_start),
-                          static_cast<hipEvent_t>(a.ev_stop), 0, dp);
-  } else {
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kDrawBlock), 0, stream, dp);
-  }
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kDrawBlock), 0, stream, dp);
   return hipGetLastError();
 }
 
@@ -1637,38 +1619,12 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace
 
-// A call's control words (counters that every call returns to zero) sit at positions that depend on its shape and
-// kind, and a call returns them to zero only in its own layout. The library remembers, per workspace pointer, the
-// layout signature of the last call that used it; when a workspace comes with another signature (or for the first
-// time), the caller clears the new layout's control region first (clear_control), on the same stream.
-bool workspace_layout_changed(const void* ws, uint64_t sig) {
-  static std::mutex mu;
-  static std::unordered_map<const void*, uint64_t> last;
-  std::lock_guard<std::mutex> lock(mu);
-  auto it = last.find(ws);
-  const bool changed = it == last.end() || it->second != sig;
-  last[ws] = sig;
-  return changed;
-}
-
-hipError_t clear_control(char* ws, size_t bytes, hipStream_t stream) {
-  const int64_t n16 = int64_t(bytes / 16);                       // control regions are multiples of 256 bytes
-  if (n16 <= 0) return hipSuccess;
-  const unsigned g = unsigned(std::min<int64_t>((n16 + 255) / 256, 1024));
-  hipLaunchKernelGGL(k_clear, dim3(g), dim3(256), 0, stream, reinterpret_cast<uint4*>(ws), n16);
-  return hipGetLastError();
-}
-
 // Resident workgroups of the kernel on the current device (compute units x workgroups per compute unit).
 int resident_workgroups() {
-  static int cached[64] = {};
   int dev = 0, ncu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 1024;
-  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
   if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0) ncu = 256;
-  const int r = ncu * kWpe;          // kWpe 4-wave workgroups per compute unit at kWpe waves per SIMD
-  if (dev >= 0 && dev < 64) cached[dev] = r;
-  return r;
+  return ncu * kWpe;                 // kWpe 4-wave workgroups per compute unit at kWpe waves per SIMD
 }
 
 DensePlan make_dense_plan(int64_t B, int32_t G, int64_t V, int32_t ntens, int dtype, int64_t resident) {
@@ -1695,13 +1651,10 @@ DensePlan make_dense_plan(int64_t B, int32_t G, int64_t V, int32_t ntens, int dt
   if (ntask2 < ntask) ntask2 = ntask;
   p.ntask2 = int32_t(ntask2);
   p.tailq = std::max<int64_t>(1, std::min<int64_t>(B, (kTailSlots * R + p.nch - 1) / p.nch));
-#ifdef SV_TAILQ
-  p.tailq = std::max<int64_t>(1, std::min<int64_t>(B, SV_TAILQ));
-#endif
   p.ntot = (B - p.tailq) * ntask + p.tailq * ntask2;
   // draw slots: the tasks plus kDrawSlackPct percent more, so that a faster XCD can take more than its share
   p.nslots = p.ntot + std::min<int64_t>((p.ntot * kDrawSlackPct + 99) / 100, kDrawSlackMax);
-  size_t off = 0;
+  size_t off = kWsHeaderBytes;
   p.off_ready = off; off = align_up(off + size_t(B) * kCtrStride * sizeof(int32_t), 256);
   p.off_done = off;  off = align_up(off + size_t(B) * kCtrStride * sizeof(int32_t), 256);
   p.off_tickets = off; off = align_up(off + kCtrStride * sizeof(int32_t), 256);

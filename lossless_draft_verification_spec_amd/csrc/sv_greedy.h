@@ -11,12 +11,9 @@
 
 namespace sv {
 
-constexpr uint64_t kLayoutGreedy = 0x2325cbf29ce48422ull;   // workspace layout kind (see workspace_layout_changed)
+constexpr uint64_t kLayoutGreedy = 0x2325cbf29ce48422ull;   // workspace control layout kind (see sv_wshdr.h)
 constexpr int64_t kGreedyMaxSeg = 64;          // segments per row at most (longer rows get longer segments)
-#ifndef SV_GR_TARGET_ITEMS
-#define SV_GR_TARGET_ITEMS 1024
-#endif
-constexpr int64_t kGreedyTargetItems = SV_GR_TARGET_ITEMS;   // workgroups a launch aims at (about the resident count)
+constexpr int64_t kGreedyTargetItems = 1024;   // workgroups a launch aims at (about the resident count)
 
 struct GreedyPlan {
   int64_t B = 0;
@@ -26,7 +23,7 @@ struct GreedyPlan {
   int64_t seg_elems = 0;   // logits per segment (a multiple of 256 vectors)
   int32_t S = 1;           // segments per row
   int64_t items = 0;       // workgroups of the launch: B * R * S
-  size_t ctr_bytes = 0;    // the control region [0, ctr_bytes): int32 per sequence, returned to 0 by its merge
+  size_t ctr_bytes = 0;    // header + control region [0, ctr_bytes): int32 per sequence, returned to 0 by its merge
   size_t off_part = 0;     // uint64 key per (sequence, row, segment)
   size_t off_part2 = 0;    // float2 (segment maximum, sum of exp(z - maximum)) per (sequence, row, segment)
   size_t total = 0;
@@ -46,8 +43,6 @@ struct GreedyArgs {
   // confidence-threshold commit: gamma = W slots, bonus 0, n_acc = committed count, token [B][W]
   bool conf_mode = false;
   const uint8_t* masked = nullptr; float tau = 0.f; uint8_t* commit = nullptr; float* conf = nullptr;
-  void* ev_start = nullptr;   // optional hipEvent_t pair recorded from the kernel's dispatch
-  void* ev_stop = nullptr;
 };
 
 hipError_t launch_greedy(const GreedyPlan& plan, const GreedyArgs& a, hipStream_t stream);

@@ -23,7 +23,6 @@
 //  * Rows of slots before `start` are not read (their workgroups only count themselves in); the bonus row is read
 //    with the others whenever the sequence is live, and used only when every verified draft matches.
 
-#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -34,16 +33,14 @@
 #include "sv_device.h"
 #include "sv_greedy.h"
 #include "sv_internal.h"
+#include "sv_wshdr.h"
 
 namespace sv {
 namespace {
 
 constexpr int kGrBlock = 256;
 constexpr int kGrWaves = kGrBlock / 64;
-#ifndef SV_GR_U
-#define SV_GR_U 4
-#endif
-constexpr int kGrU = SV_GR_U;                               // 16-byte vectors per thread per chunk
+constexpr int kGrU = 4;                                     // 16-byte vectors per thread per chunk
 constexpr int64_t kGrChunkVec = int64_t(kGrBlock) * kGrU;   // vectors per chunk (16 KB)
 constexpr uint64_t kFaultKey = ~0ull;                       // a segment holding a NaN or +inf
 constexpr uint32_t kOrdNegInf = 0x007FFFFFu;                // ord_bits(-inf)
@@ -63,6 +60,9 @@ struct GreedyParams {
   int32_t* n_acc;
   int32_t* token;
   uint32_t* flags;
+  char* ws;                    // the workspace; its header names the control layout at zero
+  uint64_t sig;                // this call's control layout
+  int64_t ctl_end;             // control words (the counters) fill [kWsHeaderBytes, ctl_end)
   int32_t* ctr;                // per sequence: workgroups finished
   uint64_t* part;              // per (sequence, row, segment): the segment's key
   // confidence-threshold commit (CONF kernels): W = G slots, no bonus row
@@ -440,6 +440,9 @@ __global__ __launch_bounds__(kGrBlock) void k_greedy(GreedyParams p) {
   const int64_t b = br / p.R;
   const int G = p.G;
   const int32_t st = (!CONF && p.start) ? p.start[b] : 0;
+  // workgroup 0 makes sure the counters are at zero for this call's layout; the others confirm it before counting
+  if (item == 0) ws_claim(p.ws, p.sig, size_t(p.ctl_end), &sh.last);
+  const bool seen = item == 0 || ws_seen_clean(p.ws, p.sig);
 
   // Is this row verified (or the bonus row of a live sequence; CONF: a masked slot)?
   bool read;
@@ -484,7 +487,12 @@ __global__ __launch_bounds__(kGrBlock) void k_greedy(GreedyParams p) {
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
-    sh.last = ctr_add(p.ctr + b) == p.R * p.S - 1;
+    if (seen || ws_ready(p.ws, p.sig)) {
+      sh.last = ctr_add(p.ctr + b) == p.R * p.S - 1;
+    } else {                                  // never counted: the sequence is not resolved in this call
+      ws_mark_dirty(p.ws);
+      sh.last = 0;
+    }
   }
   __syncthreads();
   if (!sh.last) return;
@@ -507,10 +515,10 @@ GreedyPlan make_greedy_plan(int64_t B, int32_t G, int64_t V, int32_t bonus, int 
   pl.seg_elems = ((V + S - 1) / S + gran - 1) / gran * gran;
   pl.S = int32_t((V + pl.seg_elems - 1) / pl.seg_elems);
   pl.items = rows * pl.S;
-  pl.ctr_bytes = size_t((B * 4 + 255) / 256 * 256);
+  pl.ctr_bytes = kWsHeaderBytes + size_t((B * 4 + 255) / 256 * 256);
   pl.off_part = pl.ctr_bytes;
-  pl.off_part2 = pl.off_part + size_t(pl.items) * 8;
-  pl.total = pl.off_part2 + size_t(pl.items) * 8;
+  pl.off_part2 = (pl.off_part + size_t(pl.items) * 8 + 255) / 256 * 256;
+  pl.total = (pl.off_part2 + size_t(pl.items) * 8 + 255) / 256 * 256;
   return pl;
 }
 
@@ -522,29 +530,23 @@ size_t greedy_workspace_bytes(int64_t B, int32_t G, int64_t V) {
 }
 
 hipError_t launch_greedy(const GreedyPlan& plan, const GreedyArgs& a, hipStream_t stream) {
-  if (workspace_layout_changed(a.ws, layout_mix(kLayoutGreedy, uint64_t(plan.B)))) {
-    const hipError_t e = clear_control(a.ws, plan.ctr_bytes, stream);
-    if (e != hipSuccess) return e;
-  }
   GreedyParams p{};
+  p.ws = a.ws;
+  p.sig = ws_signature(kLayoutGreedy, uint64_t(plan.B));
+  p.ctl_end = int64_t(plan.ctr_bytes);
   p.tgt = a.tgt; p.t_seq = a.t_seq; p.t_row = a.t_row;
   p.V = plan.V; p.seg_elems = plan.seg_elems;
   p.G = plan.G; p.R = plan.R; p.S = plan.S; p.bonus = a.bonus;
   p.ids = a.ids; p.start = a.start; p.order = a.order;
   p.accept = a.accept; p.n_acc = a.n_acc; p.token = a.token; p.flags = a.flags;
   p.masked = a.masked; p.tau = double(a.tau); p.commit = a.commit; p.conf = a.conf;
-  p.ctr = reinterpret_cast<int32_t*>(a.ws);
+  p.ctr = reinterpret_cast<int32_t*>(a.ws + kWsHeaderBytes);
   p.part = reinterpret_cast<uint64_t*>(a.ws + plan.off_part);
   p.part2 = reinterpret_cast<float2*>(a.ws + plan.off_part2);
   auto kern = a.conf_mode ? (a.dtype == SV_BF16 ? k_greedy<uint16_t, true> : k_greedy<float, true>)
                           : (a.dtype == SV_BF16 ? k_greedy<uint16_t, false> : k_greedy<float, false>);
   const unsigned grid = unsigned(plan.items);
-  if (a.ev_start) {
-    hipExtLaunchKernelGGL(kern, dim3(grid), dim3(kGrBlock), 0, stream, static_cast<hipEvent_t>(a.ev_start),
-                          static_cast<hipEvent_t>(a.ev_stop), 0, p);
-  } else {
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kGrBlock), 0, stream, p);
-  }
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kGrBlock), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -73,12 +73,11 @@ struct DensePlan {
 DensePlan make_dense_plan(int64_t B, int32_t G, int64_t V, int32_t ntens, int dtype, int64_t resident);
 int resident_workgroups();
 
-// Workspace layout bookkeeping shared by the calls that keep control words in a workspace (see sv_dense.hip).
+// Kinds of control layout kept in a workspace (see sv_wshdr.h): the workspace header names one of them, with the
+// size that places its control words.
 constexpr uint64_t kLayoutDense = 0xcbf29ce484222325ull;     // FNV-1a offset basis, one per kind of layout
 constexpr uint64_t kLayoutSupport = 0x84222325cbf29ce4ull;
 inline uint64_t layout_mix(uint64_t sig, uint64_t v) { return (sig ^ v) * 1099511628211ull; }
-bool workspace_layout_changed(const void* ws, uint64_t sig);
-hipError_t clear_control(char* ws, size_t bytes, hipStream_t stream);   // zeroes [ws, ws + bytes), bytes % 16 == 0
 
 struct DenseArgs {
   const void* tgt; int64_t t_seq, t_row;
@@ -90,8 +89,6 @@ struct DenseArgs {
   uint8_t* accept; int32_t* n_acc; int32_t* token;
   float* p_draft; float* q_draft; uint32_t* flags;
   char* ws;
-  void* ev_start = nullptr;   // optional hipEvent_t recorded around the row-statistics kernel
-  void* ev_stop = nullptr;
 };
 
 hipError_t launch_dense(const DensePlan& plan, const DenseArgs& a, hipStream_t stream);
@@ -116,9 +113,8 @@ struct SupportPlan {
   int32_t nseg = 1;        // segments of each later row
   int32_t nlay = 1;        // segment records per row in the workspace
   int64_t items = 0;       // workgroups of the launch
-  int64_t attach = 0;      // segments of the later rows that ride on whole-row items (0: they are items)
   size_t off_ctr = 0;      // int32 per row (one per 256 bytes): segments finished, returned to 0 by the row's merge
-  size_t ctr_bytes = 0;    // the control region [0, ctr_bytes)
+  size_t ctr_bytes = 0;    // header + control region [0, ctr_bytes)
   size_t off_keys = 0;     // per (row, segment): up to k uint64 keys
   size_t off_part = 0;     // per (row, segment): the segment's statistics
   size_t total = 0;
@@ -133,8 +129,6 @@ struct SupportArgs {
   float temperature; float top_p; int32_t renorm;
   int32_t* ids; float* probs; int32_t* count; uint32_t* flags;
   char* ws;
-  void* ev_start = nullptr;   // optional hipEvent_t pair recorded from the kernel's dispatch
-  void* ev_stop = nullptr;
 };
 
 hipError_t launch_support(const SupportPlan& plan, const SupportArgs& a, hipStream_t stream);

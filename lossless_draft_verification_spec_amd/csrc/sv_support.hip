@@ -25,7 +25,6 @@
 // Bound: HBM. Algorithmic bytes: every logit of every row once (V * s per row, s = 2 bf16, 4 fp32), plus k ids and
 // k probabilities written per row.
 
-#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -35,6 +34,7 @@
 #include "sv.h"
 #include "sv_device.h"
 #include "sv_internal.h"
+#include "sv_wshdr.h"
 
 namespace sv {
 namespace {
@@ -43,21 +43,11 @@ constexpr int kSupBlock = 256;
 constexpr int kSupWaves = kSupBlock / 64;
 constexpr int kWaveCap = 768;                      // candidate keys per wave buffer
 constexpr int kMergeCap = kSupWaves * kWaveCap;    // keys one merge holds (the wave buffers side by side)
-#ifndef SV_SUP_U_BF16
-#define SV_SUP_U_BF16 2
-#endif
-#ifndef SV_SUP_U_F32
-#define SV_SUP_U_F32 4
-#endif
 // 16-byte vectors per thread per load round (two rounds in flight): fewer for bf16, whose 8 elements per vector
 // take more registers in the candidate path.
-template <typename T> constexpr int kRoundVecs = sizeof(T) == 2 ? SV_SUP_U_BF16 : SV_SUP_U_F32;
-#ifndef SV_SUP_ATTACH
-#define SV_SUP_ATTACH 0
-#endif
-// The rows of a last, partial resident round: 1: their segments ride on the last round's whole-row items; 0: they
-// are items of their own, queued before the whole rows.
-constexpr bool kAttachTail = SV_SUP_ATTACH != 0;
+template <typename T> constexpr int kRoundVecs = sizeof(T) == 2 ? 2 : 4;
+// The rows of a last, partial resident round are cut into segments that are items of their own, queued before the
+// whole rows.
 constexpr int kSupCtrStride = 64;                  // int32 slots between row counters (one 256-byte line each)
 constexpr int kMaxSeg = 16;                        // segments per row
 constexpr int64_t kMinSegBytes = 32768;            // smallest segment worth a workgroup
@@ -78,13 +68,14 @@ struct SupportParams {
   int64_t head_rows;  // rows 0 .. head_rows - 1: one item each (the whole row)
   int32_t nseg;       // segments of each later row
   int64_t items;      // items (workgroups) in the launch
-  int64_t attach;     // > 0: the later rows' segments ride on the last `attach` whole-row items; 0: they are items
-                      // of their own, queued first
   int32_t nlay;       // segment records per row in the workspace (>= nseg)
   float c;          // log2(e) / T rounded to float32: the full-row sums
   double T;         // the temperature, widened
   double top_p;     // top_p as received (float32), widened
   int32_t* ids; float* probs; int32_t* count; uint32_t* flags;
+  char* ws;         // the workspace; its header names the control layout at zero
+  uint64_t sig;     // this call's control layout
+  int64_t ctl_end;  // control words (the row counters) fill [kWsHeaderBytes, ctl_end)
   int32_t* ctr;     // per row, kSupCtrStride apart: segments finished in this call
   uint64_t* keys;   // per (row, segment): up to k keys
   SupPartial* part; // per (row, segment)
@@ -598,7 +589,7 @@ __device__ __forceinline__ void finish_row(const SupportParams& p, int64_t row, 
 }
 
 template <typename T, bool SUM>
-__device__ __forceinline__ void support_item(const SupportParams& p, int64_t row, int seg, int nseg) {
+__device__ __forceinline__ void support_item(const SupportParams& p, int64_t row, int seg, int nseg, bool seen) {
   using VT = Vec<T>;
   constexpr int EPV = VT::kEPV;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
@@ -734,7 +725,14 @@ __device__ __forceinline__ void support_item(const SupportParams& p, int64_t row
   __builtin_amdgcn_s_waitcnt(0);                     // this segment's records are complete before it is counted
   __syncthreads();
   int32_t* ctr = p.ctr + row * kSupCtrStride;
-  if (tid == 0) g_sup.flag = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == nseg - 1;
+  if (tid == 0) {
+    if (seen || ws_ready(p.ws, p.sig)) {
+      g_sup.flag = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == nseg - 1;
+    } else {                                         // never counted: the row is not merged in this call
+      ws_mark_dirty(p.ws);
+      g_sup.flag = 0;
+    }
+  }
   __syncthreads();
   if (!g_sup.flag) return;
   // every segment of the row has counted itself: wave 0 reads their statistics, one lane per segment (in parallel)
@@ -746,7 +744,7 @@ __device__ __forceinline__ void support_item(const SupportParams& p, int64_t row
     double sv = 0.0;
     if (lane < nseg) {
       const SupPartial* pp = p.part + item0 + lane;
-      nk = ld_dev(&pp->nk);
+      nk = clamp_count(ld_dev(&pp->nk), k);        // a count read back is never trusted as an extent
       m = ld_dev(&pp->m);
       nn = ld_dev(&pp->nan);
       if (SUM) sv = ld_dev(&pp->s);
@@ -801,19 +799,16 @@ __device__ __forceinline__ void support_item(const SupportParams& p, int64_t row
 template <typename T, bool SUM>
 __global__ __launch_bounds__(kSupBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_support(SupportParams p) {
   const int64_t item = int64_t(blockIdx.x);
-  if (p.attach > 0) {
-    // every item is a whole row; the last `attach` items also take one segment of one of the rows past the head
-    support_item<T, SUM>(p, item, 0, 1);
-    const int64_t j = item - (p.head_rows - p.attach);
-    if (j >= 0) {
-      __syncthreads();                                 // the shared state is free again
-      support_item<T, SUM>(p, p.head_rows + j / p.nseg, int(j % p.nseg), p.nseg);
-    }
+  // workgroup 0 makes sure the row counters are at zero for this call's layout; the others confirm it before
+  // counting (only rows cut into segments count)
+  if (item == 0) ws_claim(p.ws, p.sig, size_t(p.ctl_end), &g_sup.flag);
+  // the segments of the rows past the head first, then the whole rows
+  const int64_t nfirst = p.items - p.head_rows;
+  if (item >= nfirst) {
+    support_item<T, SUM>(p, item - nfirst, 0, 1, true);
   } else {
-    // the segments of the rows past the head first, then the whole rows
-    const int64_t nfirst = p.items - p.head_rows;
-    if (item >= nfirst) support_item<T, SUM>(p, item - nfirst, 0, 1);
-    else support_item<T, SUM>(p, p.head_rows + item / p.nseg, int(item % p.nseg), p.nseg);
+    const bool seen = item == 0 || ws_seen_clean(p.ws, p.sig);   // read while the segment streams
+    support_item<T, SUM>(p, p.head_rows + item / p.nseg, int(item % p.nseg), p.nseg, seen);
   }
 }
 
@@ -835,28 +830,19 @@ SupportPlan make_support_plan(int64_t rows, int64_t V, int32_t k, int dtype, int
   const int32_t nlayout = max_segments(V, 4, k);     // the float32 bound sizes the workspace for both dtypes
   const int32_t ncap = max_segments(V, dtype == SV_BF16 ? 2 : 4, k);
   // Whole rows, one workgroup each, in full resident rounds. The rows of a last, partial round would stream alone at
-  // one workgroup's rate, so they are cut into segments: when there are whole rows, the segments ride on the last
-  // resident round's items (each of those workgroups takes one segment after its row, so that the round's items
-  // end together); otherwise the segments are the items.
+  // one workgroup's rate, so they are cut into segments, items of their own queued before the whole rows.
   const int64_t R = std::max<int64_t>(resident, 1);
   const int64_t tail = rows % R;
   p.head_rows = rows - tail;
   p.nlay = nlayout;
   if (tail == 0) {
     p.nseg = 1;
-    p.attach = 0;
     p.items = rows;
-  } else if (kAttachTail && p.head_rows > 0) {
-    const int64_t last_round = std::min<int64_t>(p.head_rows, R);
-    p.nseg = int32_t(std::min<int64_t>(nlayout, std::max<int64_t>(1, last_round / tail)));
-    p.attach = tail * p.nseg;
-    p.items = p.head_rows;
   } else {
     p.nseg = int32_t(std::min<int64_t>(ncap, std::max<int64_t>(1, R / tail)));
-    p.attach = 0;
     p.items = p.head_rows + tail * p.nseg;
   }
-  size_t off = 0;
+  size_t off = kWsHeaderBytes;
   p.off_ctr = off;  off = align_up(off + size_t(rows) * kSupCtrStride * sizeof(int32_t), 256);
   p.ctr_bytes = off;
   p.off_keys = off; off = align_up(off + size_t(rows) * nlayout * size_t(k) * sizeof(uint64_t), 256);
@@ -867,15 +853,13 @@ SupportPlan make_support_plan(int64_t rows, int64_t V, int32_t k, int dtype, int
 
 hipError_t launch_support(const SupportPlan& plan, const SupportArgs& a, hipStream_t stream) {
   char* ws = a.ws;
-  if (workspace_layout_changed(ws, layout_mix(kLayoutSupport, uint64_t(plan.rows)))) {
-    const hipError_t e = clear_control(ws, plan.ctr_bytes, stream);
-    if (e != hipSuccess) return e;
-  }
   SupportParams p{};
+  p.ws = ws;
+  p.sig = ws_signature(kLayoutSupport, uint64_t(plan.rows));
+  p.ctl_end = int64_t(plan.ctr_bytes);
   p.logits = a.logits; p.ld = a.ld; p.rows = plan.rows; p.V = plan.V;
   p.k = plan.k; p.renorm = a.renorm;
   p.head_rows = plan.head_rows; p.nseg = plan.nseg; p.nlay = plan.nlay; p.items = plan.items;
-  p.attach = plan.attach;
   const double T = double(a.temperature);
   p.c = float(1.4426950408889634074 / T);
   p.T = T;
@@ -887,12 +871,7 @@ hipError_t launch_support(const SupportPlan& plan, const SupportArgs& a, hipStre
   const unsigned grid = unsigned(plan.items);
   auto kern = a.dtype == SV_BF16 ? (a.renorm ? k_support<uint16_t, false> : k_support<uint16_t, true>)
                                  : (a.renorm ? k_support<float, false> : k_support<float, true>);
-  if (a.ev_start) {      // events taken from the dispatch packet itself
-    hipExtLaunchKernelGGL(kern, dim3(grid), dim3(kSupBlock), 0, stream, static_cast<hipEvent_t>(a.ev_start),
-                          static_cast<hipEvent_t>(a.ev_stop), 0, p);
-  } else {
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kSupBlock), 0, stream, p);
-  }
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kSupBlock), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -17,10 +17,10 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsv.so")
 SV_OK = 0
 SV_F32, SV_BF16 = 0, 1
 SV_KIND_DENSE, SV_KIND_ONEHOT, SV_KIND_SPARSE, SV_KIND_GREEDY = 0, 1, 2, 3
-SV_FLAG_NONFINITE, SV_FLAG_ID_RANGE, SV_FLAG_EMPTY_RESIDUAL, SV_FLAG_Q_ZERO = 1, 2, 4, 8
+SV_FLAG_NONFINITE, SV_FLAG_ID_RANGE, SV_FLAG_EMPTY_RESIDUAL, SV_FLAG_Q_ZERO, SV_FLAG_INTERNAL = 1, 2, 4, 8, 16
 SV_MAX_GAMMA, SV_MAX_K = 1024, 256
 
-EXPORTS = ("sv_workspace_bytes", "sv_status_string", "sv_profile_next_stats", "sv_verify_dense",
+EXPORTS = ("sv_workspace_bytes", "sv_status_string", "sv_verify_dense",
            "sv_verify_onehot_draft", "sv_verify_sparse", "sv_support_workspace_bytes", "sv_build_support",
            "sv_verify_greedy", "sv_confidence_commit")
 
@@ -34,8 +34,6 @@ def _load() -> ctypes.CDLL:
     lib.sv_workspace_bytes.restype = SZ
     lib.sv_status_string.argtypes = [ctypes.c_int]
     lib.sv_status_string.restype = ctypes.c_char_p
-    lib.sv_profile_next_stats.argtypes = [P, P]
-    lib.sv_profile_next_stats.restype = ctypes.c_int
     lib.sv_verify_dense.argtypes = [P, I64, I64, P, I64, I64, ctypes.c_int, I64, I32, I64, P, P, P, F, I32, P, P,
                                     P, P, P, P, P, P, P, SZ, P]
     lib.sv_verify_dense.restype = ctypes.c_int
@@ -74,13 +72,6 @@ def sv_support_workspace_bytes(rows: int, V: int, k: int) -> int:
 
 def sv_status_string(status: int) -> str:
     return LIB.sv_status_string(status).decode()
-
-
-def sv_profile_next_stats(start_event, stop_event) -> None:
-    """Time the next dense / one-hot call's row-statistics kernel with two caller-owned hipEvent_t handles."""
-    st = LIB.sv_profile_next_stats(start_event, stop_event)
-    if st != SV_OK:
-        raise SVError(st)
 
 
 def _ptr(t):
@@ -122,7 +113,9 @@ def _zeroed_workspace(n: int, device) -> torch.Tensor | None:
         raise SVError(-2)
     if n == 0:
         return None
-    ws = torch.zeros(n + 256, dtype=torch.uint8, device=device)   # control words must start at zero
+    # any initial contents are valid (the first workgroup of a call clears the control words when the workspace
+    # header does not name the call's layout); a zero-filled buffer keeps fresh allocations reproducible
+    ws = torch.zeros(n + 256, dtype=torch.uint8, device=device)
     off = (-ws.data_ptr()) % 256
     return ws[off:off + n]
 

@@ -1,10 +1,13 @@
 """GPU parity of the confidence-threshold commit (through the C ABI) against the float64 CPU oracle.
 
 Tokens are integer work on the logits (an argmax with ties to the lowest id) and must match exactly for every
-committed slot. The commit set is decided by comparing confidences with tau and with each other; it must match
-exactly except in blocks whose oracle margin (distance of a confidence to tau, gap between the two most confident
-slots) is below 1e-5 relative, where the kernel's float32 partial sums may fall on the other side. Confidences agree
-to 1e-5 relative (sums of exp in float32 partials, merged in float64). Faults match exactly.
+committed slot. The commit set is decided by comparing confidences with tau and, for the forced commit only, with
+each other; it must match exactly except in blocks whose decisive oracle margin (the distance of a masked slot's
+confidence to tau, and the gap between the two most confident slots when no slot reaches tau) is below 1e-5, where
+the kernel's float32 partial sums may fall on the other side. Such blocks are counted (at most 20% of a call's
+blocks; in practice only tau = 1 on a 5-token vocabulary has any), and their result must still be valid: committed
+tokens are the slot's argmax, the count matches the flags, at least one slot is committed. Confidences agree to 1e-5
+relative (sums of exp in float32 partials, merged in float64). Faults match exactly.
 """
 import numpy as np
 import pytest
@@ -26,6 +29,12 @@ def _gpu():
     from lossless_draft_verification_spec_amd import sv  # noqa: F401  (raises if the library is missing)
 
 
+def with_argmax(o, z, dtype):
+    """The oracle's result plus each slot's argmax (lowest id on ties), the token any commit of that slot must be."""
+    o["argmax"] = oracle.slot_confidence(oracle.widen(z, dtype))[0]
+    return o
+
+
 def run_commit(z, dtype, tau, masked=None, *, row_pad=0, ws=None):
     from lossless_draft_verification_spec_amd import sv
     B, Wn, V = z.shape
@@ -43,15 +52,45 @@ def run_commit(z, dtype, tau, masked=None, *, row_pad=0, ws=None):
     return res
 
 
-def check(g, o):
+def decisive_margin(o, tau):
+    """Per block, the oracle's distance from the comparisons that decide its commit set: |confidence - tau| for every
+    masked slot, and, only when no slot reaches tau (the forced commit), the gap between the two most confident."""
+    conf = o["confidence"]
+    t = float(np.float32(tau))
+    m = np.full(conf.shape[0], np.inf)
+    for b in range(conf.shape[0]):
+        c = conf[b][~np.isnan(conf[b])]
+        if c.size == 0:
+            continue
+        m[b] = float(np.min(np.abs(c - t)))
+        if not (c >= t).any() and c.size > 1:
+            s = np.sort(c)[::-1]
+            m[b] = min(m[b], float(s[0] - s[1]))
+    return m
+
+
+MAX_EXCLUDED = 0.2     # blocks per call whose commit set may go uncompared (near-ties), at most this fraction
+
+
+def check(g, o, tau, label=""):
     np.testing.assert_array_equal(g["flags"], o["flags"])
-    ok = o["margin"] >= MARGIN * np.maximum(1.0, np.nanmax(np.nan_to_num(o["confidence"], nan=0.0), axis=1))
-    assert ok.mean() > 0.5                 # the comparison covers most blocks (tau = 1 puts many near the edge)
+    near = decisive_margin(o, tau) < MARGIN
+    ok = ~near
+    print(f"{label}: {int(near.sum())} of {near.size} blocks at a decisive margin below {MARGIN}", flush=True)
+    assert near.sum() <= MAX_EXCLUDED * near.size
     np.testing.assert_array_equal(g["commit"][ok], o["commit"][ok])
     np.testing.assert_array_equal(g["token"][ok], o["token"][ok])
     np.testing.assert_array_equal(g["n_commit"][ok], o["n_commit"][ok])
+    # near-tie blocks: still a valid result (committed tokens are the slot argmax, which is exact integer work; the
+    # count matches the commit flags; a block with a masked slot commits at least one)
     both = (g["commit"] == 1) & (o["commit"] == 1)
     np.testing.assert_array_equal(g["token"][both], o["token"][both])
+    committed = g["commit"] == 1
+    np.testing.assert_array_equal(g["n_commit"][near], committed[near].sum(-1))
+    live = ~np.isnan(o["confidence"]).all(-1) & (o["flags"] == 0)
+    assert np.all(g["n_commit"][near & live] >= 1)
+    argmax_ok = np.where(committed, g["token"] == np.where(np.isnan(o["confidence"]), -2, o["argmax"]), True)
+    assert argmax_ok.all()
     read = ~np.isnan(o["confidence"])
     np.testing.assert_array_equal(~np.isnan(g["confidence"]), read)
     np.testing.assert_allclose(g["confidence"][read], o["confidence"][read], rtol=1e-5)
@@ -64,21 +103,21 @@ def test_blocks(dtype, V, tau):
     print(f"commit dtype={dtype} V={V} tau={tau}", flush=True)
     B = 3 if V == 151936 else 40
     c = W.commit_case(B, 4, V, dtype=dtype, tau=tau, seed=V % 97)
-    o = oracle.confidence_commit(c["logits"], dtype, tau, c["masked"])
-    check(run_commit(c["logits"], dtype, tau, c["masked"]), o)
-    o = oracle.confidence_commit(c["logits"], dtype, tau)
-    check(run_commit(c["logits"], dtype, tau), o)
+    o = with_argmax(oracle.confidence_commit(c["logits"], dtype, tau, c["masked"]), c["logits"], dtype)
+    check(run_commit(c["logits"], dtype, tau, c["masked"]), o, tau, f"{dtype} V={V} tau={tau} masked")
+    o = with_argmax(oracle.confidence_commit(c["logits"], dtype, tau), c["logits"], dtype)
+    check(run_commit(c["logits"], dtype, tau), o, tau, f"{dtype} V={V} tau={tau} all")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_unaligned_rows_and_long_blocks(dtype):
     print(f"commit unaligned dtype={dtype}", flush=True)
     c = W.commit_case(5, 37, 20011, dtype=dtype, seed=4)
-    o = oracle.confidence_commit(c["logits"], dtype, 0.8, c["masked"])
-    check(run_commit(c["logits"], dtype, 0.8, c["masked"], row_pad=3), o)
+    o = with_argmax(oracle.confidence_commit(c["logits"], dtype, 0.8, c["masked"]), c["logits"], dtype)
+    check(run_commit(c["logits"], dtype, 0.8, c["masked"], row_pad=3), o, 0.8, "unaligned")
     c = W.commit_case(2, 1024, 300, dtype=dtype, seed=5)
-    o = oracle.confidence_commit(c["logits"], dtype, 0.95, c["masked"])
-    check(run_commit(c["logits"], dtype, 0.95, c["masked"]), o)
+    o = with_argmax(oracle.confidence_commit(c["logits"], dtype, 0.95, c["masked"]), c["logits"], dtype)
+    check(run_commit(c["logits"], dtype, 0.95, c["masked"]), o, 0.95, "long blocks")
 
 
 def test_faults_and_ties():
@@ -108,11 +147,11 @@ def test_block_workload_and_shared_workspace():
     c = W.commit_case(256, 4, 151936, seed=0)
     n = max(sv.sv_workspace_bytes(sv.SV_KIND_GREEDY, 256, 4, 151936), sv.sv_workspace_bytes(sv.SV_KIND_GREEDY, 8, 3, 5000))
     ws = torch.zeros(n, dtype=torch.uint8, device=torch.device("cuda", 0))
-    o = oracle.confidence_commit(c["logits"], "bf16", c["tau"], c["masked"])
+    o = with_argmax(oracle.confidence_commit(c["logits"], "bf16", c["tau"], c["masked"]), c["logits"], "bf16")
     g0 = W.greedy_case(8, 3, 5000, seed=3)
     og = oracle.verify_greedy(g0["target"], g0["draft_ids"], dtype="bf16")
     for _ in range(2):
-        check(run_commit(c["logits"], "bf16", c["tau"], c["masked"], ws=ws), o)
+        check(run_commit(c["logits"], "bf16", c["tau"], c["masked"], ws=ws), o, c["tau"], "block workload")
         gg = sv.sv_verify_greedy(t_logits(g0["target"], "bf16"), t_(g0["draft_ids"], torch.int32), ws=ws)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(gg["out_token"].cpu().numpy(), og["out_token"])

@@ -255,15 +255,16 @@ def test_onehot_shapes(shape):
     compare_probs(g, o, "p_draft", dt)
 
 
-def test_onehot_workload_full_size_sampled():
-    """Greedy-draft workload at full size (B=256, gamma=8, V=128256, bf16, T=0.7); oracle on 64 sampled sequences."""
+def test_onehot_workload_full_size():
+    """Greedy-draft workload at full size (B=256, gamma=8, V=128256, bf16, T=0.7), the benchmark's launch
+    configuration; the oracle runs on every sequence."""
     case = W.make("onehot_B256_g8_V128256_bf16")
+    log("generated one-hot workload")
     g = run_onehot(case)
-    seqs = np.sort(np.random.default_rng(0).choice(256, 64, replace=False))
-    o = oracle_dense(case, onehot=True, seqs=seqs)
-    gs = {k: v[seqs] for k, v in g.items()}
-    s = compare_decisions(gs, o, "onehot full")
-    compare_probs(gs, o, "p_draft", "bf16")
+    log("gpu done")
+    o = oracle_dense(case, onehot=True)
+    s = compare_decisions(g, o, "onehot full")
+    compare_probs(g, o, "p_draft", "bf16")
     log(f"onehot full: {s}, mean n {g['n_accepted'].mean():.3f}")
 
 
@@ -389,7 +390,29 @@ def test_window_rounds_small():
     run_window_rounds(case)
 
 
-def test_window_workload_full_size_sampled():
-    """Masked-diffusion window at full size (B=32, W=32, V=262144, fp32, 4 rounds); oracle on 8 sequences."""
+def test_window_workload_full_size():
+    """Masked-diffusion window at full size (B=32, W=32, V=262144, fp32, 4 rounds), the benchmark's launch
+    configuration; the oracle runs every round on every sequence."""
     case = W.make("window_B32_W32_V262144_r4")
-    run_window_rounds(case, seqs=np.array([0, 3, 7, 12, 18, 21, 26, 31]))
+    log("generated window workload")
+    run_window_rounds(case)
+
+
+def test_golden_window_rounds_on_gpu():
+    """The hand-derived two-round window (tests/golden/rule_cases.json, "window"): rounds chained on the device
+    through `start`, each with its own uniforms."""
+    from lossless_draft_verification_spec_amd import sv
+    for c in _golden()["window"]:
+        zt = np.log(np.array(c["p"])).astype(np.float32)[None]
+        zd = np.log(np.array(c["q"])).astype(np.float32)[None]
+        start = torch.zeros(1, dtype=torch.int32, device=dev())
+        for r, want in enumerate(c["rounds"]):
+            out = sv.sv_verify_dense(t_logits(zt, "f32"), t_logits(zd, "f32"), t_(np.array([c["draft_ids"]]), torch.int32),
+                                     t_(np.array([want["u_accept"]]), torch.float32),
+                                     t_(np.array([want["u_sample"]]), torch.float32), c["T"], bonus=0, start=start,
+                                     order=t_(np.array([c["order"]]), torch.int32))
+            g = host(out)
+            assert list(g["accept"][0]) == want["accept"], (c["name"], r)
+            assert g["n_accepted"][0] == want["n_accepted"] and g["out_token"][0] == want["out_token"], (c["name"], r)
+            assert int(start.cpu()[0]) == want["start_out"], (c["name"], r)
+            np.testing.assert_allclose(g["p_draft"][0], want["p_draft"], rtol=1e-5, atol=1e-30)
