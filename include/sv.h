@@ -46,6 +46,7 @@ extern "C" {
 #define SV_ERR_WORKSPACE (-6)   /* workspace smaller than sv_workspace_bytes() or NULL while bytes are needed     */
 #define SV_ERR_HIP       (-7)   /* a kernel launch failed                                                         */
 #define SV_ERR_ARG       (-8)   /* any other invalid argument (bonus not 0/1, unknown kind)                       */
+#define SV_ERR_SCRATCH   (-9)   /* the call needs more scratch than SV_NOALLOC_SCRATCH_BYTES (no-allocation call)  */
 
 /* ---- logit element types ------------------------------------------------------------------------------------ */
 #define SV_F32  0
@@ -73,6 +74,7 @@ extern "C" {
 /* ---- limits ------------------------------------------------------------------------------------------------- */
 #define SV_MAX_GAMMA 1024        /* drafted positions per sequence                                                */
 #define SV_MAX_K     256         /* support size of a sparse row (kp, kq)                                          */
+#define SV_NOALLOC_SCRATCH_BYTES (16u << 20)   /* scratch each GPU holds for sv_verify_dense_noalloc               */
 
 /*
  * Bytes of device workspace a call of `kind` needs for B sequences of gamma drafts over V_or_k (V for dense,
@@ -129,6 +131,27 @@ int sv_verify_dense(const void* target_logits, int64_t t_seq, int64_t t_row,
                     uint8_t* accept, int32_t* n_accepted, int32_t* out_token,
                     float* p_draft, float* q_draft, uint32_t* flags,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sv_verify_dense without a workspace, for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc). Same arguments, outputs and errors as
+ * sv_verify_dense, minus workspace / workspace_bytes: the call's scratch is a static device array of
+ * SV_NOALLOC_SCRATCH_BYTES that every GPU the library runs on holds until the process ends. Its address is looked
+ * up once per device, on the first call with that device current; the call itself allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine). Returns SV_ERR_SCRATCH when sv_workspace_bytes(SV_KIND_DENSE, B, gamma,
+ * V) exceeds SV_NOALLOC_SCRATCH_BYTES (16 MiB: B = 64, gamma = 16, V = 151936 needs 1.8 MiB), and SV_ERR_HIP when the
+ * scratch's address cannot be found. All calls on one GPU share that GPU's array: calls that may overlap on one GPU
+ * (different streams, or host threads) race on it and must not be made; calls ordered on one stream are safe. The
+ * array keeps the last call's contents, and each call clears the control words it needs inside its own launch.
+ */
+int sv_verify_dense_noalloc(const void* target_logits, int64_t t_seq, int64_t t_row,
+                            const void* draft_logits, int64_t d_seq, int64_t d_row,
+                            int dtype, int64_t B, int32_t gamma, int64_t V,
+                            const int32_t* draft_ids, const float* u_accept, const float* u_sample,
+                            float temperature, int32_t bonus,
+                            int32_t* start, const int32_t* order,
+                            uint8_t* accept, int32_t* n_accepted, int32_t* out_token,
+                            float* p_draft, float* q_draft, uint32_t* flags, void* stream);
 
 /*
  * Greedy-draft verification (the last paragraph of the Uno page's section "What 'lossless' actually has to mean":

@@ -90,6 +90,7 @@ const char* sv_status_string(int status) {
     case SV_ERR_WORKSPACE: return "workspace missing or too small";
     case SV_ERR_HIP: return "HIP launch failed";
     case SV_ERR_ARG: return "invalid argument";
+    case SV_ERR_SCRATCH: return "the call needs more scratch than the no-allocation entry point holds";
     default: return "unknown status";
   }
 }
@@ -120,6 +121,34 @@ int sv_verify_dense(const void* target_logits, int64_t t_seq, int64_t t_row,
   sv::DenseArgs a{target_logits, t_seq, t_row, draft_logits, d_seq, d_row, dtype, draft_ids, u_accept, u_sample,
                   temperature, bonus, start, order, accept, n_accepted, out_token, p_draft, q_draft, flags,
                   static_cast<char*>(workspace)};
+  return sv::launch_dense(plan, a, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+int sv_verify_dense_noalloc(const void* target_logits, int64_t t_seq, int64_t t_row,
+                            const void* draft_logits, int64_t d_seq, int64_t d_row,
+                            int dtype, int64_t B, int32_t gamma, int64_t V,
+                            const int32_t* draft_ids, const float* u_accept, const float* u_sample,
+                            float temperature, int32_t bonus,
+                            int32_t* start, const int32_t* order,
+                            uint8_t* accept, int32_t* n_accepted, int32_t* out_token,
+                            float* p_draft, float* q_draft, uint32_t* flags, void* stream) {
+  int st = check_dense_common(target_logits, t_seq, t_row, dtype, B, gamma, V, draft_ids, u_accept, u_sample,
+                              temperature, bonus, start, order, accept, n_accepted, out_token, p_draft, flags);
+  if (st != SV_OK) return st;
+  if (!draft_logits) return SV_ERR_NULL;
+  if (d_seq < 1 || d_row < 1) return SV_ERR_SHAPE;
+  if (double(B - 1) * double(d_seq) + double(gamma - 1) * double(d_row) + double(V) > 9.0e18) return SV_ERR_SHAPE;
+  if (!aligned(draft_logits, dtype == SV_BF16 ? 2 : 4)) return SV_ERR_ALIGN;
+  if (q_draft && !aligned(q_draft, 4)) return SV_ERR_ALIGN;
+  // the scratch must hold the largest plan of this shape (the float32 one), whatever the dtype of this call
+  if (sv::make_dense_plan(B, gamma, V, 2, SV_F32, 1).total > size_t(SV_NOALLOC_SCRATCH_BYTES)) return SV_ERR_SCRATCH;
+  const sv::DensePlan plan = sv::make_dense_plan(B, gamma, V, 2, dtype, sv::resident_workgroups());
+  st = check_grid(plan);
+  if (st != SV_OK) return st;
+  char* ws = nullptr;
+  if (sv::noalloc_scratch(&ws) != hipSuccess) return SV_ERR_HIP;
+  sv::DenseArgs a{target_logits, t_seq, t_row, draft_logits, d_seq, d_row, dtype, draft_ids, u_accept, u_sample,
+                  temperature, bonus, start, order, accept, n_accepted, out_token, p_draft, q_draft, flags, ws};
   return sv::launch_dense(plan, a, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 

@@ -30,11 +30,17 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "sv.h"
 #include "sv_device.h"
 #include "sv_internal.h"
 #include "sv_wshdr.h"
+
+// Scratch of the no-allocation entry point (sv_verify_dense_noalloc): every GPU the library runs on holds its own copy
+// until the process ends. Host code never passes this name to a kernel: it looks the device address up with
+// hipGetSymbolAddress (noalloc_scratch) and passes that.
+static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
 
 namespace sv {
 namespace {
@@ -1668,6 +1674,27 @@ DensePlan make_dense_plan(int64_t B, int32_t G, int64_t V, int32_t ntens, int dt
   p.off_masses = off; off = align_up(off + size_t(B) * size_t(p.nch) * sizeof(double), 256);
   p.total = off;
   return p;
+}
+
+// The current device's copy of `scratch`, looked up once per device (with that device current) and kept.
+hipError_t noalloc_scratch(char** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static char* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & 255u) != 0) return hipErrorInvalidSymbol;
+    addr[dev] = static_cast<char*>(p);
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_dense(const DensePlan& plan, const DenseArgs& a, hipStream_t stream) {

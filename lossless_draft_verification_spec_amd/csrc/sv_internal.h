@@ -92,6 +92,8 @@ struct DenseArgs {
 };
 
 hipError_t launch_dense(const DensePlan& plan, const DenseArgs& a, hipStream_t stream);
+// Device address of the current device's no-allocation scratch (SV_NOALLOC_SCRATCH_BYTES), looked up once per device.
+hipError_t noalloc_scratch(char** out);
 
 struct SparseArgs {
   const int32_t* p_ids; const float* p_probs;

@@ -19,8 +19,10 @@ SV_F32, SV_BF16 = 0, 1
 SV_KIND_DENSE, SV_KIND_ONEHOT, SV_KIND_SPARSE, SV_KIND_GREEDY = 0, 1, 2, 3
 SV_FLAG_NONFINITE, SV_FLAG_ID_RANGE, SV_FLAG_EMPTY_RESIDUAL, SV_FLAG_Q_ZERO, SV_FLAG_INTERNAL = 1, 2, 4, 8, 16
 SV_MAX_GAMMA, SV_MAX_K = 1024, 256
+SV_NOALLOC_SCRATCH_BYTES = 16 << 20
+SV_ERR_SCRATCH = -9
 
-EXPORTS = ("sv_workspace_bytes", "sv_status_string", "sv_verify_dense",
+EXPORTS = ("sv_workspace_bytes", "sv_status_string", "sv_verify_dense", "sv_verify_dense_noalloc",
            "sv_verify_onehot_draft", "sv_verify_sparse", "sv_support_workspace_bytes", "sv_build_support",
            "sv_verify_greedy", "sv_confidence_commit")
 
@@ -37,6 +39,9 @@ def _load() -> ctypes.CDLL:
     lib.sv_verify_dense.argtypes = [P, I64, I64, P, I64, I64, ctypes.c_int, I64, I32, I64, P, P, P, F, I32, P, P,
                                     P, P, P, P, P, P, P, SZ, P]
     lib.sv_verify_dense.restype = ctypes.c_int
+    lib.sv_verify_dense_noalloc.argtypes = [P, I64, I64, P, I64, I64, ctypes.c_int, I64, I32, I64, P, P, P, F, I32,
+                                            P, P, P, P, P, P, P, P, P]
+    lib.sv_verify_dense_noalloc.restype = ctypes.c_int
     lib.sv_verify_onehot_draft.argtypes = [P, I64, I64, ctypes.c_int, I64, I32, I64, P, P, P, F, I32, P, P,
                                            P, P, P, P, P, P, SZ, P]
     lib.sv_verify_onehot_draft.restype = ctypes.c_int
@@ -176,6 +181,36 @@ def sv_verify_dense(target, draft, draft_ids, u_accept, u_sample, temperature, b
                              _ptr(start), _ptr(order), _ptr(o.get("accept")), _ptr(o["n_accepted"]),
                              _ptr(o["out_token"]), _ptr(o.get("p_draft")), _ptr(o.get("q_draft")), _ptr(o.get("flags")),
                              _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    if st != SV_OK:
+        raise SVError(st)
+    return o
+
+
+def sv_verify_dense_noalloc(target, draft, draft_ids, u_accept, u_sample, temperature, bonus=1, start=None,
+                            order=None, *, out=None, stream=None,
+                            outputs=("accept", "n_accepted", "out_token", "p_draft", "q_draft", "flags")):
+    """sv_verify_dense on the library's static per-GPU scratch (see ``sv_verify_dense_noalloc`` in include/sv.h):
+    no workspace argument. Outputs are allocated here unless `out` holds them already."""
+    B, G = draft_ids.shape
+    dev = target.device
+    V = target.shape[-1]
+    t_seq, t_row = _logits_layout(target, "target", G + bonus, B, dev)
+    d_seq, d_row = _logits_layout(draft, "draft", G, B, dev)
+    if draft.dtype != target.dtype or draft.shape[-1] != V:
+        raise ValueError("draft must match target in dtype and vocabulary size")
+    _need(draft_ids, "draft_ids", torch.int32, (B, G), dev)
+    _need(u_accept, "u_accept", torch.float32, (B, G), dev)
+    _need(u_sample, "u_sample", torch.float32, (B, G + 1), dev)
+    if start is not None:
+        _need(start, "start", torch.int32, (B,), dev)
+    if order is not None:
+        _need(order, "order", torch.int32, (B, G), dev)
+    o = _outputs(B, G, dev, out, outputs)
+    st = LIB.sv_verify_dense_noalloc(_ptr(target), t_seq, t_row, _ptr(draft), d_seq, d_row, _dtype_code(target), B, G,
+                                     V, _ptr(draft_ids), _ptr(u_accept), _ptr(u_sample), float(temperature), int(bonus),
+                                     _ptr(start), _ptr(order), _ptr(o.get("accept")), _ptr(o["n_accepted"]),
+                                     _ptr(o["out_token"]), _ptr(o.get("p_draft")), _ptr(o.get("q_draft")),
+                                     _ptr(o.get("flags")), _stream(stream))
     if st != SV_OK:
         raise SVError(st)
     return o
