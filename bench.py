@@ -176,7 +176,8 @@ def bench_support(case, steps, warmup, torch, sv, d, k=50, top_p=0.95):
                 support_ms_target=kt, support_ms_draft=kd, sparse_ms=kv,
                 support_bytes_target=bytes_t, support_bytes_draft=bytes_d,
                 support_GBps_target=gt, support_GBps_draft=gd, support_frac_target=ft, support_frac_draft=fd,
-                roofline=roofline(bytes_t, kt, "k_support<bf16> (target rows)"))
+                roofline=roofline(bytes_t, kt, "k_support<bf16> (target rows)",
+                                  profile_traffic("k_support.txt", "support_chain target rows (1088 x 151936 bf16)")))
 
 
 # ----------------------------------------------------------------------------------------------------------------------
@@ -210,7 +211,8 @@ def bench_greedy(steps, warmup, torch, sv, d):
     gbps, frac = hbm(nbytes, ms)
     return dict(ms_per_step=ms, wall_ms_per_step=wall, positions=B * G, positions_per_s=B * G / (ms * 1e-3),
                 mean_n_accepted=float(n.mean()), algorithmic_bytes=nbytes, hbm_GBps=gbps, hbm_frac=frac,
-                input_copies=ncopies, roofline=roofline(nbytes, ms, "k_greedy<bf16>"))
+                input_copies=ncopies, roofline=roofline(nbytes, ms, "k_greedy<bf16>",
+                                                        profile_traffic("k_greedy.txt", GREEDY)))
 
 
 COMMIT = "commit_block_B256_W4_V151936_bf16"
@@ -239,7 +241,8 @@ def bench_commit(steps, warmup, torch, sv, d):
     gbps, frac = hbm(nbytes, ms)
     return dict(ms_per_step=ms, wall_ms_per_step=wall, slots=B * Wn, masked_slots=nm,
                 committed=int(out["n_commit"].sum().item()), algorithmic_bytes=nbytes, hbm_GBps=gbps,
-                hbm_frac=frac, roofline=roofline(nbytes, ms, "k_greedy<bf16> (commit mode)"))
+                hbm_frac=frac, roofline=roofline(nbytes, ms, "k_greedy<bf16> (commit mode)",
+                                                 profile_traffic("k_greedy.txt", COMMIT)))
 
 
 # ----------------------------------------------------------------------------------------------------------------------
@@ -261,7 +264,9 @@ def bench_sparse(case, steps, warmup, torch, sv, d):
     out_bytes = sum(int(v.numel() * v.element_size()) for v in out.values())
     gbps, frac = hbm(in_bytes + out_bytes, ms)
     return dict(ms_per_step=ms, wall_ms_per_step=wall, positions=B * G, positions_per_s=B * G / (ms * 1e-3),
-                algorithmic_bytes=in_bytes + out_bytes, hbm_GBps=gbps, hbm_frac=frac)
+                algorithmic_bytes=in_bytes + out_bytes, hbm_GBps=gbps, hbm_frac=frac,
+                roofline=roofline(in_bytes + out_bytes, ms, "k_sparse",
+                                  profile_traffic("k_sparse.txt", "sparse_B1024_g16_k64_V151936")))
 
 
 def bench_window(case, steps, warmup, torch, sv, d):
@@ -314,7 +319,8 @@ def bench_window(case, steps, warmup, torch, sv, d):
     gbps, frac = hbm(total_bytes, ms)
     return dict(ms_per_step=ms, wall_ms_per_step=wall, rounds=rounds, positions=positions,
                 positions_per_s=positions / (ms * 1e-3), algorithmic_bytes=total_bytes, hbm_GBps=gbps, hbm_frac=frac,
-                roofline=roofline(rounds[0]["algorithmic_bytes"], rounds[0]["ms"], "k_verify<f32> (round 0)"))
+                roofline=roofline(rounds[0]["algorithmic_bytes"], rounds[0]["ms"], "k_verify<f32> (round 0)",
+                                  profile_traffic("k_verify.txt", "window_B32_W32_V262144_r4 round 0")))
 
 
 # ----------------------------------------------------------------------------------------------------------------------
@@ -468,7 +474,7 @@ def main():
         del src, dst
         torch.cuda.empty_cache()
     r = bench_dense(head, args.steps, args.warmup, torch, sv, d,
-                    traffic=profile_traffic("k_verify_traffic.txt", HEADLINE))
+                    traffic=profile_traffic("k_verify.txt", HEADLINE))
     log("headline", json.dumps(r))
 
     others = {}
@@ -491,7 +497,7 @@ def main():
         c = workloads.make(name)
         if c["kind"] in ("dense", "onehot"):
             others[name] = bench_dense(c, args.steps, args.warmup, torch, sv, d,
-                                       traffic=profile_traffic("k_verify_traffic.txt", name))
+                                       traffic=profile_traffic("k_verify.txt", name))
         elif c["kind"] == "sparse":
             others[name] = bench_sparse(c, args.steps, args.warmup, torch, sv, d)
         else:
