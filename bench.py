@@ -327,7 +327,7 @@ def bench_window(case, steps, warmup, torch, sv, d):
 # tree verification
 # ----------------------------------------------------------------------------------------------------------------------
 
-TREE = "tree_B64_N16_V151936_bf16"
+TREE = "tree_B64_N17_V151936_bf16"
 
 
 def bench_tree(steps, warmup, torch, sv, d):

@@ -292,7 +292,55 @@ def window_case(B: int, W: int, V: int, *, rounds: int = 4, sigma_d: float = 2.0
 
 
 # ----------------------------------------------------------------------------------------------------------------------
-# The five named workloads
+# Token trees (several candidates per position)
+# ----------------------------------------------------------------------------------------------------------------------
+
+def random_tree_parents(rng, B: int, N: int, p_chain: float = 0.5) -> np.ndarray:
+    """parent[b][0] = -1; node i >= 1 hangs under node i - 1 with probability p_chain, else under a uniformly chosen
+    earlier node (a random recursive tree: deep main lines with side branches)."""
+    parent = np.full((B, N), -1, dtype=np.int32)
+    for b in range(B):
+        for i in range(1, N):
+            parent[b, i] = i - 1 if rng.random() < p_chain else int(rng.integers(0, i))
+    return parent
+
+
+def tree_case(B: int, N: int, V: int, *, dtype: str = DTYPE_BF16, sigma: float = 2.0, zipf: float = 1.1,
+              spike: tuple = (12.0, 24.0), sigma_x: float = 1.5, temperature: float = 1.0, seed: int = 0) -> dict:
+    """Token trees of N nodes (node 0 the root): target logits [B, N, V], one row per node (the target's distribution
+    after the path to that node): N(0, sigma^2) plus the Zipf bias plus a spike of height U(spike) at one uniform id, so
+    that the top candidates carry much of the mass; parents from ``random_tree_parents``; the children of a node, in
+    increasing node index, carry the drafter's top candidates in decreasing order: the largest entries of that node's
+    row + N(0, sigma_x^2) (distinct tokens, as a top-m drafter proposes them); u_accept [B, N] and u_sample [B, N]."""
+    r_z, r_h, r_i, r_p, r_x, r_a, r_s = _streams(seed, 7)
+    z = _normal_f32(r_z, (B, N, V), sigma)
+    if zipf:
+        z += (-zipf * np.log1p(np.arange(V, dtype=np.float64))).astype(np.float32)
+    h = np.float32(spike[0]) + uniforms(r_h, (B, N)) * np.float32(spike[1] - spike[0])
+    at = (uniforms(r_i, (B, N)) * V).astype(np.int64)
+    np.put_along_axis(z, at[..., None], np.take_along_axis(z, at[..., None], axis=-1) + h[..., None], axis=-1)
+    zs = f32_to_bf16_bits(z) if dtype == DTYPE_BF16 else z
+    z_eff = bf16_bits_to_f32(zs) if dtype == DTYPE_BF16 else z
+    parent = random_tree_parents(r_p.rng, B, N)
+    token = np.zeros((B, N), dtype=np.int32)
+    noisy = _normal_f32(r_x, (B, N, V), sigma_x)
+    noisy += z_eff
+    for b in range(B):
+        nkids = np.bincount(parent[b, 1:], minlength=N)
+        for u in range(N):
+            k = int(nkids[u])
+            if k == 0:
+                continue
+            top = np.argpartition(-noisy[b, u], k - 1)[:k]
+            top = top[np.argsort(-noisy[b, u, top], kind="stable")]
+            token[b, np.flatnonzero(parent[b] == u)] = top
+    del noisy
+    return dict(kind="tree", dtype=dtype, B=B, N=N, V=V, temperature=float(np.float32(temperature)), target=zs,
+                parent=parent, token=token, u_accept=uniforms(r_a, (B, N)), u_sample=uniforms(r_s, (B, N)))
+
+
+# ----------------------------------------------------------------------------------------------------------------------
+# The named workloads
 # ----------------------------------------------------------------------------------------------------------------------
 
 WORKLOADS = {
@@ -309,6 +357,8 @@ WORKLOADS = {
     "sparse_B1024_g16_k64_V151936": lambda seed=0: sparse_case(1024, 16, 64, 151936, seed=seed),
     # masked-diffusion window: B=32, W=32, V=262144, fp32, 4 rounds
     "window_B32_W32_V262144_r4": lambda seed=0: window_case(32, 32, 262144, rounds=4, seed=seed),
+    # token trees: B=64 trees of 17 nodes (root + 16 drafted, the Uno page's B = 16 tree sampler), V=151936, bf16
+    "tree_B64_N17_V151936_bf16": lambda seed=0: tree_case(64, 17, 151936, dtype=DTYPE_BF16, seed=seed),
 }
 
 

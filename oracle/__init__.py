@@ -10,9 +10,10 @@ from .verify import (FLAG_EMPTY_RESIDUAL, FLAG_ID_RANGE, FLAG_NONFINITE, FLAG_Q_
 from .support import build_support, topk_order
 from .greedy import first_argmax, verify_greedy
 from .commit import confidence_commit, slot_confidence
+from .tree import tree_children, tree_is_valid, verify_tree
 
 __all__ = ["FLAG_EMPTY_RESIDUAL", "FLAG_ID_RANGE", "FLAG_NONFINITE", "FLAG_Q_ZERO", "FATAL", "accept_test",
            "accept_test_exact",
            "inverse_cdf", "log_softmax_at", "residual", "softmax", "verify_dense", "verify_onehot", "verify_sparse",
            "verify_windows", "widen", "build_support", "topk_order", "first_argmax", "verify_greedy",
-           "confidence_commit", "slot_confidence"]
+           "confidence_commit", "slot_confidence", "tree_children", "tree_is_valid", "verify_tree"]

@@ -60,6 +60,37 @@ MUTATIONS = {
     "support_renorm_over_all_k": (
         "support", "out[:m] = e[:m] / cum[m - 1]", "out[:m] = e[:m] / cum[-1]",
         ("tests/test_support_pins.py", None), "kept probabilities renormalised over all k slots"),
+    # tree verification (SpecInfer's multi-step speculative sampling with one-hot q per candidate)
+    "tree_no_renormalisation": (
+        "tree", "P = p[x] / np.sum(p[~excluded])", "P = p[x]",
+        ("tests/test_tree_pins.py", "golden or exact_law"), "a later candidate is tested against p, not p without the "
+        "rejected tokens"),
+    "tree_draw_keeps_rejected": (
+        "tree", "r = np.where(excluded, 0.0, p)", "r = p",
+        ("tests/test_tree_pins.py", "golden or exact_law"), "the final draw can return a rejected candidate"),
+    "tree_children_descending": (
+        "tree", "kids[int(parent[i])].append(i)", "kids[int(parent[i])].insert(0, i)",
+        ("tests/test_tree_pins.py", "golden or exact_law"), "siblings tested from the highest node index"),
+    "tree_non_strict_test": (
+        "tree", "if ua[b, c] < min(1.0, P):", "if ua[b, c] <= min(1.0, P):",
+        ("tests/test_tree_pins.py", "golden or exact_law"), "u equal to p'(x) accepts (a repeated token passes at "
+        "u = 0)"),
+    "tree_exclusions_kept_after_accept": (
+        "tree", """        cur, path, fault = 0, [], False
+        while True:
+            p = row_p(cur)
+            if p is None:
+                fault = True
+                break
+            excluded = np.zeros(V, bool)
+""", """        cur, path, fault = 0, [], False
+        excluded = np.zeros(V, bool)
+        while True:
+            p = row_p(cur)
+            if p is None:
+                fault = True
+                break
+""", ("tests/test_tree_pins.py", "golden or exact_law"), "tokens rejected at one node stay excluded at the next"),
 }
 
 
