@@ -57,6 +57,7 @@ extern "C" {
 #define SV_KIND_ONEHOT 1
 #define SV_KIND_SPARSE 2
 #define SV_KIND_GREEDY 3
+#define SV_KIND_TREE   4
 
 /* ---- per-sequence flags ------------------------------------------------------------------------------------- */
 #define SV_FLAG_NONFINITE      1u  /* NaN or +inf logit (or a row all -inf) in a row that was read; for sparse, a
@@ -75,6 +76,7 @@ extern "C" {
 #define SV_MAX_GAMMA 1024        /* drafted positions per sequence                                                */
 #define SV_MAX_K     256         /* support size of a sparse row (kp, kq)                                          */
 #define SV_NOALLOC_SCRATCH_BYTES (16u << 20)   /* scratch each GPU holds for sv_verify_dense_noalloc               */
+#define SV_MAX_TREE_NODES 1024   /* nodes of one token tree (the root included)                                    */
 
 /*
  * Bytes of device workspace a call of `kind` needs for B sequences of gamma drafts over V_or_k (V for dense,
@@ -296,6 +298,50 @@ int sv_confidence_commit(const void* logits, int64_t l_seq, int64_t l_row, int d
                          int64_t V, const uint8_t* masked, float tau, uint8_t* commit, int32_t* token,
                          float* confidence, int32_t* n_commit, uint32_t* flags,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Tree (multi-candidate) verification. The pages verify trees of drafted tokens (the Uno page's B = 16 tree sampler,
+ * section "One backbone, two pathways"; EAGLE-2's dynamic draft trees, DFlash/DFlash2 guide section 3; DFlash2's
+ * top-m candidates per position submitted as a dense verification tree, section 5.2) but state the acceptance rule
+ * for one candidate per position, with its one-hot form for a greedy drafter (Uno, "What 'lossless' actually has to
+ * mean"). For several candidates the rule is SpecInfer's multi-step speculative sampling (Miao et al., ASPLOS 2024)
+ * with q one-hot at each candidate (candidates chosen deterministically, as top-m drafters choose them):
+ * - node 0 is the root; row i of the target logits is the target's distribution after the path to node i, and
+ *   p_i = softmax(row_i / T);
+ * - at node u the children of u are tested in increasing node index: child c with token x passes when
+ *   u_accept[c] < min(1, p'(x)), p' = p_u without the tokens of the children of u already rejected, renormalised
+ *   (a token already rejected has p'(x) = 0 and fails); a passing child is accepted and the walk continues there;
+ * - where every child fails, or at a node without children, one token is drawn from p' (p_u without the rejected
+ *   tokens; at a leaf, p_u itself) by the draw rule above, at t = u_sample[u] * (mass of p').
+ * With distinct candidates the emitted tokens follow the target's own law (Leviathan et al.'s guarantee).
+ *
+ * target_logits  [B][N][V] of `dtype` at target_logits[b*t_seq + i*t_row + v]; pointer aligned to the element size
+ *                (rows need no further alignment; strides >= 1; V contiguous). Every row is read once, the stop
+ *                node's row twice.
+ * B, N, V        1 <= B <= 2^31-1, 1 <= N <= SV_MAX_TREE_NODES, 1 <= V <= 2^31-1.
+ * parent, token  [B][N] int32: parent[b][i] in [0, i) and token[b][i] in [0, V) for i >= 1 (element 0 unused),
+ *                else the sequence is flagged SV_FLAG_ID_RANGE and not verified.
+ * u_accept       [B][N] float in [0, 1): the test of node i (element 0 unused).
+ * u_sample       [B][N] float in [0, 1): the draw when the walk stops at node i.
+ * temperature    T > 0, finite.
+ * accept         [B][N] uint8 (required): 1 for the accepted nodes, 0 elsewhere.
+ * n_accepted     [B] int32 (required): accepted nodes (the depth of the stop node), -1 for a failed sequence.
+ * path           [B][N] int32 (required): the accepted nodes from the root down, -1 after them.
+ * out_token      [B] int32 (required): the token drawn at the stop node, -1 for a failed sequence.
+ * p_test         [B][N] float or NULL: p'(x) of every tested node, NaN for nodes not tested.
+ * flags          [B] uint32 or NULL: SV_FLAG_ID_RANGE (tree or token out of range), SV_FLAG_NONFINITE (a NaN or
+ *                +inf logit, or a row all -inf, in a row the walk reaches; rows off the walk are not checked),
+ *                SV_FLAG_EMPTY_RESIDUAL (the rejected tokens held all of p at the stop node: drawn from p).
+ * workspace      >= sv_workspace_bytes(SV_KIND_TREE, B, N, V) bytes, 256-byte aligned, any initial contents (same
+ *                contract as the other calls).
+ * Two kernels on `stream`: the row statistics with the walk, then the draw.
+ * Errors: SV_ERR_NULL, SV_ERR_DTYPE, SV_ERR_SHAPE, SV_ERR_TEMP, SV_ERR_ALIGN, SV_ERR_WORKSPACE, SV_ERR_HIP.
+ */
+int sv_verify_tree(const void* target_logits, int64_t t_seq, int64_t t_row, int dtype, int64_t B, int32_t N,
+                   int64_t V, const int32_t* parent, const int32_t* token, const float* u_accept,
+                   const float* u_sample, float temperature, uint8_t* accept, int32_t* n_accepted, int32_t* path,
+                   int32_t* out_token, float* p_test, uint32_t* flags, void* workspace, size_t workspace_bytes,
+                   void* stream);
 
 #ifdef __cplusplus
 }

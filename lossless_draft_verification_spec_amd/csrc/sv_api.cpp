@@ -74,6 +74,9 @@ size_t sv_workspace_bytes(int kind, int64_t B, int32_t gamma, int64_t V_or_k) {
     case SV_KIND_GREEDY:
       if (V_or_k > kMaxI32) return bad;
       return sv::greedy_workspace_bytes(B, gamma, V_or_k);
+    case SV_KIND_TREE:
+      if (V_or_k > kMaxI32 || gamma > SV_MAX_TREE_NODES) return bad;
+      return sv::make_tree_plan(B, gamma, V_or_k).total;
     default:
       return bad;
   }
@@ -282,6 +285,32 @@ int sv_confidence_commit(const void* logits, int64_t l_seq, int64_t l_row, int d
   a.commit = commit;
   a.conf = confidence;
   return sv::launch_greedy(plan, a, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+int sv_verify_tree(const void* target_logits, int64_t t_seq, int64_t t_row, int dtype, int64_t B, int32_t N,
+                   int64_t V, const int32_t* parent, const int32_t* token, const float* u_accept,
+                   const float* u_sample, float temperature, uint8_t* accept, int32_t* n_accepted, int32_t* path,
+                   int32_t* out_token, float* p_test, uint32_t* flags, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  if (!target_logits || !parent || !token || !u_accept || !u_sample || !accept || !n_accepted || !path || !out_token)
+    return SV_ERR_NULL;
+  if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
+  if (B < 1 || B > kMaxI32 || N < 1 || N > SV_MAX_TREE_NODES || V < 1 || V > kMaxI32) return SV_ERR_SHAPE;
+  if (t_seq < 1 || t_row < 1) return SV_ERR_SHAPE;
+  if (double(B - 1) * double(t_seq) + double(N - 1) * double(t_row) + double(V) > 9.0e18) return SV_ERR_SHAPE;
+  if (double(B) * double(N) > double(kMaxI32)) return SV_ERR_SHAPE;
+  if (!std::isfinite(temperature) || !(temperature > 0.f)) return SV_ERR_TEMP;
+  if (!aligned(target_logits, dtype == SV_BF16 ? 2 : 4)) return SV_ERR_ALIGN;
+  const void* ptrs[] = {parent, token, u_accept, u_sample, n_accepted, path, out_token, p_test, flags};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, 4)) return SV_ERR_ALIGN;
+  const sv::TreePlan plan = sv::make_tree_plan(B, N, V);
+  if (double(B) * double(plan.ntask) > double(kMaxI32)) return SV_ERR_SHAPE;
+  const int st = check_workspace(workspace, workspace_bytes, plan.total);
+  if (st != SV_OK) return st;
+  sv::TreeArgs a{target_logits, t_seq, t_row, dtype, parent, token, u_accept, u_sample, temperature, accept,
+                 n_accepted, path, out_token, p_test, flags, static_cast<char*>(workspace)};
+  return sv::launch_tree(plan, a, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
 }  // extern "C"

@@ -36,6 +36,7 @@
 #include "sv_device.h"
 #include "sv_internal.h"
 #include "sv_wshdr.h"
+#include "sv_fexp.h"
 
 // Scratch of the no-allocation entry point (sv_verify_dense_noalloc): every GPU the library runs on holds its own copy
 // until the process ends. Host code never passes this name to a kernel: it looks the device address up with
@@ -541,33 +542,6 @@ __device__ __forceinline__ Job seq_scan(DP& prm, int64_t b, bool leader, uint32_
   }
   return job;
 }
-
-// 2^y in float64, table-driven in the manner of Tang's exponential (P. T. P. Tang, ACM TOMS 15(2), 1989): y is
-// rounded to a multiple of 1/256, n = 256 k + j; 2^(j/256) comes from a 256-entry table in LDS, 2^f for the remainder
-// |f| <= 1/512 from its degree-4 Taylor polynomial (truncation below 4e-17 relative) and 2^k is applied exactly with
-// ldexp. Every workgroup that draws fills the table first (one entry per thread).
-__shared__ double s_exp2tab[256];
-
-// The core takes a finite y in [-2000, 1023]; below -1075 its result is exactly 0 (ldexp underflows).
-__device__ __forceinline__ double fexp_core(double y) {
-  const double kMagic = 26388279066624.0;                      // 1.5 * 2^44: its ulp is 1/256
-  const double t = y + kMagic;
-  const int n = int(__double2loint(t));                        // round(256 y), two's complement in the low bits
-  const double f = y - (t - kMagic);                           // y - n / 256, exact, |f| <= 1/512
-  double q = fma(0x1.3b2ab6fba4e77p-7, f, 0x1.c6b08d704a0c0p-5);  // ln2^4/24, ln2^3/6
-  q = fma(q, f, 0x1.ebfbdff82c58fp-3);                         // ln2^2/2
-  q = fma(q, f, 0x1.62e42fefa39efp-1);                         // ln2
-  q = fma(q, f, 1.0);
-  return ldexp(s_exp2tab[n & 255] * q, n >> 8);
-}
-
-// Any y up to 1023: the argument is clamped at -2000 (one instruction), so -inf and every y below -1075 give exactly
-// 0. NaN gives 0 too: a row holding NaN or +inf is reported as non-finite before any weight of it is used.
-__device__ __forceinline__ double fexp_scaled(double y) { return fexp_core(fmax(y, -2000.0)); }
-
-// The exponent (z - m) * log2(e) / T of an element, formed as z * c2 + nm with one rounding, nm = -(m * c2). Every
-// evaluation of an element's weight goes through here, so repeated evaluations agree bit for bit.
-__device__ __forceinline__ double xarg(float z, double c2, double nm) { return fma(double(z), c2, nm); }
 
 template <int BLOCK>
 __device__ __forceinline__ double block_max_d(double v, double* sh) {
@@ -1514,7 +1488,7 @@ __global__ __launch_bounds__(kDrawBlock) __attribute__((amdgpu_waves_per_eu(kWpe
   // draw slot: the next draw task from the ticket counter (tickets in sequence order, task order within a sequence),
   // then that sequence's job. There are more draw slots than tasks: the XCDs that run faster start more slots and take more of
   // the tasks; a slot that finds none left ends at once.
-  s_exp2tab[tid] = exp2(double(tid) * 0.00390625);   // the draw's exp2 table (kDrawBlock == 256 entries)
+  fexp_fill_table();                                 // the draw's exp2 table
   const int64_t ntot = prm.ntot;
   const int64_t head = (prm.B - prm.tailq) * int64_t(prm.ntask);    // tickets of the sequences with large tasks
   auto seq_of = [&](int64_t t) { return t < head ? t / prm.ntask : prm.B - prm.tailq + (t - head) / prm.ntask2; };

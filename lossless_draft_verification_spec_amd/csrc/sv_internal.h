@@ -135,4 +135,50 @@ struct SupportArgs {
 
 hipError_t launch_support(const SupportPlan& plan, const SupportArgs& a, hipStream_t stream);
 
+// Tree verification (sv_tree.hip): per-row statistics outside the node's child tokens, the draw job of a sequence,
+// the sizes and workspace layout of one call.
+constexpr uint64_t kLayoutTree = 0x62325cbf29ce4842ull;
+
+struct alignas(16) TreeRow {
+  float m;          // max of the row's logits outside its node's child tokens (-inf when there are none)
+  uint32_t bad;     // 1: a NaN or +inf among them
+  double s;         // sum over them of 2^((z - m) * c), c = log2(e)/T rounded to float
+};
+
+struct alignas(16) TreeJob {
+  int32_t stop;     // node where the walk stopped (-1: nothing to draw)
+  float m;          // max of the stop node's whole row
+  float u;          // the draw's uniform
+  uint32_t flags;   // the sequence's flags from the walk
+};
+
+struct TreePlan {
+  int64_t B = 0;
+  int32_t N = 0;
+  int64_t V = 0;
+  int64_t nch = 0;          // 512-element chunks per row in the draw
+  int32_t ntask = 1;        // draw tasks per sequence
+  int32_t task_chunks = 16; // chunks per draw task
+  size_t off_ctr1 = 0;      // int32 per sequence: rows finished (first launch), back to 0 after the walk
+  size_t off_ctr2 = 0;      // int32 per sequence: draw tasks finished (second launch), back to 0 after the pick
+  size_t ctl_end = 0;       // the control region is [header end, ctl_end)
+  size_t off_rows = 0;      // TreeRow per (b, node)
+  size_t off_zc = 0;        // float per (b, node): the node's logit in its parent's row
+  size_t off_jobs = 0;      // TreeJob per b
+  size_t off_chunk = 0;     // double per (b, chunk)
+  size_t total = 0;
+};
+
+TreePlan make_tree_plan(int64_t B, int32_t N, int64_t V);
+
+struct TreeArgs {
+  const void* tgt; int64_t t_seq, t_row; int dtype;
+  const int32_t* parent; const int32_t* token; const float* ua; const float* us;
+  float temperature;
+  uint8_t* accept; int32_t* n_acc; int32_t* path; int32_t* out_token; float* p_test; uint32_t* flags;
+  char* ws;
+};
+
+hipError_t launch_tree(const TreePlan& plan, const TreeArgs& a, hipStream_t stream);
+
 }  // namespace sv

@@ -16,15 +16,16 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsv.so")
 
 SV_OK = 0
 SV_F32, SV_BF16 = 0, 1
-SV_KIND_DENSE, SV_KIND_ONEHOT, SV_KIND_SPARSE, SV_KIND_GREEDY = 0, 1, 2, 3
+SV_KIND_DENSE, SV_KIND_ONEHOT, SV_KIND_SPARSE, SV_KIND_GREEDY, SV_KIND_TREE = 0, 1, 2, 3, 4
 SV_FLAG_NONFINITE, SV_FLAG_ID_RANGE, SV_FLAG_EMPTY_RESIDUAL, SV_FLAG_Q_ZERO, SV_FLAG_INTERNAL = 1, 2, 4, 8, 16
 SV_MAX_GAMMA, SV_MAX_K = 1024, 256
 SV_NOALLOC_SCRATCH_BYTES = 16 << 20
+SV_MAX_TREE_NODES = 1024
 SV_ERR_SCRATCH = -9
 
 EXPORTS = ("sv_workspace_bytes", "sv_status_string", "sv_verify_dense", "sv_verify_dense_noalloc",
            "sv_verify_onehot_draft", "sv_verify_sparse", "sv_support_workspace_bytes", "sv_build_support",
-           "sv_verify_greedy", "sv_confidence_commit")
+           "sv_verify_greedy", "sv_confidence_commit", "sv_verify_tree")
 
 
 def _load() -> ctypes.CDLL:
@@ -55,6 +56,8 @@ def _load() -> ctypes.CDLL:
     lib.sv_verify_greedy.restype = ctypes.c_int
     lib.sv_confidence_commit.argtypes = [P, I64, I64, ctypes.c_int, I64, I32, I64, P, F, P, P, P, P, P, P, SZ, P]
     lib.sv_confidence_commit.restype = ctypes.c_int
+    lib.sv_verify_tree.argtypes = [P, I64, I64, ctypes.c_int, I64, I32, I64, P, P, P, P, F, P, P, P, P, P, P, P, SZ, P]
+    lib.sv_verify_tree.restype = ctypes.c_int
     return lib
 
 
@@ -357,6 +360,35 @@ def sv_build_support(logits, k, top_p, temperature=1.0, renorm=True, *, out=None
     st = LIB.sv_build_support(_ptr(logits), ld, _dtype_code(logits), rows, V, float(temperature), int(k),
                               float(top_p), 1 if renorm else 0, _ptr(o["ids"]), _ptr(o["probs"]), _ptr(o["count"]),
                               _ptr(o["flags"]), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    if st != SV_OK:
+        raise SVError(st)
+    return o
+
+
+def sv_verify_tree(target, parent, token, u_accept, u_sample, temperature, *, out=None, ws=None, stream=None):
+    """Tree verification (see ``sv_verify_tree`` in include/sv.h). target [B, N, V] float32 or bfloat16 (vocabulary
+    axis contiguous): row i is the target's distribution after the path to node i; parent, token int32 [B, N];
+    u_accept, u_sample float32 [B, N]. Returns accept, n_accepted, path, out_token, p_test, flags."""
+    B, N = parent.shape
+    dev = target.device
+    V = target.shape[-1]
+    t_seq, t_row = _logits_layout(target, "target", N, B, dev)
+    _need(parent, "parent", torch.int32, (B, N), dev)
+    _need(token, "token", torch.int32, (B, N), dev)
+    _need(u_accept, "u_accept", torch.float32, (B, N), dev)
+    _need(u_sample, "u_sample", torch.float32, (B, N), dev)
+    o = {} if out is None else out
+    for name, shape, dt in (("accept", (B, N), torch.uint8), ("n_accepted", (B,), torch.int32),
+                            ("path", (B, N), torch.int32), ("out_token", (B,), torch.int32),
+                            ("p_test", (B, N), torch.float32), ("flags", (B,), torch.int32)):
+        if name not in o:
+            o[name] = torch.empty(shape, dtype=dt, device=dev)
+    if ws is None:
+        ws = workspace(SV_KIND_TREE, B, N, V, dev)
+    st = LIB.sv_verify_tree(_ptr(target), t_seq, t_row, _dtype_code(target), B, N, V, _ptr(parent), _ptr(token),
+                            _ptr(u_accept), _ptr(u_sample), float(temperature), _ptr(o["accept"]), _ptr(o["n_accepted"]),
+                            _ptr(o["path"]), _ptr(o["out_token"]), _ptr(o["p_test"]), _ptr(o["flags"]), _ptr(ws),
+                            0 if ws is None else ws.numel(), _stream(stream))
     if st != SV_OK:
         raise SVError(st)
     return o

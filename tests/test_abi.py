@@ -24,7 +24,7 @@ def test_exports_match_header():
     names = declared_functions()
     assert set(names) == {"sv_workspace_bytes", "sv_status_string", "sv_verify_dense", "sv_verify_dense_noalloc",
                           "sv_verify_onehot_draft", "sv_verify_sparse", "sv_support_workspace_bytes",
-                          "sv_build_support", "sv_verify_greedy", "sv_confidence_commit"}
+                          "sv_build_support", "sv_verify_greedy", "sv_confidence_commit", "sv_verify_tree"}
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (sv_[a-z_]+)\b", out))
     assert set(names) <= exported

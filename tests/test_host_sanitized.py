@@ -13,7 +13,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "lossless_draft_verification_spec_amd", "csrc")
-SOURCES = ["sv_api.cpp", "sv_dense.hip", "sv_sparse.hip", "sv_support.hip", "sv_greedy.hip"]
+SOURCES = ["sv_api.cpp", "sv_dense.hip", "sv_sparse.hip", "sv_support.hip", "sv_greedy.hip", "sv_tree.hip"]
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 CLANG = "/opt/rocm/llvm/bin/clang++"
 SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
