@@ -17,7 +17,8 @@
 //    then a sum of positive terms (the rest of the row, plus the children not rejected yet), so a child holding most
 //    of the mass cannot leave a remainder that cancels. The last row of a sequence to finish (a counter) walks the
 //    tree in float64 and publishes where it stopped.
-//  - k_tree_draw: per sequence, tasks of 16 chunks of 512 elements of the stop row: float64 weights (table-driven
+//  - k_tree_draw: per sequence, tasks of at least 4 chunks of 512 elements of the stop row (all tasks about one
+//    resident round): float64 weights (table-driven
 //    2^y) with the rejected children's tokens removed, one sum per chunk; the last task of the sequence finds the
 //    chunk holding t, recomputes it and searches it.
 // Bound: HBM, B * N * V * s bytes in the first launch (every node row once); the draw re-reads one row per sequence.
@@ -67,17 +68,22 @@ struct TreeParams {
 struct TreeShared {
   int32_t par[SV_MAX_TREE_NODES];
   int32_t tok[SV_MAX_TREE_NODES];
-  int32_t xs[SV_MAX_TREE_NODES];       // masked tokens: the child tokens of the row's node (or of the stop node)
-  int32_t hits[kTBlock][kHits];        // per thread: the masked elements it streams, (group << 8) | slot
-  int32_t kid[SV_MAX_TREE_NODES];      // walk: the children of the current node in node order
-  double ex[SV_MAX_TREE_NODES];        // walk: their weights 2^((z - max) c)
-  uint8_t first[SV_MAX_TREE_NODES];    // walk: the child is the first of its siblings with its token
+  union {
+    struct {                           // the row pass (and the draw)
+      int32_t xs[SV_MAX_TREE_NODES];   // masked tokens: the child tokens of the row's node (or of the stop node)
+      int32_t hits[kTBlock][kHits];    // per thread: the masked elements it streams, (group << 8) | slot
+    } rp;
+    struct {                           // the walk, after the row pass of the same workgroup
+      float rm[SV_MAX_TREE_NODES];     // per node: max of its row outside its children's tokens (NaN: bad row)
+      double rs[SV_MAX_TREE_NODES];    // per node: the sum relative to it
+      float zk[SV_MAX_TREE_NODES];     // per node >= 1: its logit in its parent's row
+      int32_t kid[SV_MAX_TREE_NODES];  // the children of the current node in node order
+      double pk[SV_MAX_TREE_NODES];    // p'(x) of each of them
+    } wk;
+  } u;
   double redd[kTWaves];
   float redf[kTWaves];
-  int32_t nx, overflow, nk, flag;
-  int32_t cur, n, stop;
-  float mstop;
-  uint32_t fl;
+  int32_t nx, overflow, flag;
 };
 __shared__ TreeShared g_tree;          // at file scope: functions that are not inlined reach it as LDS
 
@@ -176,7 +182,7 @@ __device__ void tree_row_pass(const TreeParams& p, int64_t b, int u) {
     float z = NAN;
     if (x >= 0 && int64_t(x) < V) {
       z = Vec<T>::load1(row + x);
-      sh.xs[atomicAdd(&sh.nx, 1)] = x;
+      sh.u.rp.xs[atomicAdd(&sh.nx, 1)] = x;
     }
     st_dev(p.zc + b * N + ci, z);
   }
@@ -195,12 +201,12 @@ __device__ void tree_row_pass(const TreeParams& p, int64_t b, int u) {
   // the masked elements this thread streams
   int nh = 0;
   for (int j = 0; j < nx; ++j) {
-    const int64_t x = sh.xs[j];
+    const int64_t x = sh.u.rp.xs[j];
     if (x < head || x >= tail0) continue;
     const int64_t vx = (x - head) / EPV;
     if (int(vx % kTBlock) != tid) continue;
     const int g = int(vx / (int64_t(kTU) * kTBlock)), k = int((vx / kTBlock) % kTU), e = int((x - head) % EPV);
-    if (nh < kHits) sh.hits[tid][nh] = (g << 8) | (k * EPV + e);
+    if (nh < kHits) sh.u.rp.hits[tid][nh] = (g << 8) | (k * EPV + e);
     ++nh;
   }
   if (nh > kHits) atomicOr(&sh.overflow, 1);
@@ -212,7 +218,7 @@ __device__ void tree_row_pass(const TreeParams& p, int64_t b, int u) {
   if (!slow) {
     for (int64_t i = tid; i < head; i += kTBlock) {
       float z = Vec<T>::load1(row + i);
-      if (in_list(sh.xs, nx, i)) z = -INFINITY;
+      if (in_list(sh.u.rp.xs, nx, i)) z = -INFINITY;
       t_absorb<1>(st, &z, c);
     }
     if (ngroups > 0) {
@@ -222,21 +228,21 @@ __device__ void tree_row_pass(const TreeParams& p, int64_t b, int u) {
       int64_t g = 0;
       for (; g + 1 < ngroups; g += 2) {
         t_load_group<T>(wb, vp, g + 1, nvec);
-        t_fold_group<T>(st, wa, g, nvec, nh, sh.hits[tid], c);
+        t_fold_group<T>(st, wa, g, nvec, nh, sh.u.rp.hits[tid], c);
         if (g + 2 < ngroups) t_load_group<T>(wa, vp, g + 2, nvec);
-        t_fold_group<T>(st, wb, g + 1, nvec, nh, sh.hits[tid], c);
+        t_fold_group<T>(st, wb, g + 1, nvec, nh, sh.u.rp.hits[tid], c);
       }
-      if (g < ngroups) t_fold_group<T>(st, wa, g, nvec, nh, sh.hits[tid], c);
+      if (g < ngroups) t_fold_group<T>(st, wa, g, nvec, nh, sh.u.rp.hits[tid], c);
     }
     for (int64_t i = tail0 + tid; i < V; i += kTBlock) {
       float z = Vec<T>::load1(row + i);
-      if (in_list(sh.xs, nx, i)) z = -INFINITY;
+      if (in_list(sh.u.rp.xs, nx, i)) z = -INFINITY;
       t_absorb<1>(st, &z, c);
     }
   } else {                                           // many child tokens in one thread's share: element by element
     for (int64_t i = tid; i < V; i += kTBlock) {
       float z = Vec<T>::load1(row + i);
-      if (in_list(sh.xs, nx, i)) z = -INFINITY;
+      if (in_list(sh.u.rp.xs, nx, i)) z = -INFINITY;
       t_absorb<1>(st, &z, c);
     }
   }
@@ -255,117 +261,129 @@ __device__ void tree_row_pass(const TreeParams& p, int64_t b, int u) {
   }
 }
 
-// The children of node `cur` in node order into sh.kid (sh.nk of them), by wave 0 (ballot compaction in order).
-__device__ __forceinline__ void list_children(int N, int cur) {
-  TreeShared& sh = g_tree;
-  const int lane = threadIdx.x & 63;
-  int base = 0;
-  for (int c0 = 1; c0 < N; c0 += 64) {
-    const int ci = c0 + lane;
-    const bool hit = ci < N && sh.par[ci] == cur;
-    const uint64_t m = wave_ballot(hit);
-    if (hit) sh.kid[base + lane_rank(m)] = ci;
-    base += __popcll(m);
-  }
-  if (lane == 0) sh.nk = base;
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// The walk of sequence b by the workgroup of its last row (sh.par / sh.tok hold its tree): every test in node order,
-// float64 weights from the row records, the outputs of every node and the draw job.
+// The walk of sequence b by wave 0 of the workgroup of its last row (sh.par / sh.tok hold its tree), with no barrier:
+// every row record and child logit the walk may read comes into LDS in one round of loads; at each node the children
+// are listed in node order (ballots), the tests are evaluated for all of them at once (p'(x) over the mass outside
+// the earlier siblings' tokens: the rest of the row plus a suffix sum of the later siblings' weights, positive terms
+// only), and the first passing child is found with a ballot. Writes the outputs of every node and the draw job.
 __device__ void tree_walk(const TreeParams& p, int64_t b) {
   TreeShared& sh = g_tree;
-  const int tid = threadIdx.x, wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
   const int N = p.N;
   const int64_t V = p.V;
   const double c = double(p.c);
   int bad = 0;
-  for (int ci = 1 + tid; ci < N; ci += kTBlock)
-    bad |= !(sh.par[ci] >= 0 && sh.par[ci] < ci) || !(sh.tok[ci] >= 0 && int64_t(sh.tok[ci]) < V);
-  bad = __syncthreads_or(bad);
-  for (int i = tid; i < N; i += kTBlock) {
+  for (int i = lane; i < N; i += 64) {
+    const TreeRow* r = p.rows + b * N + i;
+    const float m = ld_dev(&r->m);
+    const double s = ld_dev(&r->s);
+    const uint32_t rb = ld_dev(&r->bad);
+    const float z = i > 0 ? ld_dev(p.zc + b * N + i) : 0.f;
+    sh.u.wk.rm[i] = rb ? NAN : m;
+    sh.u.wk.rs[i] = s;
+    sh.u.wk.zk[i] = z;
+    if (i > 0) bad |= !(sh.par[i] >= 0 && sh.par[i] < i) || !(sh.tok[i] >= 0 && int64_t(sh.tok[i]) < V);
     p.accept[b * N + i] = 0;
     p.path[b * N + i] = -1;
     if (p.p_test) p.p_test[b * N + i] = NAN;
   }
-  if (tid == 0) { sh.cur = 0; sh.n = 0; sh.fl = bad ? SV_FLAG_ID_RANGE : 0u; sh.stop = bad ? -1 : -2; }
-  __syncthreads();
-  while (!bad && sh.stop == -2) {
-    const int cur = sh.cur;
-    if (wave == 0) list_children(N, cur);
-    __syncthreads();
-    const int nk = sh.nk;
-    // the row's maximum over all of it: the rest's maximum and the children's logits
-    const TreeRow* r = p.rows + b * N + cur;
-    const float mr = ld_dev(&r->m);
-    const double sr = ld_dev(&r->s);
-    const uint32_t rbad = ld_dev(&r->bad);
+  bad = __any(bad);
+  wave_sync();
+  uint32_t fl = bad ? SV_FLAG_ID_RANGE : 0u;
+  int cur = 0, n = 0, stop = -1;
+  float mstop = 0.f;
+  while (!bad) {
+    wave_sync();                                     // the previous level's reads of kid / pk are done
+    // children of cur in node order
+    int nk = 0;
+    for (int c0 = 1; c0 < N; c0 += 64) {
+      const int ci = c0 + lane;
+      const bool hit = ci < N && sh.par[ci] == cur;
+      const uint64_t m = wave_ballot(hit);
+      if (hit) sh.u.wk.kid[nk + lane_rank(m)] = ci;
+      nk += __popcll(m);
+    }
+    wave_sync();
+    // the row's maximum (the rest's and the children's) and its faults
     float mk = -INFINITY;
     int kbad = 0;
-    for (int j = tid; j < nk; j += kTBlock) {
-      const float z = ld_dev(p.zc + b * N + sh.kid[j]);
-      kbad |= !(z < INFINITY);                       // NaN or +inf
+    for (int j = lane; j < nk; j += 64) {
+      const float z = sh.u.wk.zk[sh.u.wk.kid[j]];
+      kbad |= !(z < INFINITY);
       mk = fmaxf(mk, z);
     }
-    kbad = __syncthreads_or(kbad);
-    mk = block_max<kTBlock>(mk, sh.redf);
+    mk = wave_max_f(mk);
+    kbad = __any(kbad);
+    const float mr = sh.u.wk.rm[cur];
     const float M = fmaxf(mr, mk);
-    if (rbad || kbad || M == -INFINITY) {            // a NaN or +inf in the row, or nothing but -inf
-      if (tid == 0) { sh.fl |= SV_FLAG_NONFINITE; sh.stop = -1; }
-      __syncthreads();
+    if (mr != mr || kbad || M == -INFINITY) {        // a NaN or +inf in the row, or nothing but -inf
+      fl |= SV_FLAG_NONFINITE;
+      stop = -1;
       break;
     }
-    for (int j = tid; j < nk; j += kTBlock) {
-      const int ci = sh.kid[j];
-      const float z = ld_dev(p.zc + b * N + ci);
-      sh.ex[j] = exp2((double(z) - double(M)) * c);
-      int f = 1;
-      for (int i = 0; i < j; ++i) f &= sh.tok[sh.kid[i]] != sh.tok[ci];
-      sh.first[j] = uint8_t(f);
+    const double rest = mr == -INFINITY ? 0.0 : sh.u.wk.rs[cur] * exp2((double(mr) - double(M)) * c);
+    // p'(x) of every child, chunks of 64 from the last: a child's denominator is the rest plus the weights of the
+    // first holders of the tokens of it and of its later siblings (reverse scan within a chunk, carry across chunks)
+    double carry = 0.0;
+    for (int c0 = ((nk + 63) / 64 - 1) * 64; c0 >= 0; c0 -= 64) {
+      const int j = c0 + lane;
+      const bool valid = j < nk;
+      const int ci = valid ? sh.u.wk.kid[j] : 0;
+      int first = valid;
+      for (int i = 0; i < j && first && valid; ++i) first = sh.tok[sh.u.wk.kid[i]] != sh.tok[ci];
+      const double ex = first ? exp2((double(sh.u.wk.zk[ci]) - double(M)) * c) : 0.0;
+      const double rev = wave_incl_scan(__shfl(ex, 63 - lane));   // suffix sums, read back in lane order
+      const double suffix = __shfl(rev, 63 - lane);
+      if (valid) sh.u.wk.pk[j] = first ? ex / (rest + (carry + suffix)) : 0.0;
+      carry += readlane_d(rev, 63);
     }
-    __syncthreads();
-    if (tid == 0) {
-      // the rest of the row in the same units; the mass outside the rejected tokens before test j is the rest plus
-      // the weights of the first holders of the tokens of children j, j+1, ... (positive terms only)
-      const double rest = mr == -INFINITY ? 0.0 : sr * exp2((double(mr) - double(M)) * c);
-      double tailsum = 0.0;
-      for (int j = nk - 1; j >= 0; --j) {
-        if (sh.first[j]) tailsum += sh.ex[j];
-        sh.ex[j] = sh.first[j] ? sh.ex[j] / (rest + tailsum) : 0.0;     // p'(x) of child j
-      }
-      int next = -1;
-      for (int j = 0; j < nk; ++j) {
-        const int ci = sh.kid[j];
-        const double P = sh.ex[j];
-        if (p.p_test) p.p_test[b * N + ci] = float(P);
-        if (double(p.ua[b * N + ci]) < fmin(1.0, P)) { next = ci; break; }
-      }
-      if (next >= 0) {
-        p.accept[b * N + next] = 1;
-        p.path[b * N + sh.n] = next;
-        sh.n += 1;
-        sh.cur = next;
-      } else {
-        sh.stop = cur;
-        sh.mstop = M;
-      }
+    wave_sync();
+    // the tests in node order: the first passing child is accepted
+    int next = -1;
+    for (int c0 = 0; c0 < nk && next < 0; c0 += 64) {
+      const int j = c0 + lane;
+      const bool valid = j < nk;
+      const int ci = valid ? sh.u.wk.kid[j] : 0;
+      const double P = valid ? sh.u.wk.pk[j] : 0.0;
+      const float u = valid ? p.ua[b * N + ci] : 1.f;
+      const uint64_t pass = wave_ballot(valid && double(u) < fmin(1.0, P));
+      const int jstar = pass ? c0 + __builtin_ctzll(pass) : INT_MAX;
+      if (valid && j <= jstar && p.p_test) p.p_test[b * N + ci] = float(P);
+      if (pass) next = __builtin_amdgcn_readlane(ci, __builtin_ctzll(pass));
     }
-    __syncthreads();
+    if (next < 0) {
+      stop = cur;
+      mstop = M;
+      break;
+    }
+    if (lane == 0) {
+      p.accept[b * N + next] = 1;
+      p.path[b * N + n] = next;
+    }
+    ++n;
+    cur = next;
   }
-  if (tid == 0) {
-    const bool fatal = sh.stop < 0;
-    TreeJob j{};
-    j.stop = fatal ? -1 : sh.stop;
-    j.m = fatal ? 0.f : sh.mstop;
-    j.u = fatal ? 0.f : p.us[b * N + sh.stop];
-    j.flags = sh.fl;
-    p.jobs[b] = j;
-    p.n_acc[b] = fatal ? -1 : sh.n;
+  if (lane == 0) {
+    const bool fatal = stop < 0;
+    TreeJob jb{};
+    jb.stop = stop;
+    jb.m = fatal ? 0.f : mstop;
+    jb.u = fatal ? 0.f : p.us[b * N + stop];
+    jb.flags = fl;
+    p.jobs[b] = jb;
+    p.n_acc[b] = fatal ? -1 : n;
     p.out_token[b] = -1;
-    if (p.flags) p.flags[b] = sh.fl;
+    if (p.flags) p.flags[b] = fl;
   }
-  if (sh.stop < 0) {                                 // a failed sequence: no accepted node, no tested node
-    __syncthreads();
-    for (int i = tid; i < N; i += kTBlock) {
+  if (stop < 0) {                                    // a failed sequence: no accepted node, no tested node
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int i = lane; i < N; i += 64) {
       p.accept[b * N + i] = 0;
       p.path[b * N + i] = -1;
       if (p.p_test) p.p_test[b * N + i] = NAN;
@@ -394,7 +412,7 @@ __global__ __launch_bounds__(kTBlock) void k_tree_rows(TreeParams p) {
     }
   }
   __syncthreads();
-  if (!sh.flag) return;
+  if (!sh.flag || threadIdx.x >= 64) return;       // the walk is wave 0's
   tree_walk(p, b);
   if (threadIdx.x == 0) st_dev(p.ctr1 + b, int32_t(0));   // ready for the next call
 }
@@ -420,7 +438,7 @@ __device__ __forceinline__ void t_chunk_weights(const T* row, bool vec, int64_t 
   for (int e = 0; e < kTPer; ++e) w[e] = fexp_scaled(xarg(z[e], c2, nm));
   if (!all) {
     for (int j = 0; j < nx; ++j) {
-      const int64_t d = int64_t(g_tree.xs[j]) - i0;
+      const int64_t d = int64_t(g_tree.u.rp.xs[j]) - i0;
 #pragma unroll
       for (int e = 0; e < kTPer; ++e) w[e] = d == e ? 0.0 : w[e];
     }
@@ -491,16 +509,22 @@ __global__ __launch_bounds__(kTBlock) void k_tree_draw(TreeParams p) {
   const int tid = threadIdx.x, wave = tid >> 6;
   const int64_t b = int64_t(blockIdx.x) / p.ntask;
   const int task = int(int64_t(blockIdx.x) % p.ntask);
-  const TreeJob job = p.jobs[b];                     // written by the first launch
+  const int N = p.N;
+  // the job (written by the first launch) and the tree are requested together: the children of the stop node (all
+  // rejected) give the tokens to remove
+  const TreeJob job = p.jobs[b];
+  for (int i = tid; i < N; i += kTBlock) {
+    sh.par[i] = p.parent[b * N + i];
+    sh.tok[i] = p.token[b * N + i];
+  }
   fexp_fill_table();
   if (tid == 0) sh.nx = 0;
   __syncthreads();
-  const int N = p.N;
-  if (job.stop >= 0 && job.stop < N) {               // the stop node's children (all rejected): tokens to remove
+  if (job.stop >= 0 && job.stop < N) {
     for (int ci = 1 + tid; ci < N; ci += kTBlock)
-      if (p.parent[b * N + ci] == job.stop) {
-        const int x = p.token[b * N + ci];
-        if (x >= 0 && int64_t(x) < p.V) sh.xs[atomicAdd(&sh.nx, 1)] = x;
+      if (sh.par[ci] == job.stop) {
+        const int x = sh.tok[ci];
+        if (x >= 0 && int64_t(x) < p.V) sh.u.rp.xs[atomicAdd(&sh.nx, 1)] = x;
       }
   }
   __syncthreads();
@@ -558,7 +582,11 @@ TreePlan make_tree_plan(int64_t B, int32_t N, int64_t V) {
   TreePlan pl;
   pl.B = B; pl.N = N; pl.V = V;
   pl.nch = (V + kTChunk - 1) / kTChunk;
-  pl.task_chunks = 16;
+  // draw tasks: the sequences' tasks together about fill one resident round (1024 workgroups), each task at least
+  // 4 chunks (one per wave)
+  const int64_t want = std::max<int64_t>(1, 1024 / std::max<int64_t>(B, 1));
+  int64_t tc = std::max<int64_t>(4, (pl.nch + want - 1) / want);
+  pl.task_chunks = int32_t(std::min<int64_t>(tc, std::max<int64_t>(pl.nch, 1)));
   pl.ntask = int32_t((pl.nch + pl.task_chunks - 1) / pl.task_chunks);
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   size_t off = kWsHeaderBytes;
