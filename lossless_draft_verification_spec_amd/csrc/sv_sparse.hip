@@ -7,10 +7,20 @@
 // adds the first-rejection scan and the draw from the correction distribution at that slot (or a bonus draw from p's
 // support of row gamma), as the dense path does.
 //
-// One workgroup (4 waves) per sequence; each wave handles one slot at a time with the slot's supports staged in LDS.
-// Every sum is float64 and runs strictly in slot order, so all outputs equal the float64 evaluation of the
-// definitions: the accept test u * q_spec < p_spec is exact for float32 inputs, and the draw index is chosen on
-// the same running sums a sequential CPU evaluation forms. Ids are matched by direct comparison (no sorting).
+// One workgroup of 8 waves per sequence (three fit a compute unit); the slots go in batches whose correction weights
+// fit the LDS table (one batch for the usual sizes, e.g. 16 slots of 64-entry supports).
+//  1. a wave per slot (slots wave, wave + 8, ...), the slot's supports in its lanes (entry e in lane e % 64, register
+//     e / 64): the rows are checked; p_spec and q_spec come from a ballot of the entries whose id is the drafted one;
+//     the accept test; then each p entry's q probability, every lane comparing its p ids with one q entry at a time
+//     (q staged in LDS), and the weights max(p - q_on_p, 0) into the LDS table with their ids. With one batch, the
+//     checks of every row end before any output is written; with several, all rows are checked in a pass before.
+//  2. one thread per slot sums its weights in slot order (and keeps the running sums of the slot to be drawn from);
+//     the outputs and the normalised correction distribution are written by all threads.
+//  3. the draw, by one wave: a ballot over the stored running sums finds the first that exceeds t.
+// Every float64 sum runs strictly in support-slot order, as a sequential CPU evaluation forms it (a q_on_p term has
+// one matching q entry unless q's ids repeat, in which case that slot's matches are summed in slot order as well),
+// so all outputs equal the float64 evaluation of the definitions: the accept test u * q_spec < p_spec is exact for
+// float32 inputs, and the draw index is chosen on the same running sums.
 
 #include <hip/hip_runtime.h>
 
@@ -24,77 +34,184 @@
 namespace sv {
 namespace {
 
-constexpr int kBlock = 256;
+constexpr int kBlock = 512;
 constexpr int kWaves = kBlock / 64;
-
-struct WaveLds {
-  int32_t pid[SV_MAX_K];
-  float pp[SV_MAX_K];
-  int32_t qid[SV_MAX_K];
-  float qp[SV_MAX_K];
-  double w[SV_MAX_K];     // draw weights of the slot (correction, or p when the correction is empty)
-};
+constexpr int kEntMax = SV_MAX_K / 64;  // support entries per lane for the largest supports
+constexpr int kTable = 1536;            // float64 weights (and their ids) the LDS tables hold: a batch of slots
+constexpr int kBatchMax = 256;          // slots per batch at most
 
 __device__ __forceinline__ bool bad_prob(float v) { return !(v >= 0.f) || v == INFINITY; }   // NaN, <0, inf
 
-// Stage row j's supports into the wave's LDS area.
-__device__ __forceinline__ void stage(WaveLds& L, const int32_t* pi, const float* pp, int kp, const int32_t* qi,
-                                      const float* qp, int kq, int lane) {
-  for (int i = lane; i < kp; i += 64) { L.pid[i] = pi[i]; L.pp[i] = pp[i]; }
-  if (qi)
-    for (int i = lane; i < kq; i += 64) { L.qid[i] = qi[i]; L.qp[i] = qp[i]; }
+// One support row in the lanes of a wave: entry e = 64 m + lane in (id[m], pr[m]); entries past k are id -1, 0.
+// kEnt entries per lane hold supports of up to 64 kEnt entries.
+template <int kEnt>
+struct Row {
+  int32_t id[kEnt];
+  float pr[kEnt];
+};
+template <int kEnt>
+__device__ __forceinline__ Row<kEnt> load_row(const int32_t* ids, const float* pr, int k, int lane) {
+  Row<kEnt> r;
+#pragma unroll
+  for (int m = 0; m < kEnt; ++m) {
+    const int e = m * 64 + lane;
+    r.id[m] = e < k ? ids[e] : -1;
+    r.pr[m] = e < k ? pr[e] : 0.f;
+  }
+  return r;
+}
+// Whether a row holds a probability that is NaN, negative or +inf (bad_nf), or an id outside [0, vocab) (bad_id).
+template <int kEnt>
+__device__ __forceinline__ void check_row(const Row<kEnt>& r, int k, int64_t vocab, int& bad_nf, int& bad_id) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int m = 0; m < kEnt; ++m) {
+    if (m * 64 + lane < k) {
+      bad_nf |= bad_prob(r.pr[m]);
+      if (vocab > 0) bad_id |= (r.id[m] < 0 || r.id[m] >= vocab);
+    }
+  }
 }
 
-// Correction weights max(p_i - q_on_p_i, 0) of the staged row into L.w; returns their slot-order sum.
-__device__ __forceinline__ double correction(WaveLds& L, int kp, int kq, int lane) {
-#pragma clang fp contract(off)
-  for (int i = lane; i < kp; i += 64) {
-    const int id = L.pid[i];
-    double qop = 0.0;
-    for (int l = 0; l < kq; ++l) qop += (L.qid[l] == id) ? double(L.qp[l]) : 0.0;
-    const double r = double(L.pp[i]) - qop;
-    L.w[i] = r > 0.0 ? r : 0.0;
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+// Sum, in slot order, of the probabilities of the entries whose id is x (usually one entry or none).
+template <int kEnt>
+__device__ __forceinline__ double match_sum(const Row<kEnt>& r, int k, int32_t x) {
   double s = 0.0;
-  for (int i = 0; i < kp; ++i) s += L.w[i];
+#pragma unroll
+  for (int m = 0; m < kEnt; ++m) {
+    if (m * 64 >= k) break;
+    uint64_t hit = __ballot(r.id[m] == x && m * 64 + int(threadIdx.x & 63) < k);
+    while (hit) {
+      const int l = __builtin_ctzll(hit);
+      hit &= hit - 1;
+      s += double(__uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(r.pr[m]), l)));
+    }
+  }
   return s;
 }
 
-// Replace the weights by p (the empty-residual fallback); returns the slot-order sum.
-__device__ __forceinline__ double weights_from_p(WaveLds& L, int kp, int lane) {
-  for (int i = lane; i < kp; i += 64) L.w[i] = double(L.pp[i]);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  double s = 0.0;
-  for (int i = 0; i < kp; ++i) s += L.w[i];
-  return s;
-}
-
-// Smallest slot whose slot-order running sum of L.w exceeds t; the last positive slot if none (rounding).
-__device__ __forceinline__ int draw_slot(const WaveLds& L, int kp, double t) {
-  double acc = 0.0;
-  int found = -1, last = -1;
-  for (int i = 0; i < kp; ++i) {
-    const double w = L.w[i];
-    acc += w;
-    if (w > 0.0) last = i;
-    if (found < 0 && acc > t) found = i;
-  }
-  return found >= 0 ? found : last;
-}
-
-struct SpParams {
-  SparseArgs a;
+struct SpShared {
+  double w[kTable];                    // weights of the batch's slots, row stride ldw
+  int32_t pid[kTable];                 // their p ids
+  double S[kBatchMax];                 // per slot of the batch: its normaliser
+  int2 q[kWaves][SV_MAX_K];            // per wave: the q support of its slot (id, probability bits)
+  double cum[SV_MAX_K];                // the drawn slot's running sums of its weights (slot order)
+  float ps[kBatchMax], qs[kBatchMax];  // per slot of the batch: p_spec, q_spec
+  float us[kBatchMax];                 // per slot of the batch: its draw uniform
+  uint8_t acc[SV_MAX_GAMMA];
+  uint8_t empty[kBatchMax];            // per slot of the batch: no leftover mass (the weights are p)
+  int32_t k;
+  int32_t tok;
 };
 
+// Sum of n weights in slot order (one thread), their values requested four at a time; with cum, every running sum
+// is stored too.
+__device__ __forceinline__ double seq_sum(const double* w, int n, double* cum) {
+  double s = 0.0;
+  int e = 0;
+  for (; e + 4 <= n; e += 4) {
+    double v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = w[e + i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s += v[i];
+      if (cum) cum[e + i] = s;
+    }
+  }
+  for (; e < n; ++e) {
+    s += w[e];
+    if (cum) cum[e] = s;
+  }
+  return s;
+}
+
+// The draw over a row of n weights whose running sums are in cum (by one wave): the smallest slot whose running sum
+// exceeds t; the last slot with positive weight if none (rounding); -1 when no weight is positive.
+__device__ __forceinline__ int wave_draw(const double* w, const double* cum, int n, double t) {
+  const int lane = threadIdx.x & 63;
+  for (int e0 = 0; e0 < n; e0 += 64) {
+    const uint64_t hit = __ballot(e0 + lane < n && cum[e0 + lane] > t);
+    if (hit) return e0 + __builtin_ctzll(hit);
+  }
+  for (int e0 = (n - 1) / 64 * 64; e0 >= 0; e0 -= 64) {
+    const uint64_t pos = __ballot(e0 + lane < n && w[e0 + lane] > 0.0);
+    if (pos) return e0 + 63 - __builtin_clzll(pos);
+  }
+  return -1;
+}
+
+// The correction weights max(p_e - q_on_p_e, 0) of one slot (by one wave) into w, and the p ids into ids: each p
+// entry's q probability is found by comparing every lane's p ids with one q entry at a time (q is staged in qs from
+// the lanes that hold it); when q repeats an id of p, that slot's matches are summed again in float64, in q's slot
+// order.
+template <int kEnt>
+__device__ __forceinline__ void slot_weights(const Row<kEnt>& P, const Row<kEnt>& Q, int kp, int kq, int2* qs,
+                                             double* w, int32_t* ids) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int m = 0; m < kEnt; ++m)
+    if (m * 64 + lane < kq) qs[m * 64 + lane] = make_int2(Q.id[m], __float_as_int(Q.pr[m]));
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float qm[kEnt];
+  int nm[kEnt];
+#pragma unroll
+  for (int m = 0; m < kEnt; ++m) { qm[m] = 0.f; nm[m] = 0; }
+#pragma unroll 4
+  for (int l = 0; l < kq; ++l) {
+    const int2 qe = qs[l];
+#pragma unroll
+    for (int m = 0; m < kEnt; ++m) {
+      if (m * 64 >= kp) break;
+      const bool hit = P.id[m] == qe.x;
+      qm[m] = hit ? __int_as_float(qe.y) : qm[m];
+      nm[m] += hit ? 1 : 0;
+    }
+  }
+  double qop[kEnt];
+#pragma unroll
+  for (int m = 0; m < kEnt; ++m) qop[m] = double(qm[m]);
+  bool multi = false;
+#pragma unroll
+  for (int m = 0; m < kEnt; ++m) multi |= nm[m] > 1;
+  if (__any(multi)) {
+#pragma unroll
+    for (int m = 0; m < kEnt; ++m) qop[m] = 0.0;
+    for (int l = 0; l < kq; ++l) {
+      const int2 qe = qs[l];
+#pragma unroll
+      for (int m = 0; m < kEnt; ++m)
+        if (m * 64 < kp) qop[m] += (P.id[m] == qe.x) ? double(__int_as_float(qe.y)) : 0.0;
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < kEnt; ++m) {
+#pragma clang fp contract(off)
+    const int e = m * 64 + lane;
+    const double r = double(P.pr[m]) - qop[m];
+    if (e < kp) {
+      w[e] = r > 0.0 ? r : 0.0;
+      ids[e] = P.id[m];
+    }
+  }
+}
+
+// A slot's normaliser (one thread), with the running sums when cum is given; no leftover mass: the weights become p.
+__device__ __forceinline__ double slot_norm(double* w, const float* p_pr, int kp, double* cum, bool& empty) {
+  double S = seq_sum(w, kp, cum);
+  empty = !(S > 0.0);
+  if (empty) {
+    for (int e = 0; e < kp; ++e) w[e] = double(p_pr[e]);
+    S = seq_sum(w, kp, cum);
+  }
+  return S;
+}
+
+template <int kEnt>
 __global__ __launch_bounds__(kBlock) void k_sparse(SparseArgs a) {
-  __shared__ WaveLds lds[kWaves];
-  __shared__ uint8_t s_acc[SV_MAX_GAMMA];
-  __shared__ int s_k;
+  __shared__ SpShared sh;
 
   const int64_t b = blockIdx.x;
   const int G = a.G, kp = a.kp, kq = a.kq;
@@ -104,25 +221,13 @@ __global__ __launch_bounds__(kBlock) void k_sparse(SparseArgs a) {
   const float* P_pr = a.p_probs + b * int64_t(rows_p) * kp;
   const int32_t* Q_ids = a.q_ids + b * int64_t(G) * kq;
   const float* Q_pr = a.q_probs + b * int64_t(G) * kq;
+  const int ldw = kp | 1;                            // odd row stride: the lanes of the normaliser step use distinct banks
+  const int nb = min(kTable / ldw, kBatchMax);       // slots per batch
+  const bool single = G <= nb;                       // one batch: checked while it is read (the usual case)
+  const bool weights = single || a.corr;             // weights of every slot (else only the rejected slot's, at the end)
 
-  // validation of every verified row (rows 0 .. G-1) before anything is written
   int bad_id = 0, bad_nf = 0;
-  for (int64_t i = tid; i < int64_t(G) * kp; i += kBlock) {
-    bad_nf |= bad_prob(P_pr[i]);
-    if (a.vocab > 0) bad_id |= (P_ids[i] < 0 || P_ids[i] >= a.vocab);
-  }
-  for (int64_t i = tid; i < int64_t(G) * kq; i += kBlock) {
-    bad_nf |= bad_prob(Q_pr[i]);
-    if (a.vocab > 0) bad_id |= (Q_ids[i] < 0 || Q_ids[i] >= a.vocab);
-  }
-  if (a.vocab > 0)
-    for (int j = tid; j < G; j += kBlock) bad_id |= (a.spec[b * G + j] < 0 || a.spec[b * G + j] >= a.vocab);
-  bad_id = __syncthreads_or(bad_id);
-  bad_nf = __syncthreads_or(bad_nf);
-  const bool fatal = bad_id || bad_nf;
-  uint32_t flg = (bad_id ? SV_FLAG_ID_RANGE : 0u) | (bad_nf ? SV_FLAG_NONFINITE : 0u);
-
-  if (fatal) {
+  auto fail = [&]() {
     for (int j = tid; j < G; j += kBlock) {
       if (a.accept) a.accept[b * G + j] = 0;
       if (a.p_spec) a.p_spec[b * G + j] = NAN;
@@ -133,105 +238,188 @@ __global__ __launch_bounds__(kBlock) void k_sparse(SparseArgs a) {
     if (tid == 0) {
       a.n_acc[b] = -1;
       a.token[b] = -1;
-      if (a.flags) a.flags[b] = flg;
+      if (a.flags) a.flags[b] = (bad_id ? SV_FLAG_ID_RANGE : 0u) | (bad_nf ? SV_FLAG_NONFINITE : 0u);
     }
-    return;
+  };
+  if (!single) {                                     // every verified row is checked before anything is written
+    for (int64_t i = tid; i < int64_t(G) * kp; i += kBlock) {
+      bad_nf |= bad_prob(P_pr[i]);
+      if (a.vocab > 0) bad_id |= (P_ids[i] < 0 || P_ids[i] >= a.vocab);
+    }
+    for (int64_t i = tid; i < int64_t(G) * kq; i += kBlock) {
+      bad_nf |= bad_prob(Q_pr[i]);
+      if (a.vocab > 0) bad_id |= (Q_ids[i] < 0 || Q_ids[i] >= a.vocab);
+    }
+    if (a.vocab > 0)
+      for (int j = tid; j < G; j += kBlock) bad_id |= (a.spec[b * G + j] < 0 || a.spec[b * G + j] >= a.vocab);
+    bad_id = __syncthreads_or(bad_id);
+    bad_nf = __syncthreads_or(bad_nf);
+    if (bad_id || bad_nf) { fail(); return; }
   }
 
-  WaveLds& L = lds[wv];
+  uint32_t flg = 0;
   int qzero_any = 0;
-  for (int j0 = 0; j0 < G; j0 += kWaves) {
-    const int j = j0 + wv;
-    if (j < G) {
-      stage(L, P_ids + int64_t(j) * kp, P_pr + int64_t(j) * kp, kp, Q_ids + int64_t(j) * kq,
-            Q_pr + int64_t(j) * kq, kq, lane);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const int x = a.spec[b * G + j];
-      double ps = 0.0, qs = 0.0;
-      for (int i = 0; i < kp; ++i) ps += (L.pid[i] == x) ? double(L.pp[i]) : 0.0;
-      for (int l = 0; l < kq; ++l) qs += (L.qid[l] == x) ? double(L.qp[l]) : 0.0;
-      const double u = double(a.ua[b * G + j]);
-      const bool acc = (qs > 0.0) && (u * qs < ps);
-      qzero_any |= (qs == 0.0);
-      double S = correction(L, kp, kq, lane);
-      if (!(S > 0.0)) S = weights_from_p(L, kp, lane);
-      if (a.corr)
-        for (int i = lane; i < kp; i += 64) a.corr[(b * G + j) * int64_t(kp) + i] = float(L.w[i] / S);
-      if (lane == 0) {
-        s_acc[j] = acc ? 1 : 0;
-        if (a.accept) a.accept[b * G + j] = acc ? 1 : 0;
-        if (a.p_spec) a.p_spec[b * G + j] = float(ps);
-        if (a.q_spec) a.q_spec[b * G + j] = float(qs);
+  if (tid == 0) { sh.k = G; sh.tok = -1; }
+  for (int j0 = 0; j0 < G; j0 += nb) {
+    const int j1 = min(j0 + nb, G);
+    // 1. a wave per slot: accept test and, when needed, the correction weights
+    for (int j = j0 + wv; j < j1; j += kWaves) {
+      const Row<kEnt> P = load_row<kEnt>(P_ids + int64_t(j) * kp, P_pr + int64_t(j) * kp, kp, lane);
+      const Row<kEnt> Q = load_row<kEnt>(Q_ids + int64_t(j) * kq, Q_pr + int64_t(j) * kq, kq, lane);
+      const int32_t x = a.spec[b * G + j];
+      const float u = a.ua[b * G + j];
+      const float uds = a.us[b * (G + 1) + j];
+      if (single) {
+        check_row(P, kp, a.vocab, bad_nf, bad_id);
+        check_row(Q, kq, a.vocab, bad_nf, bad_id);
+        if (a.vocab > 0) bad_id |= (x < 0 || x >= a.vocab);
       }
+      const double ps = match_sum(P, kp, x);
+      const double qs = match_sum(Q, kq, x);
+      const bool acc = (qs > 0.0) && (double(u) * qs < ps);
+      qzero_any |= (qs == 0.0);
+      if (lane == 0) {
+        sh.acc[j] = acc ? 1 : 0;
+        sh.ps[j - j0] = float(ps);
+        sh.qs[j - j0] = float(qs);
+        sh.us[j - j0] = uds;
+      }
+      if (weights) slot_weights(P, Q, kp, kq, sh.q[wv], sh.w + (j - j0) * ldw, sh.pid + (j - j0) * ldw);
+    }
+    if (single) {
+      bad_id = __syncthreads_or(bad_id);
+      bad_nf = __syncthreads_or(bad_nf);
+      if (bad_id || bad_nf) { fail(); return; }
+    }
+    __syncthreads();
+    if (single && wv == 0) {                         // the first rejection (G: none)
+      int k = G;
+      for (int i0 = 0; i0 < G; i0 += 64) {
+        const uint64_t rej = __ballot(i0 + lane < G && sh.acc[i0 + lane] == 0);
+        if (rej) {
+          k = i0 + __builtin_ctzll(rej);
+          break;
+        }
+      }
+      if (lane == 0) sh.k = k;
+    }
+    __syncthreads();
+    const int k = sh.k;                              // known here only with a single batch
+    // 2. normalisers, one thread per slot
+    if (weights) {
+      for (int s = tid; s < j1 - j0; s += kBlock) {
+        bool empty;
+        sh.S[s] = slot_norm(sh.w + s * ldw, P_pr + int64_t(j0 + s) * kp, kp, j0 + s == k ? sh.cum : nullptr, empty);
+        sh.empty[s] = empty ? 1 : 0;
+      }
+    }
+    __syncthreads();
+    // 3. the batch's outputs, then (single batch) the draw
+    for (int s = tid; s < j1 - j0; s += kBlock) {
+      if (a.accept) a.accept[b * G + j0 + s] = sh.acc[j0 + s];
+      if (a.p_spec) a.p_spec[b * G + j0 + s] = sh.ps[s];
+      if (a.q_spec) a.q_spec[b * G + j0 + s] = sh.qs[s];
+    }
+    if (a.corr) {
+      for (int i = tid; i < (j1 - j0) * kp; i += kBlock) {
+        const int s = i / kp, e = i - s * kp;
+        a.corr[(b * G + j0 + s) * int64_t(kp) + e] = float(sh.w[s * ldw + e] / sh.S[s]);
+      }
+    }
+    if (single && k < G && wv == 0) {
+      const int sl = k - j0;
+      const int e = wave_draw(sh.w + sl * ldw, sh.cum, kp, double(sh.us[sl]) * sh.S[sl]);
+      if (lane == 0) sh.tok = e >= 0 ? sh.pid[sl * ldw + e] : -1;
+      if (sh.empty[sl]) flg |= SV_FLAG_EMPTY_RESIDUAL;
     }
     __syncthreads();
   }
   qzero_any = __syncthreads_or(qzero_any);
   if (qzero_any) flg |= SV_FLAG_Q_ZERO;
-
-  // first rejection; then the draw, by wave 0
-  if (tid == 0) {
-    int k = G;
-    for (int j = 0; j < G; ++j)
-      if (!s_acc[j]) { k = j; break; }
-    s_k = k;
-  }
-  __syncthreads();
-  const int k = s_k;
   if (wv != 0) return;
-  int tok = -1;
-  if (k < G) {
-    stage(L, P_ids + int64_t(k) * kp, P_pr + int64_t(k) * kp, kp, Q_ids + int64_t(k) * kq, Q_pr + int64_t(k) * kq,
-          kq, lane);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    double S = correction(L, kp, kq, lane);
-    if (!(S > 0.0)) {
-      S = weights_from_p(L, kp, lane);
-      flg |= SV_FLAG_EMPTY_RESIDUAL;
+  int k = sh.k;
+  if (!single) {                                     // several batches: the first rejection, then its correction
+    k = G;
+    for (int i0 = 0; i0 < G; i0 += 64) {
+      const uint64_t rej = __ballot(i0 + lane < G && sh.acc[i0 + lane] == 0);
+      if (rej) {
+        k = i0 + __builtin_ctzll(rej);
+        break;
+      }
     }
-    const double t = double(a.us[b * (G + 1) + k]) * S;
-    const int slot = draw_slot(L, kp, t);
-    tok = slot >= 0 ? L.pid[slot] : -1;
-  } else if (a.bonus) {
-    const int32_t* bi = P_ids + int64_t(G) * kp;
-    const float* bp = P_pr + int64_t(G) * kp;
+    if (k < G) {
+      const Row<kEnt> P = load_row<kEnt>(P_ids + int64_t(k) * kp, P_pr + int64_t(k) * kp, kp, lane);
+      const Row<kEnt> Q = load_row<kEnt>(Q_ids + int64_t(k) * kq, Q_pr + int64_t(k) * kq, kq, lane);
+      slot_weights(P, Q, kp, kq, sh.q[0], sh.w, sh.pid);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      double S = 0.0;
+      int empty = 0;
+      if (lane == 0) {
+        bool em;
+        S = slot_norm(sh.w, P_pr + int64_t(k) * kp, kp, sh.cum, em);
+        empty = em;
+      }
+      S = __shfl(S, 0);
+      empty = __shfl(empty, 0);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int e = wave_draw(sh.w, sh.cum, kp, double(a.us[b * (G + 1) + k]) * S);
+      if (lane == 0) sh.tok = e >= 0 ? sh.pid[e] : -1;
+      if (empty) flg |= SV_FLAG_EMPTY_RESIDUAL;
+    }
+  }
+  if (k == G && a.bonus) {                           // every slot accepted: the bonus draw from p's row gamma (wave 0)
+    const Row<kEnt> P = load_row<kEnt>(P_ids + int64_t(G) * kp, P_pr + int64_t(G) * kp, kp, lane);
     int bad = 0, badid = 0;
-    for (int i = lane; i < kp; i += 64) {
-      bad |= bad_prob(bp[i]);
-      if (a.vocab > 0) badid |= (bi[i] < 0 || bi[i] >= a.vocab);
-    }
-    bad = __any(bad);          // wave-wide
+    check_row(P, kp, a.vocab, bad, badid);
+    bad = __any(bad);
     badid = __any(badid);
     if (bad) {
       flg |= SV_FLAG_NONFINITE;
     } else if (badid) {
       flg |= SV_FLAG_ID_RANGE;
     } else {
-      stage(L, bi, bp, kp, nullptr, nullptr, 0, lane);
+#pragma unroll
+      for (int m = 0; m < kEnt; ++m)
+        if (m * 64 + lane < kp) sh.w[m * 64 + lane] = double(P.pr[m]);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const double S = weights_from_p(L, kp, lane);
-      const double t = double(a.us[b * (G + 1) + G]) * S;
-      const int slot = draw_slot(L, kp, t);
-      tok = slot >= 0 ? L.pid[slot] : -1;
+      double S = 0.0;
+      if (lane == 0) S = seq_sum(sh.w, kp, sh.cum);
+      S = __shfl(S, 0);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int e = wave_draw(sh.w, sh.cum, kp, double(a.us[b * (G + 1) + G]) * S);
+      int32_t id = -1;
+#pragma unroll
+      for (int m = 0; m < kEnt; ++m)
+        if (e >= m * 64 && e < m * 64 + 64) id = __builtin_amdgcn_readlane(P.id[m], e - m * 64);
+      if (lane == 0) sh.tok = id;
     }
   }
-  if (lane == 0) {
-    a.n_acc[b] = k;
-    a.token[b] = tok;
-    if (a.flags) a.flags[b] = flg;
-  }
+  if (lane != 0) return;
+  a.n_acc[b] = k;
+  a.token[b] = sh.tok;
+  if (a.flags) a.flags[b] = flg;
 }
 
 }  // namespace
 
 hipError_t launch_sparse(const SparseArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(k_sparse, dim3(unsigned(a.B)), dim3(kBlock), 0, stream, a);
+  // the narrowest register layout that holds both supports
+  const int k = a.kp > a.kq ? a.kp : a.kq;
+  if (k <= 64) {
+    hipLaunchKernelGGL(k_sparse<1>, dim3(unsigned(a.B)), dim3(kBlock), 0, stream, a);
+  } else if (k <= 128) {
+    hipLaunchKernelGGL(k_sparse<2>, dim3(unsigned(a.B)), dim3(kBlock), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(k_sparse<kEntMax>, dim3(unsigned(a.B)), dim3(kBlock), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
