@@ -159,11 +159,13 @@ __device__ __forceinline__ void fold_chunk(const uint4 (&w)[kGrU], int c, int64_
   }
   if constexpr (CONF) {                    // sum of exp(z - m) with m the running maximum (masked-off lanes: -inf)
     if (m > -INFINITY) {
+      // exp(z - m) = 2^(z log2(e) - m log2(e)): one fused multiply-add per element before the exp2
+      const float nml = -(m * kLog2e);
       float acc = 0.0f;
 #pragma unroll
       for (int u = 0; u < kGrU; ++u)
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc += ex2f((v[u][e] - m) * kLog2e);
+        for (int e = 0; e < E; ++e) acc += ex2f(fmaf(v[u][e], kLog2e, nml));
       sum += acc;
     }
   }
