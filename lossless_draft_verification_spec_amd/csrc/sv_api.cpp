@@ -76,7 +76,7 @@ size_t sv_workspace_bytes(int kind, int64_t B, int32_t gamma, int64_t V_or_k) {
       return sv::greedy_workspace_bytes(B, gamma, V_or_k);
     case SV_KIND_TREE:
       if (V_or_k > kMaxI32 || gamma > SV_MAX_TREE_NODES) return bad;
-      return sv::make_tree_plan(B, gamma, V_or_k).total;
+      return sv::make_tree_plan(B, gamma, V_or_k, SV_F32, 1).total;
     default:
       return bad;
   }
@@ -304,8 +304,8 @@ int sv_verify_tree(const void* target_logits, int64_t t_seq, int64_t t_row, int 
   const void* ptrs[] = {parent, token, u_accept, u_sample, n_accepted, path, out_token, p_test, flags};
   for (const void* p : ptrs)
     if (p && !aligned(p, 4)) return SV_ERR_ALIGN;
-  const sv::TreePlan plan = sv::make_tree_plan(B, N, V);
-  if (double(B) * double(plan.ntask) > double(kMaxI32)) return SV_ERR_SHAPE;
+  const sv::TreePlan plan = sv::make_tree_plan(B, N, V, dtype, sv::tree_resident_workgroups(dtype));
+  if (double(plan.items) + double(B) * double(plan.ntask) > double(kMaxI32)) return SV_ERR_SHAPE;
   const int st = check_workspace(workspace, workspace_bytes, plan.total);
   if (st != SV_OK) return st;
   sv::TreeArgs a{target_logits, t_seq, t_row, dtype, parent, token, u_accept, u_sample, temperature, accept,

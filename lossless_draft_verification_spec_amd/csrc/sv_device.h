@@ -225,6 +225,15 @@ template <typename V>
 __device__ __forceinline__ V ld_dev(const V* p) {
   return __hip_atomic_load(const_cast<V*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// System-scope forms, for the counters that workgroups poll (they are updated with system-scope atomics).
+template <typename V>
+__device__ __forceinline__ void st_sys(V* p, V v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+template <typename V>
+__device__ __forceinline__ V ld_sys(const V* p) {
+  return __hip_atomic_load(const_cast<V*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
 __device__ __forceinline__ int32_t ctr_add(int32_t* p) {
   return __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }

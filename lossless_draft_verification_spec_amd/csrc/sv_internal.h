@@ -150,26 +150,48 @@ struct alignas(16) TreeJob {
   float m;          // max of the stop node's whole row
   float u;          // the draw's uniform
   uint32_t flags;   // the sequence's flags from the walk
+  int32_t n;        // accepted nodes (-1: a failed sequence)
 };
 
 struct TreePlan {
   int64_t B = 0;
   int32_t N = 0;
   int64_t V = 0;
+  int64_t head_rows = 0;    // rows taken whole by the row items (rows b * N + u below it)
+  int32_t nseg = 1;         // pieces of every later row (1: those rows are whole too)
+  int64_t items = 0;        // row items (workgroups before the draw tasks in the launch)
   int64_t nch = 0;          // 512-element chunks per row in the draw
   int32_t ntask = 1;        // draw tasks per sequence
   int32_t task_chunks = 16; // chunks per draw task
-  size_t off_ctr1 = 0;      // int32 per sequence: rows finished (first launch), back to 0 after the walk
-  size_t off_ctr2 = 0;      // int32 per sequence: draw tasks finished (second launch), back to 0 after the pick
+  size_t off_ctr1 = 0;      // int32 per sequence: rows finished, N + 1 once the walk published the job; back to 0
+                            // after the pick
+  size_t off_ctr2 = 0;      // int32 per sequence: draw tasks finished, back to 0 after the pick
+  size_t off_rctr = 0;      // int32 per cut row: pieces finished, back to 0 after the row's merge
   size_t ctl_end = 0;       // the control region is [header end, ctl_end)
   size_t off_rows = 0;      // TreeRow per (b, node)
-  size_t off_zc = 0;        // float per (b, node): the node's logit in its parent's row
+  size_t off_piece = 0;     // TreeRow per (cut row, piece)
   size_t off_jobs = 0;      // TreeJob per b
   size_t off_chunk = 0;     // double per (b, chunk)
   size_t total = 0;
 };
 
-TreePlan make_tree_plan(int64_t B, int32_t N, int64_t V);
+// Row item `item` of the tree launch: row r = b * N + u and piece seg of it. The whole rows come first (r = item
+// below head_rows), then the pieces of the later rows, the nseg pieces of one row together.
+__host__ __device__ inline void tree_item(int64_t item, int64_t head_rows, int32_t nseg, int64_t* r, int32_t* seg) {
+  if (item < head_rows || nseg <= 1) {
+    *r = item;
+    *seg = 0;
+  } else {
+    const int64_t j = item - head_rows;
+    *r = head_rows + j / nseg;
+    *seg = int32_t(j % nseg);
+  }
+}
+
+// resident: workgroups of the tree launch resident on the device at once (it sets which rows are cut into pieces;
+// the workspace size depends on neither it nor the dtype).
+TreePlan make_tree_plan(int64_t B, int32_t N, int64_t V, int dtype, int64_t resident);
+int tree_resident_workgroups(int dtype);
 
 struct TreeArgs {
   const void* tgt; int64_t t_seq, t_row; int dtype;

@@ -2,7 +2,8 @@
 // (tests/test_host_sanitized.py builds and runs it; no GPU is needed and no call here reaches a HIP call):
 //  1. the check applied to a draw job read back from the workspace (job_valid), on random and garbage words: every
 //     job it accepts names only rows and ids inside the call's tensors;
-//  2. the count check of the support builder's segment records (clamp_count);
+//  2. the count check of the support builder's segment records (clamp_count), and the item map, piece sizes and
+//     workspace regions of the tree's first launch over many shapes and residencies;
 //  3. every entry point with arguments it must reject on the host (NULLs, shapes, dtypes, strides, alignment,
 //     temperatures, workspace sizes), and workspace sizing over extreme shapes, so that the sanitizers see the size
 //     arithmetic of every plan.
@@ -109,6 +110,53 @@ static void check_signatures() {
       CHECK(sv::ws_signature(kind, n) != sv::ws_signature(kind, n + 1));
     }
   CHECK(sv::ws_signature(sv::kLayoutDense, 64) != sv::ws_signature(sv::kLayoutSupport, 64));
+}
+
+// The tree's first launch over many shapes and residencies: its items cover every piece of every row exactly once,
+// in order, the piece and row-counter indexes stay inside their workspace regions, every piece of a cut row holds at
+// least 512 vectors at any alignment, and the workspace size depends on neither the dtype nor the residency.
+static void check_tree_plans() {
+  int64_t cut_plans = 0;
+  for (int64_t B : {int64_t(1), int64_t(3), int64_t(64), int64_t(100), int64_t(1000)})
+    for (int32_t N : {1, 2, 17, 64, 200})
+      for (int64_t V : {int64_t(1), int64_t(9), int64_t(4099), int64_t(50000), int64_t(151936), int64_t(2147483647)}) {
+        const size_t total = sv::make_tree_plan(B, N, V, SV_F32, 1).total;
+        for (int dt : {SV_F32, SV_BF16})
+          for (int64_t W : {int64_t(1), int64_t(7), int64_t(1024), int64_t(2048), int64_t(100000)}) {
+            const sv::TreePlan pl = sv::make_tree_plan(B, N, V, dt, W);
+            CHECK(pl.total == total);
+            const int64_t R = B * N;
+            CHECK(pl.nseg >= 1 && pl.nseg <= 64 && pl.head_rows >= 0 && pl.head_rows <= R);
+            if (pl.nseg == 1) CHECK(pl.head_rows == R && pl.items == R);
+            const int64_t epv = dt == SV_BF16 ? 8 : 4;
+            const int64_t nvec_min = (V - (epv - 1)) / epv;
+            if (pl.nseg > 1) {
+              ++cut_plans;
+              CHECK(nvec_min / pl.nseg >= 512);
+            }
+            const size_t piece_cap = (pl.off_jobs - pl.off_piece) / sizeof(sv::TreeRow);
+            const size_t rctr_cap = (pl.ctl_end - pl.off_rctr) / sizeof(int32_t);
+            CHECK((pl.off_piece - pl.off_rows) / sizeof(sv::TreeRow) >= size_t(R));
+            CHECK(pl.off_rctr >= pl.off_ctr2 + size_t(B) * 4 && pl.off_ctr2 >= pl.off_ctr1 + size_t(B) * 4);
+            std::vector<int32_t> seen(size_t(R), 0);
+            for (int64_t it = 0; it < pl.items; ++it) {
+              int64_t r = -1;
+              int32_t seg = -1;
+              sv::tree_item(it, pl.head_rows, pl.nseg, &r, &seg);
+              if (!(r >= 0 && r < R)) { CHECK(r >= 0 && r < R); break; }
+              const int32_t nseg = it < pl.head_rows ? 1 : pl.nseg;
+              CHECK(seg >= 0 && seg < nseg);
+              CHECK(seg == seen[size_t(r)]);          // the pieces of a row come in order, each once
+              ++seen[size_t(r)];
+              if (nseg > 1) {
+                CHECK(size_t((r - pl.head_rows) * nseg + seg) < piece_cap);
+                CHECK(size_t(r - pl.head_rows) < rctr_cap);
+              }
+            }
+            for (int64_t r = 0; r < R; ++r) CHECK(seen[size_t(r)] == (r < pl.head_rows ? 1 : pl.nseg));
+          }
+      }
+  CHECK(cut_plans > 100);
 }
 
 static void check_entry_points() {
@@ -224,6 +272,7 @@ int main() {
   check_jobs();
   check_counts();
   check_signatures();
+  check_tree_plans();
   check_entry_points();
   if (g_fail) {
     std::fprintf(stderr, "%d checks failed\n", g_fail);
