@@ -89,6 +89,13 @@ struct TreeShared {
       int32_t xs[SV_MAX_TREE_NODES];   // the stop node's child tokens: removed from the draw
       double tab[256];                 // the float64 exp table
     } dr;
+    struct {                           // the walk of a tree of at most 64 nodes, per node:
+      uint64_t kids[64];               // its children (bit c for child c)
+      float z[64];                     // its logit in its parent's row
+      float M[64];                     // its row's max, its children's logits included
+      double rest[64];                 // the weight of its row outside its children's tokens, relative to M
+      double ex[64];                   // its weight in its parent's row (0 unless the first holder of its token)
+    } sw;
     struct {                           // the walk, after the row pass of the same workgroup
       float rm[SV_MAX_TREE_NODES];     // per node: max of its row outside its children's tokens (NaN: bad row)
       double rs[SV_MAX_TREE_NODES];    // per node: the sum relative to it
@@ -458,7 +465,8 @@ __device__ void tree_walk(const TreeParams& p, int64_t b) {
 // the parent, so every node's test is evaluated at once: as a parent, the lane forms its row's max M (the rest of the
 // row and its children's logits) and the rest's weight; as a child, its own weight and denominator (the parent's rest
 // plus the weights of the first holders of the tokens of it and of its later siblings, summed from the last sibling
-// down). The walk is then a chain of ballots.
+// down) and its test; as a parent again, its first passing child. The walk is then a chain of lane reads. Each lane
+// loops over its own children or siblings only (bit masks built in LDS), never over the whole tree.
 template <typename T>
 __device__ void tree_walk_small(const TreeParams& p, int64_t b) {
   TreeShared& sh = g_tree;
@@ -469,7 +477,7 @@ __device__ void tree_walk_small(const TreeParams& p, int64_t b) {
   const double c = double(p.c);
   const bool in = lane < N;
   const int i = in ? lane : 0;
-  // one round of loads: the node's row record, its logit in its parent's row, its uniforms
+  // one round of loads: the node's row record, its logit in its parent's row, its uniform
   const TreeRow* r = p.rows + b * N + i;
   const float m = ld_dev(&r->m);
   const double s = ld_dev(&r->s);
@@ -479,72 +487,81 @@ __device__ void tree_walk_small(const TreeParams& p, int64_t b) {
   const bool zok = child && pa >= 0 && pa < N && tk >= 0 && int64_t(tk) < V;
   const float zr = Vec<T>::load1(static_cast<const T*>(p.tgt) + b * p.t_seq + (zok ? int64_t(pa) * p.t_row + tk : 0));
   const float ua = p.ua[b * N + i];
+  const int bad = __any(child && (!(pa >= 0 && pa < lane) || !(tk >= 0 && int64_t(tk) < V)));
+  const bool linked = child && pa >= 0 && pa < lane;  // a parent index that can be used (always, unless bad)
+  const int src = linked ? pa : 0;
+  sh.u.sw.kids[lane] = 0;
+  wave_sync();
+  if (linked) atomicOr(reinterpret_cast<unsigned long long*>(&sh.u.sw.kids[pa]), 1ull << lane);
   const float mr = in ? (rb ? NAN : m) : -INFINITY;
   const float z = zok ? zr : NAN;
-  const int bad = __any(child && (!(pa >= 0 && pa < lane) || !(tk >= 0 && int64_t(tk) < V)));
-  // as a parent
+  sh.u.sw.z[lane] = z;
+  wave_sync();
+  // as a parent: the row's max over the rest and the children's logits, a NaN or +inf among the children's logits
+  const uint64_t kids = sh.u.sw.kids[lane];
   float M = mr;
   int kb = 0;
-  for (int q = 1; q < N; ++q) {
-    const int pq = __builtin_amdgcn_readlane(pa, q);
-    const float zq = readlane_f(z, q);
-    if (pq == lane) {
-      M = fmaxf(M, zq);
-      kb |= !(zq < INFINITY);
-    }
+  for (uint64_t q = kids; q; q &= q - 1) {
+    const float zq = sh.u.sw.z[__builtin_ctzll(q)];
+    M = fmaxf(M, zq);
+    kb |= !(zq < INFINITY);
   }
   const bool nodebad = mr != mr || kb || M == -INFINITY;
   const double rest = (mr == -INFINITY || nodebad) ? 0.0 : s * exp2((double(mr) - double(M)) * c);
-  // as a child of u = pa
-  const int src = pa >= 0 && pa < 64 ? pa : 0;
-  const float Mu = __shfl(M, src);
-  const double restu = __shfl(rest, src);
-  bool first = child;
-  for (int q = 1; q < N; ++q) {
-    const int pq = __builtin_amdgcn_readlane(pa, q), tq = __builtin_amdgcn_readlane(tk, q);
-    first = first && !(q < lane && pq == pa && tq == tk);
-  }
+  sh.u.sw.M[lane] = M;
+  sh.u.sw.rest[lane] = rest;
+  wave_sync();
+  // as a child of pa: first holder of its token among its siblings, its weight, the denominator, the test
+  const float Mu = sh.u.sw.M[src];
+  const double restu = sh.u.sw.rest[src];
+  const uint64_t sib = linked ? sh.u.sw.kids[src] : 0;
+  bool first = linked;
+  for (uint64_t q = sib & ((1ull << lane) - 1); q && first; q &= q - 1) first = sh.tok[__builtin_ctzll(q)] != tk;
   const double ex = first ? exp2((double(z) - double(Mu)) * c) : 0.0;
+  sh.u.sw.ex[lane] = ex;
+  wave_sync();
   double S = 0.0;
-  for (int q = N - 1; q >= 1; --q) {
-    const int pq = __builtin_amdgcn_readlane(pa, q);
-    const double eq = readlane_d(ex, q);
-    if (pq == pa && q >= lane) S += eq;
+  for (uint64_t q = (sib >> lane) << lane; q;) {     // this child and its later siblings, from the last down
+    const int k = 63 - __builtin_clzll(q);
+    S += sh.u.sw.ex[k];
+    q &= ~(1ull << k);
   }
   const double P = first ? ex / (restu + S) : 0.0;
-  const uint64_t passm = wave_ballot(child && double(ua) < fmin(1.0, P));
+  const uint64_t passm = wave_ballot(linked && double(ua) < fmin(1.0, P));
   const uint64_t badm = wave_ballot(in && nodebad);
+  // as a parent: the first passing child in node order
+  const uint64_t okk = kids & passm;
+  const int next = okk ? __builtin_ctzll(okk) : -1;
   // the walk
   uint32_t fl = bad ? SV_FLAG_ID_RANGE : 0u;
   int cur = 0, n = 0, stop = -1, pathv = -1;
   float mstop = 0.f;
-  uint64_t tested = 0, onpath = 0;
+  uint64_t onpath = 0;
   while (!bad) {
     if ((badm >> cur) & 1ull) {                      // a NaN or +inf in the row, or nothing but -inf
       fl |= SV_FLAG_NONFINITE;
       stop = -1;
       break;
     }
-    const uint64_t kids = wave_ballot(child && pa == cur);
-    const uint64_t ok = kids & passm;
-    if (!ok) {                                       // every child rejected (or a leaf): draw at cur
-      tested |= kids;
+    const int nx = __builtin_amdgcn_readlane(next, cur);
+    if (nx < 0) {                                    // every child rejected (or a leaf): draw at cur
       stop = cur;
       mstop = readlane_f(M, cur);
       break;
     }
-    const int next = __builtin_ctzll(ok);            // the first passing child in node order
-    tested |= kids & (((uint64_t(1) << next) << 1) - 1);
-    onpath |= uint64_t(1) << next;
-    if (lane == n) pathv = next;
+    onpath |= 1ull << nx;
+    if (lane == n) pathv = nx;
     ++n;
-    cur = next;
+    cur = nx;
   }
+  // outputs: the children of the visited nodes are tested up to the accepted one (all of them at the stop node)
   const bool fatal = stop < 0;
+  const int nextpa = __shfl(next, src);
+  const bool tested = linked && (((onpath | 1ull) >> src) & 1ull) && (nextpa < 0 || lane <= nextpa);
   if (in) {
     p.accept[b * N + lane] = (!fatal && ((onpath >> lane) & 1ull)) ? 1 : 0;
     p.path[b * N + lane] = (!fatal && lane < n) ? pathv : -1;
-    if (p.p_test) p.p_test[b * N + lane] = (!fatal && ((tested >> lane) & 1ull)) ? float(P) : NAN;
+    if (p.p_test) p.p_test[b * N + lane] = (!fatal && tested) ? float(P) : NAN;
   }
   if (lane == 0) {
     TreeJob* jb = p.jobs + b;
