@@ -353,7 +353,8 @@ def bench_tree(steps, warmup, torch, sv, d):
     gbps, frac = hbm(nbytes, ms)
     del tgts
     return dict(ms_per_step=ms, wall_ms_per_step=wall, sequences=B, nodes=N, mean_accepted_path=float(n.mean()),
-                algorithmic_bytes=nbytes, hbm_GBps=gbps, hbm_frac=frac, roofline=roofline(nbytes, ms, "k_tree<bf16>"))
+                algorithmic_bytes=nbytes, hbm_GBps=gbps, hbm_frac=frac,
+                roofline=roofline(nbytes, ms, "k_tree<bf16>", profile_traffic("k_tree.txt", TREE)))
 
 
 # ----------------------------------------------------------------------------------------------------------------------
