@@ -102,6 +102,27 @@ def test_tree_shapes(idx):
     print(f"  {compare_tree(g, run_oracle(case), dt, f'tree {SHAPES[idx]}')}", flush=True)
 
 
+@pytest.mark.parametrize("N", [63, 64, 65])
+def test_tree_sizes_at_the_walk_boundary(N):
+    """Trees of 63, 64 and 65 nodes: up to 64 nodes the walk evaluates every node's test at once (one lane per node,
+    the 64th lane included), from 65 on it walks level by level; deep and bushy trees of each size, both dtypes, and
+    a root with all the other nodes as children (sibling masks of 63 and 64 bits)."""
+    for dt, pc, seed in (("bf16", 0.3, 301), ("f32", 0.8, 302)):
+        case = W.tree_case(9, N, 20_000, dtype=dt, seed=seed + N)
+        case["parent"] = W.random_tree_parents(np.random.default_rng(seed + N), 9, N, p_chain=pc)
+        case = _retoken(case)
+        print(f"tree N={N} {dt}: {compare_tree(run_tree(case), run_oracle(case), dt, f'N={N} {dt}')}", flush=True)
+    case = W.tree_case(4, N, 9_000, dtype="f32", seed=303 + N)
+    case["parent"][:] = 0
+    case["parent"][:, 0] = -1
+    case = _retoken(case)
+    case["token"][:, 1:] = case["token"][:, 1:][:, ::-1]     # the root's top candidate on its last child
+    case["u_accept"][:] = np.float32(0.97)                  # long sibling walks at the root
+    r = compare_tree(run_tree(case), run_oracle(case), 'f32', f'star N={N}')
+    print(f"star N={N}: {r}", flush=True)
+    assert r["tests"] > 4 * (N - 1) // 2                      # most siblings were tested
+
+
 def _retoken(case):
     """Children tokens for a new parent array: the top candidates of each node's row, in decreasing order."""
     z = oracle.widen(case["target"], case["dtype"])
