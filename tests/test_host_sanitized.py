@@ -1,9 +1,10 @@
 """The library's host code under AddressSanitizer and UndefinedBehaviorSanitizer.
 
 tests/native/check_host.cpp unit-tests the checks applied to words read back from a workspace (job_valid on random and
-garbage jobs, clamp_count, the layout signatures) and drives every entry point through its host-side argument
-checks (no call reaches a HIP call, so no GPU is needed). The library's sources are compiled with both sanitizers on
-the host pass (the device code is built as usual and never runs) and linked into one executable with the driver.
+garbage jobs, clamp_count, the layout signatures, the tree launch's item map and workspace regions) and drives every
+entry point through its host-side argument checks (no call reaches a HIP call, so no GPU is needed). The library's
+sources are compiled with both sanitizers on the host pass (the device code is built as usual and never runs) and
+linked into one executable with the checks.
 """
 import os
 import shutil
