@@ -131,8 +131,9 @@ SUPPORT = "support_chain_B64_g16_V151936_k50_p095_bf16"
 
 def bench_support(case, steps, warmup, torch, sv, d, k=50, top_p=0.95):
     """Dense -> sparse -> verify on the headline workload's logits: top-k / top-p supports of the target rows
-    (B x (gamma+1)) and of the draft rows (B x gamma), then the sparse verify of the drafted ids on them. Each of the
-    three kernels is timed alone in its own region, then the whole chain."""
+    (B x (gamma+1)) and of the draft rows (B x gamma) in one launch, then the sparse verify of the drafted ids on
+    them. Each kernel is timed alone in its own region (the two row sets also each in a launch of its own), then the
+    whole chain."""
     B, G, V = case["B"], case["gamma"], case["V"]
     rows_t, rows_d = B * (G + 1), B * G
     ncopies = 2                                                         # 1.28 GB per step pair: no cache reuse
@@ -141,27 +142,30 @@ def bench_support(case, steps, warmup, torch, sv, d, k=50, top_p=0.95):
     ids = torch.from_numpy(case["draft_ids"]).to(d)
     ua = torch.from_numpy(case["u_accept"]).to(d)
     us = torch.from_numpy(case["u_sample"]).to(d)
-    ws_t = sv.support_workspace(rows_t, V, k, d)
-    ws_d = sv.support_workspace(rows_d, V, k, d)
+    ws = sv.support_workspace(rows_t + rows_d, V, k, d)
     po, qo, vo = {}, {}, {}
 
     def sup_t(i):
-        sv.sv_build_support(tgts[i % ncopies], k, top_p, case["temperature"], True, out=po, ws=ws_t)
+        sv.sv_build_support(tgts[i % ncopies], k, top_p, case["temperature"], True, out=po, ws=ws)
 
     def sup_d(i):
-        sv.sv_build_support(dfts[i % ncopies], k, top_p, case["temperature"], True, out=qo, ws=ws_d)
+        sv.sv_build_support(dfts[i % ncopies], k, top_p, case["temperature"], True, out=qo, ws=ws)
+
+    def sup_pair(i):
+        sv.sv_build_support_pair(tgts[i % ncopies], dfts[i % ncopies], k, top_p, case["temperature"], True,
+                                 out_a=po, out_b=qo, ws=ws)
 
     def verify(i):
         sv.sv_verify_sparse(po["ids"].view(B, G + 1, k), po["probs"].view(B, G + 1, k), qo["ids"].view(B, G, k),
                             qo["probs"].view(B, G, k), ids, ua, us, bonus=1, vocab_size=V, out=vo)
 
     def chain(i):
-        sup_t(i)
-        sup_d(i)
+        sup_pair(i)
         verify(i)
 
     kt, _ = time_region(sup_t, steps, warmup, torch)
     kd, _ = time_region(sup_d, steps, warmup, torch)
+    kp, _ = time_region(sup_pair, steps, warmup, torch)
     kv, _ = time_region(verify, steps, warmup, torch)
     ms, wall = time_region(chain, steps, warmup, torch)
     out_row = k * 8 + 8                                                 # ids, probs, count, flags per row
@@ -169,15 +173,18 @@ def bench_support(case, steps, warmup, torch, sv, d, k=50, top_p=0.95):
     n = vo["n_accepted"].cpu().numpy()
     gt, ft = hbm(bytes_t, kt)
     gd, fd = hbm(bytes_d, kd)
+    gp, fp = hbm(bytes_t + bytes_d, kp)
     return dict(ms_per_step=ms, wall_ms_per_step=wall, positions=B * G, positions_per_s=B * G / (ms * 1e-3),
                 k=k, top_p=top_p, mean_n_accepted=float(n.mean()),
                 mean_kept_target=float(po["count"].float().mean().item()),
                 mean_kept_draft=float(qo["count"].float().mean().item()),
-                support_ms_target=kt, support_ms_draft=kd, sparse_ms=kv,
+                support_ms_pair=kp, support_ms_target=kt, support_ms_draft=kd, sparse_ms=kv,
                 support_bytes_target=bytes_t, support_bytes_draft=bytes_d,
+                support_GBps_pair=gp, support_frac_pair=fp,
                 support_GBps_target=gt, support_GBps_draft=gd, support_frac_target=ft, support_frac_draft=fd,
-                roofline=roofline(bytes_t, kt, "k_support<bf16> (target rows)",
-                                  profile_traffic("k_support.txt", "support_chain target rows (1088 x 151936 bf16)")))
+                roofline=roofline(bytes_t + bytes_d, kp, "k_support<bf16> (target and draft rows, one launch)",
+                                  profile_traffic("k_support.txt",
+                                                  "support_chain target and draft rows (2112 x 151936 bf16)")))
 
 
 # ----------------------------------------------------------------------------------------------------------------------

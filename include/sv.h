@@ -232,6 +232,28 @@ int sv_build_support(const void* logits, int64_t ld, int dtype, int64_t rows, in
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The same support builder over two sets of rows in one launch: the target's rows and the draft's that one sparse
+ * verify takes as p and q (Uno page, section "What 'lossless' actually has to mean"), under the same settings. Each
+ * output row is the one sv_build_support gives for that row alone; one launch lets the second set's rows fill the
+ * schedule the first set's leave partly empty, and pays one launch and one tail instead of two.
+ *
+ * logits_a, ld_a, rows_a   the first set, as logits, ld, rows of sv_build_support; ids_a, probs_a, count_a, flags_a
+ *                          its outputs, as there.
+ * logits_b ... flags_b     the second set, the same way (rows_b >= 1; rows_a + rows_b <= 2^31-1).
+ * dtype, V, temperature, k, top_p, renorm   shared by both sets, as in sv_build_support.
+ * workspace                >= sv_support_workspace_bytes(rows_a + rows_b, V, k) bytes, as in sv_build_support.
+ * The two sets' outputs must not overlap each other; their logits may (the rows are only read).
+ * Errors: those of sv_build_support, for either set; SV_ERR_SHAPE also when rows_b < 1 or the two sets together
+ * pass 2^31-1 rows.
+ */
+int sv_build_support_pair(const void* logits_a, int64_t ld_a, int64_t rows_a,
+                          const void* logits_b, int64_t ld_b, int64_t rows_b,
+                          int dtype, int64_t V, float temperature, int32_t k, float top_p, int32_t renorm,
+                          int32_t* ids_a, float* probs_a, int32_t* count_a, uint32_t* flags_a,
+                          int32_t* ids_b, float* probs_b, int32_t* count_b, uint32_t* flags_b,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Greedy verification at temperature 0 (DFlash/DFlash2 guide, section 4.4: under greedy decoding a drafted token is
  * kept exactly when it is the target's most likely token; the block is cut at the first one that is not). The
  * target's choice at a row is the argmax of its logits, equal maxima going to the lowest id. Slots start[b] ..

@@ -6,7 +6,7 @@ input generators work without the built library; using a verifier entry point wi
 """
 _BINDING = ("sv_verify_dense", "sv_verify_onehot_draft", "sv_verify_sparse", "sv_workspace_bytes",
             "sv_status_string", "SVError", "workspace", "sv_build_support", "sv_support_workspace_bytes",
-            "support_workspace", "sv_verify_greedy",
+            "sv_build_support_pair", "support_workspace", "sv_verify_greedy",
             "sv_confidence_commit")
 
 

@@ -208,29 +208,67 @@ size_t sv_support_workspace_bytes(int64_t rows, int64_t V, int32_t k) {
   return sv::make_support_plan(rows, V, k, SV_F32, 1).total;
 }
 
-int sv_build_support(const void* logits, int64_t ld, int dtype, int64_t rows, int64_t V,
-                     float temperature, int32_t k, float top_p, int32_t renorm,
-                     int32_t* ids, float* probs, int32_t* count, uint32_t* flags,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// Checks one row set of a support build; SV_OK or the status to return.
+int check_support_rows(const void* logits, int64_t ld, int64_t rows, int dtype, int64_t V, const int32_t* ids,
+                       const float* probs, const int32_t* count, const uint32_t* flags) {
   if (!logits || !ids || !probs) return SV_ERR_NULL;
-  if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
-  if (rows < 1 || rows > kMaxI32 || V < 1 || V > kMaxI32 || k < 1 || k > SV_MAX_K || k > V || ld < V)
-    return SV_ERR_SHAPE;
+  if (rows < 1 || rows > kMaxI32 || ld < V) return SV_ERR_SHAPE;
   if (double(rows - 1) * double(ld) + double(V) > 9.0e18) return SV_ERR_SHAPE;
-  if (!std::isfinite(temperature) || !(temperature > 0.f)) return SV_ERR_TEMP;
-  if (!(top_p > 0.f && top_p <= 1.f)) return SV_ERR_ARG;
-  if (renorm != 0 && renorm != 1) return SV_ERR_ARG;
   if (!aligned(logits, dtype == SV_BF16 ? 2 : 4)) return SV_ERR_ALIGN;
   const void* ptrs[] = {ids, probs, count, flags};
   for (const void* p : ptrs)
     if (p && !aligned(p, 4)) return SV_ERR_ALIGN;
+  return SV_OK;
+}
+
+// The shared part of sv_build_support and sv_build_support_pair: settings, plan, workspace, launch.
+int build_support(const sv::SupportRows& a, const sv::SupportRows& b, int dtype, int64_t V, float temperature,
+                  int32_t k, float top_p, int32_t renorm, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
+  if (V < 1 || V > kMaxI32 || k < 1 || k > SV_MAX_K || k > V) return SV_ERR_SHAPE;
+  int st = check_support_rows(a.logits, a.ld, a.rows, dtype, V, a.ids, a.probs, a.count, a.flags);
+  if (st != SV_OK) return st;
+  if (b.rows != 0) {
+    st = check_support_rows(b.logits, b.ld, b.rows, dtype, V, b.ids, b.probs, b.count, b.flags);
+    if (st != SV_OK) return st;
+  }
+  const int64_t rows = a.rows + b.rows;
+  if (rows > kMaxI32) return SV_ERR_SHAPE;
+  if (!std::isfinite(temperature) || !(temperature > 0.f)) return SV_ERR_TEMP;
+  if (!(top_p > 0.f && top_p <= 1.f)) return SV_ERR_ARG;
+  if (renorm != 0 && renorm != 1) return SV_ERR_ARG;
   const sv::SupportPlan plan = sv::make_support_plan(rows, V, k, dtype, sv::resident_workgroups());
   if (double(plan.items) > double(kMaxI32)) return SV_ERR_SHAPE;
-  const int st = check_workspace(workspace, workspace_bytes, plan.total);
+  st = check_workspace(workspace, workspace_bytes, plan.total);
   if (st != SV_OK) return st;
-  sv::SupportArgs a{logits, ld, dtype, temperature, top_p, renorm, ids, probs, count, flags,
-                    static_cast<char*>(workspace)};
-  return sv::launch_support(plan, a, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
+  sv::SupportArgs args{{a, b}, dtype, temperature, top_p, renorm, static_cast<char*>(workspace)};
+  return sv::launch_support(plan, args, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+}  // namespace
+
+int sv_build_support(const void* logits, int64_t ld, int dtype, int64_t rows, int64_t V,
+                     float temperature, int32_t k, float top_p, int32_t renorm,
+                     int32_t* ids, float* probs, int32_t* count, uint32_t* flags,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  const sv::SupportRows a{logits, ld, rows, ids, probs, count, flags};
+  const sv::SupportRows none{nullptr, 0, 0, nullptr, nullptr, nullptr, nullptr};
+  return build_support(a, none, dtype, V, temperature, k, top_p, renorm, workspace, workspace_bytes, stream);
+}
+
+int sv_build_support_pair(const void* logits_a, int64_t ld_a, int64_t rows_a,
+                          const void* logits_b, int64_t ld_b, int64_t rows_b,
+                          int dtype, int64_t V, float temperature, int32_t k, float top_p, int32_t renorm,
+                          int32_t* ids_a, float* probs_a, int32_t* count_a, uint32_t* flags_a,
+                          int32_t* ids_b, float* probs_b, int32_t* count_b, uint32_t* flags_b,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!logits_b || !ids_b || !probs_b) return SV_ERR_NULL;
+  if (rows_b < 1) return SV_ERR_SHAPE;
+  const sv::SupportRows a{logits_a, ld_a, rows_a, ids_a, probs_a, count_a, flags_a};
+  const sv::SupportRows b{logits_b, ld_b, rows_b, ids_b, probs_b, count_b, flags_b};
+  return build_support(a, b, dtype, V, temperature, k, top_p, renorm, workspace, workspace_bytes, stream);
 }
 
 int sv_verify_greedy(const void* target_logits, int64_t t_seq, int64_t t_row,

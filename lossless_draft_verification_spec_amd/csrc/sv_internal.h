@@ -126,10 +126,17 @@ struct SupportPlan {
 // depends on neither it nor the dtype).
 SupportPlan make_support_plan(int64_t rows, int64_t V, int32_t k, int dtype, int64_t resident);
 
-struct SupportArgs {
-  const void* logits; int64_t ld; int dtype;
-  float temperature; float top_p; int32_t renorm;
+// One set of logit rows and its outputs. A launch takes two sets; the rows of the second follow those of the first
+// (rows = 0 for a launch of one set).
+struct SupportRows {
+  const void* logits; int64_t ld; int64_t rows;
   int32_t* ids; float* probs; int32_t* count; uint32_t* flags;
+};
+
+struct SupportArgs {
+  SupportRows set[2];
+  int dtype;
+  float temperature; float top_p; int32_t renorm;
   char* ws;
 };
 

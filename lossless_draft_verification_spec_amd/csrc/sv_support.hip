@@ -10,17 +10,20 @@
 // 0..j-1 is below top_p (the shortest prefix that reaches top_p); a kept slot gets its probability renormalised over
 // the kept slots (renorm = 1) or its full-vocabulary softmax probability (renorm = 0), every other slot 0.
 //
-// How. One launch on the caller's stream, one 256-thread workgroup per item: one segment of one row (the segments
-// of a row are consecutive items). Each wave streams its share of the segment with 16-byte non-temporal loads and
-// keeps candidate keys in its own LDS buffer. A key holds the logit, mapped to an order-preserving unsigned integer,
-// in its high 32 bits and the complement of the id in its low 32, so keys are distinct and a larger key is a larger
-// logit or, for equal logits, the lower id. An element enters the buffer only if its key exceeds the wave's
-// threshold, the k-th largest key the wave (or another wave of the workgroup) has kept so far; a 16-byte vector is
-// tested first through its maximum, so once the threshold has risen, within the first few thousand elements of a
-// row, nearly every vector costs one compare. When a buffer fills, its wave raises the threshold by a radix select
-// over the buffer, without a barrier. At the end of the segment one more select merges the waves' candidates; with
-// several segments per row the last segment to finish (a counter per row) merges the segments'. The row's k keys are
-// then ranked, their probabilities formed in float64 and the top-p cut taken in float64.
+// How. One launch on the caller's stream, one 256-thread workgroup per item: one segment of one row (the segments of a
+// row are consecutive items). A launch may take two sets of rows with the same settings (a target's rows and a
+// draft's), the second numbered after the first, so that the two share one schedule and one tail. Each wave streams its
+// share of the segment with 16-byte non-temporal loads and keeps candidate keys in its own LDS buffer. A key holds the
+// logit, mapped to an order-preserving unsigned integer, in its high 32 bits and the complement of the id in its low
+// 32, so keys are distinct and a larger key is a larger logit or, for equal logits, the lower id. An element enters the
+// buffer only if its key exceeds the wave's threshold, the k-th largest key the wave (or another wave of the workgroup)
+// has kept so far; a 16-byte vector is tested first through its maximum, so once the threshold has risen, within the
+// first few thousand elements of a row, nearly every vector costs one compare. When a buffer fills, its wave raises the
+// threshold by a radix select over the buffer, without a barrier. At the end of the segment the waves' candidates (on
+// these rows a few dozen past k) are put in order in one pass, each thread counting the keys above its own; with
+// several segments per row the last segment to finish (a counter per row) merges the segments' keys the same way, after
+// a radix select when they are more than one per thread. The row's probabilities are then formed in float64 and the
+// top-p cut taken in float64.
 //
 // Bound: HBM. Algorithmic bytes: every logit of every row once (V * s per row, s = 2 bf16, 4 fp32), plus k ids and
 // k probabilities written per row.
@@ -63,7 +66,9 @@ struct SupPartial {
 };
 
 struct SupportParams {
-  const void* logits; int64_t ld; int64_t rows; int64_t V;
+  SupportRows s0, s1;   // the row sets: global rows 0 .. rows0 - 1 are s0's, the rest s1's
+  int64_t rows0;
+  int64_t rows; int64_t V;
   int32_t k; int32_t renorm;
   int64_t head_rows;  // rows 0 .. head_rows - 1: one item each (the whole row)
   int32_t nseg;       // segments of each later row
@@ -72,7 +77,6 @@ struct SupportParams {
   float c;          // log2(e) / T rounded to float32: the full-row sums
   double T;         // the temperature, widened
   double top_p;     // top_p as received (float32), widened
-  int32_t* ids; float* probs; int32_t* count; uint32_t* flags;
   char* ws;         // the workspace; its header names the control layout at zero
   uint64_t sig;     // this call's control layout
   int64_t ctl_end;  // control words (the row counters) fill [kWsHeaderBytes, ctl_end)
@@ -452,6 +456,23 @@ __device__ __forceinline__ void seed(int w, WaveCands& wc, int k, const float* v
   }
 }
 
+// Ranks the n distinct keys a[0..n), n <= kSupBlock, one per thread: thread tid counts the keys above a[tid],
+// reading all n as broadcasts, four per step, and calls f(key, rank). All threads of the workgroup, with the same n;
+// a[] is only read. Every thread reads every key, so this pays only for the few dozen keys left at the end of a
+// segment; larger sets go through a radix select first.
+template <typename F>
+__device__ __forceinline__ void rank_keys(const uint64_t* a, int n, F f) {
+  const int tid = threadIdx.x;
+  const uint64_t key = tid < n ? a[tid] : ~0ull;
+  int r = 0, j = 0;
+  for (; j + 4 <= n; j += 4) {
+    const uint64_t a0 = a[j], a1 = a[j + 1], a2 = a[j + 2], a3 = a[j + 3];
+    r += int(a0 > key) + int(a1 > key) + int(a2 > key) + int(a3 > key);
+  }
+  for (; j < n; ++j) r += a[j] > key;
+  if (tid < n) f(key, r);
+}
+
 // After the first rounds of a segment: one exact threshold for the whole workgroup. The waves' candidates so far go
 // side by side (a wave with more than SV_MAX_K is compacted first), one wave selects their k-th largest, and every
 // wave takes it as its threshold. That is the k-th largest key of every element the workgroup has seen, a bound
@@ -530,29 +551,45 @@ __device__ __forceinline__ void take_round(int w, WaveCands& wc, RowRun& st, boo
 // the row's support from its k keys
 // ----------------------------------------------------------------------------------------------------------------
 
-// cand[0..kk): the row's candidate keys, kk = min(k, keys the row offered); M, S: the row's max and sum of
-// 2^((z - M) * c) (renorm = 0); nan: a NaN was seen. All threads of the workgroup.
-__device__ __forceinline__ void finish_row(const SupportParams& p, int64_t row, const uint64_t* cand,
-                                           int kk, double S, bool nan) {
-  const int tid = threadIdx.x, w = tid >> 6, k = p.k;
-  if (tid < kk) {                                    // rank sort: keys are distinct
-    const uint64_t key = cand[tid];
-    int r = 0;
-    for (int j = 0; j < kk; ++j) r += cand[j] > key;
-    g_sup.sorted[r] = key;
+// The set that global row `row` belongs to; r: the row's index within it.
+__device__ __forceinline__ SupportRows row_set(const SupportParams& p, int64_t row, int64_t& r) {
+  const bool second = row >= p.rows0;
+  r = second ? row - p.rows0 : row;
+  return second ? p.s1 : p.s0;
+}
+
+// The k largest of the n distinct keys a[0..n) in descending order to g_sup.sorted[0..min(n, k)). All threads of
+// the workgroup. Up to kSupBlock keys: one rank pass. More: one wave's radix select moves the k largest to a[0..k)
+// first, and those are ranked.
+__device__ __forceinline__ void top_sorted(uint64_t* a, int n, int k) {
+  if (n > kSupBlock) {
+    if (threadIdx.x < 64) wave_select(a, n, k, g_sup.hist[0]);
+    n = k;
+    __syncthreads();
   }
+  rank_keys(a, n, [&](uint64_t key, int r) {
+    if (r < k) g_sup.sorted[r] = key;
+  });
   __syncthreads();
+}
+
+// g_sup.sorted[0..kk): the row's largest keys in descending order, kk = min(k, keys the row offered); S: the row's
+// sum of 2^((z - M) * c) with M its max (renorm = 0); nan: a NaN was seen. All threads of the workgroup.
+__device__ __forceinline__ void finish_row(const SupportParams& p, int64_t grow, int kk, double S, bool nan) {
+  const int tid = threadIdx.x, w = tid >> 6, k = p.k;
+  int64_t row;
+  const SupportRows rs = row_set(p, grow, row);
   const float z0 = kk > 0 ? val_of(g_sup.sorted[0]) : NAN;
-  int32_t* ids = p.ids + row * k;
-  float* probs = p.probs + row * k;
+  int32_t* ids = rs.ids + row * k;
+  float* probs = rs.probs + row * k;
   if (nan || kk < k || !(z0 < INFINITY) || z0 == -INFINITY) {   // NaN, +inf, or a row all -inf
     for (int j = tid; j < k; j += kSupBlock) {
       ids[j] = -1;
       probs[j] = NAN;
     }
     if (tid == 0) {
-      if (p.count) p.count[row] = 0;
-      if (p.flags) p.flags[row] = SV_FLAG_NONFINITE;
+      if (rs.count) rs.count[row] = 0;
+      if (rs.flags) rs.flags[row] = SV_FLAG_NONFINITE;
     }
     return;
   }
@@ -583,8 +620,8 @@ __device__ __forceinline__ void finish_row(const SupportParams& p, int64_t row, 
     probs[tid] = pr;
   }
   if (tid == 0) {
-    if (p.count) p.count[row] = count;
-    if (p.flags) p.flags[row] = 0u;
+    if (rs.count) rs.count[row] = count;
+    if (rs.flags) rs.flags[row] = 0u;
   }
 }
 
@@ -595,7 +632,9 @@ __device__ __forceinline__ void support_item(const SupportParams& p, int64_t row
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int64_t rec = row * p.nlay + seg;            // this segment's records in the workspace
   const int k = p.k;
-  const T* base = static_cast<const T*>(p.logits) + row * p.ld;
+  int64_t srow;
+  const SupportRows rs = row_set(p, row, srow);
+  const T* base = static_cast<const T*>(rs.logits) + srow * rs.ld;
   const int64_t V = p.V;
 
   if (lane == 0) lds_store_u64(&g_sup.theta[w], 0ull);
@@ -678,7 +717,7 @@ __device__ __forceinline__ void support_item(const SupportParams& p, int64_t row
   }
 
   // each wave drops its keys below the workgroup's best threshold (the segment's k largest are all at or above
-  // it) and keeps at most SV_MAX_K; the waves' keys side by side; one wave selects the segment's k largest
+  // it) and keeps at most SV_MAX_K; the waves' keys side by side; the segment's k largest, in order
   refresh(wc);
   if (wc.theta != 0) wc.cnt = keep_from(g_sup.buf + w * kWaveCap, wc.cnt, wc.theta);
   if (wc.cnt > SV_MAX_K) compact(w, wc, k, SV_MAX_K);
@@ -693,7 +732,7 @@ __device__ __forceinline__ void support_item(const SupportParams& p, int64_t row
   }
   for (int j = lane; j < wc.cnt; j += 64) g_sup.uni[off + j] = (g_sup.buf + w * kWaveCap)[j];
   __syncthreads();
-  if (w == 0 && n > k) wave_select(g_sup.uni, n, k, g_sup.hist[0]);
+  top_sorted(g_sup.uni, n, k);
   const int kk = n < k ? n : k;
 
   // the segment's full-row statistics (renorm = 0): common max, then each thread's sum rescaled in float64
@@ -708,13 +747,13 @@ __device__ __forceinline__ void support_item(const SupportParams& p, int64_t row
   __syncthreads();
 
   if (nseg == 1) {
-    finish_row(p, row, g_sup.uni, kk, Sseg, seg_nan);
+    finish_row(p, row, kk, Sseg, seg_nan);
     return;
   }
 
   // several segments: publish this one's keys and statistics, count it; the row's last segment merges
   uint64_t* kout = p.keys + rec * k;
-  for (int j = tid; j < kk; j += kSupBlock) st_dev(kout + j, g_sup.uni[j]);
+  for (int j = tid; j < kk; j += kSupBlock) st_dev(kout + j, g_sup.sorted[j]);
   if (tid == 0) {
     SupPartial* pp = p.part + rec;
     st_dev(&pp->m, Mseg);
@@ -791,9 +830,8 @@ __device__ __forceinline__ void support_item(const SupportParams& p, int64_t row
     if (f < nall) merge[f] = kv[i];
   }
   __syncthreads();
-  if (w == 0 && nall > k) wave_select(merge, nall, k, g_sup.hist[0]);
-  __syncthreads();
-  finish_row(p, row, merge, nall < k ? nall : k, S, row_nan);
+  top_sorted(merge, nall, k);
+  finish_row(p, row, nall < k ? nall : k, S, row_nan);
 }
 
 template <typename T, bool SUM>
@@ -857,14 +895,14 @@ hipError_t launch_support(const SupportPlan& plan, const SupportArgs& a, hipStre
   p.ws = ws;
   p.sig = ws_signature(kLayoutSupport, uint64_t(plan.rows));
   p.ctl_end = int64_t(plan.ctr_bytes);
-  p.logits = a.logits; p.ld = a.ld; p.rows = plan.rows; p.V = plan.V;
+  p.s0 = a.set[0]; p.s1 = a.set[1]; p.rows0 = a.set[0].rows;
+  p.rows = plan.rows; p.V = plan.V;
   p.k = plan.k; p.renorm = a.renorm;
   p.head_rows = plan.head_rows; p.nseg = plan.nseg; p.nlay = plan.nlay; p.items = plan.items;
   const double T = double(a.temperature);
   p.c = float(1.4426950408889634074 / T);
   p.T = T;
   p.top_p = double(a.top_p);
-  p.ids = a.ids; p.probs = a.probs; p.count = a.count; p.flags = a.flags;
   p.ctr = reinterpret_cast<int32_t*>(ws + plan.off_ctr);
   p.keys = reinterpret_cast<uint64_t*>(ws + plan.off_keys);
   p.part = reinterpret_cast<SupPartial*>(ws + plan.off_part);

@@ -25,7 +25,7 @@ SV_ERR_SCRATCH = -9
 
 EXPORTS = ("sv_workspace_bytes", "sv_status_string", "sv_verify_dense", "sv_verify_dense_noalloc",
            "sv_verify_onehot_draft", "sv_verify_sparse", "sv_support_workspace_bytes", "sv_build_support",
-           "sv_verify_greedy", "sv_confidence_commit", "sv_verify_tree")
+           "sv_build_support_pair", "sv_verify_greedy", "sv_confidence_commit", "sv_verify_tree")
 
 
 def _load() -> ctypes.CDLL:
@@ -52,6 +52,9 @@ def _load() -> ctypes.CDLL:
     lib.sv_support_workspace_bytes.restype = SZ
     lib.sv_build_support.argtypes = [P, I64, ctypes.c_int, I64, I64, F, I32, F, I32, P, P, P, P, P, SZ, P]
     lib.sv_build_support.restype = ctypes.c_int
+    lib.sv_build_support_pair.argtypes = [P, I64, I64, P, I64, I64, ctypes.c_int, I64, F, I32, F, I32,
+                                          P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.sv_build_support_pair.restype = ctypes.c_int
     lib.sv_verify_greedy.argtypes = [P, I64, I64, ctypes.c_int, I64, I32, I64, P, I32, P, P, P, P, P, P, P, SZ, P]
     lib.sv_verify_greedy.restype = ctypes.c_int
     lib.sv_confidence_commit.argtypes = [P, I64, I64, ctypes.c_int, I64, I32, I64, P, F, P, P, P, P, P, P, SZ, P]
@@ -330,11 +333,8 @@ def sv_verify_sparse(p_ids, p_probs, q_ids, q_probs, spec_ids, u_accept, u_sampl
     return o
 
 
-def sv_build_support(logits, k, top_p, temperature=1.0, renorm=True, *, out=None, ws=None, stream=None):
-    """Top-k / top-p supports of logit rows (see ``sv_build_support`` in include/sv.h). logits [..., V] float32 or
-    bfloat16: a contiguous tensor, or a 2-D tensor whose rows may be strided. Returns a dict: ids [..., k] int32,
-    probs [..., k] float32, count [...] int32, flags [...] int32 (the uint32 bits)."""
-    dev = logits.device
+def _support_rows(logits, name):
+    """(rows, ld, leading shape) of a logits tensor for the support builder."""
     V = logits.shape[-1]
     lead = tuple(logits.shape[:-1])
     if logits.dim() == 2 and logits.stride(-1) == 1:
@@ -346,7 +346,11 @@ def sv_build_support(logits, k, top_p, temperature=1.0, renorm=True, *, out=None
             rows *= d
         ld = V
     else:
-        raise ValueError("logits must be contiguous, or 2-D with a contiguous vocabulary axis")
+        raise ValueError(f"{name} must be contiguous, or 2-D with a contiguous vocabulary axis")
+    return rows, ld, lead
+
+
+def _support_out(out, lead, k, dev):
     o = {} if out is None else out
     spec = {"ids": (lead + (k,), torch.int32), "probs": (lead + (k,), torch.float32), "count": (lead, torch.int32),
             "flags": (lead, torch.int32)}
@@ -355,6 +359,17 @@ def sv_build_support(logits, k, top_p, temperature=1.0, renorm=True, *, out=None
             o[n] = torch.empty(shape, dtype=dt, device=dev)
         else:
             _need(o[n], n, dt, shape, dev)
+    return o
+
+
+def sv_build_support(logits, k, top_p, temperature=1.0, renorm=True, *, out=None, ws=None, stream=None):
+    """Top-k / top-p supports of logit rows (see ``sv_build_support`` in include/sv.h). logits [..., V] float32 or
+    bfloat16: a contiguous tensor, or a 2-D tensor whose rows may be strided. Returns a dict: ids [..., k] int32,
+    probs [..., k] float32, count [...] int32, flags [...] int32 (the uint32 bits)."""
+    dev = logits.device
+    V = logits.shape[-1]
+    rows, ld, lead = _support_rows(logits, "logits")
+    o = _support_out(out, lead, k, dev)
     if ws is None:
         ws = support_workspace(rows, V, k, dev)
     st = LIB.sv_build_support(_ptr(logits), ld, _dtype_code(logits), rows, V, float(temperature), int(k),
@@ -363,6 +378,31 @@ def sv_build_support(logits, k, top_p, temperature=1.0, renorm=True, *, out=None
     if st != SV_OK:
         raise SVError(st)
     return o
+
+
+def sv_build_support_pair(logits_a, logits_b, k, top_p, temperature=1.0, renorm=True, *, out_a=None, out_b=None,
+                          ws=None, stream=None):
+    """Supports of two sets of logit rows in one launch (see ``sv_build_support_pair`` in include/sv.h): each set as
+    the logits of ``sv_build_support``, of one dtype and vocabulary size. Returns the two output dicts."""
+    dev = logits_a.device
+    V = logits_a.shape[-1]
+    if logits_b.shape[-1] != V or logits_b.dtype != logits_a.dtype or logits_b.device != dev:
+        raise ValueError("logits_a and logits_b must share the vocabulary size, dtype and device")
+    rows_a, ld_a, lead_a = _support_rows(logits_a, "logits_a")
+    rows_b, ld_b, lead_b = _support_rows(logits_b, "logits_b")
+    oa = _support_out(out_a, lead_a, k, dev)
+    ob = _support_out(out_b, lead_b, k, dev)
+    if ws is None:
+        ws = support_workspace(rows_a + rows_b, V, k, dev)
+    st = LIB.sv_build_support_pair(_ptr(logits_a), ld_a, rows_a, _ptr(logits_b), ld_b, rows_b,
+                                   _dtype_code(logits_a), V, float(temperature), int(k), float(top_p),
+                                   1 if renorm else 0,
+                                   _ptr(oa["ids"]), _ptr(oa["probs"]), _ptr(oa["count"]), _ptr(oa["flags"]),
+                                   _ptr(ob["ids"]), _ptr(ob["probs"]), _ptr(ob["count"]), _ptr(ob["flags"]),
+                                   _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    if st != SV_OK:
+        raise SVError(st)
+    return oa, ob
 
 
 def sv_verify_tree(target, parent, token, u_accept, u_sample, temperature, *, out=None, ws=None, stream=None):

@@ -24,7 +24,8 @@ def test_exports_match_header():
     names = declared_functions()
     assert set(names) == {"sv_workspace_bytes", "sv_status_string", "sv_verify_dense", "sv_verify_dense_noalloc",
                           "sv_verify_onehot_draft", "sv_verify_sparse", "sv_support_workspace_bytes",
-                          "sv_build_support", "sv_verify_greedy", "sv_confidence_commit", "sv_verify_tree"}
+                          "sv_build_support", "sv_build_support_pair", "sv_verify_greedy", "sv_confidence_commit",
+                          "sv_verify_tree"}
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (sv_[a-z_]+)\b", out))
     assert set(names) <= exported
@@ -161,6 +162,37 @@ def test_support_rejects_bad_arguments(kw, code):
                                  a["renorm"], a["ids"], a["probs"], a["count"], a["flags"], a["ws"], a["ws_bytes"],
                                  None)
     assert st == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(la=None), -1), (dict(lb=None), -1), (dict(ids_a=None), -1), (dict(probs_b=None), -1),
+    (dict(dtype=3), -3),
+    (dict(rows_a=0), -2), (dict(rows_b=0), -2), (dict(rows_a=1 << 30, rows_b=1 << 30, V=1, ld_a=1, ld_b=1, k=1), -2),
+    (dict(ld_b=127), -2), (dict(V=0), -2), (dict(k=129), -2),
+    (dict(T=0.0), -4), (dict(top_p=0.0), -8), (dict(renorm=2), -8),
+    (dict(lb=A + 2), -5), (dict(flags_b=A + 1), -5), (dict(count_a=A + 3), -5),
+    (dict(ws=A + 16), -5), (dict(ws=None), -6), (dict(ws_bytes=16), -6),
+])
+def test_support_pair_rejects_bad_arguments(kw, code):
+    from lossless_draft_verification_spec_amd import sv
+    a = dict(la=A, ld_a=128, rows_a=3, lb=A, ld_b=128, rows_b=2, dtype=0, V=128, T=1.0, k=8, top_p=0.9, renorm=1,
+             ids_a=A, probs_a=A, count_a=A, flags_a=A, ids_b=A, probs_b=A, count_b=A, flags_b=A, ws=A,
+             ws_bytes=1 << 30)
+    a.update(kw)
+    st = sv.LIB.sv_build_support_pair(a["la"], a["ld_a"], a["rows_a"], a["lb"], a["ld_b"], a["rows_b"], a["dtype"],
+                                      a["V"], a["T"], a["k"], a["top_p"], a["renorm"], a["ids_a"], a["probs_a"],
+                                      a["count_a"], a["flags_a"], a["ids_b"], a["probs_b"], a["count_b"],
+                                      a["flags_b"], a["ws"], a["ws_bytes"], None)
+    assert st == code
+
+
+def test_support_pair_workspace_is_that_of_the_rows_together():
+    from lossless_draft_verification_spec_amd import sv
+    need = sv.sv_support_workspace_bytes(5, 128, 8)
+    # one byte short of the two sets' rows together is refused before any launch
+    st = sv.LIB.sv_build_support_pair(A, 128, 3, A, 128, 2, 0, 128, 1.0, 8, 0.9, 1, A, A, A, A, A, A, A, A, A,
+                                      need - 1, None)
+    assert st == -6
 
 
 def test_binding_marshalling_checks_without_gpu():

@@ -172,3 +172,114 @@ def test_workspace_shared_with_the_verifier():
         compare_decisions(gd, od, "dense tiny")
     g = run_support(z[:7], "bf16", 64, 0.95, 1.0, True, ws=ws)     # another shape through the same workspace
     check(g, oracle.build_support(z[:7], "bf16", 64, 0.95, 1.0), True)
+
+
+# ----------------------------------------------------------------------------------------------------------------
+# two row sets in one launch
+# ----------------------------------------------------------------------------------------------------------------
+
+def dev_rows(z, dtype, ld_pad=0):
+    if not ld_pad:
+        return t_logits(z, dtype)
+    big = np.zeros((z.shape[0], z.shape[1] + ld_pad), dtype=z.dtype)
+    big[:, :z.shape[1]] = z
+    return t_logits(big, dtype)[:, :z.shape[1]]
+
+
+def run_pair(za, zb, dtype, k, top_p, T, renorm, *, ld_pad_b=0, ws=None):
+    from lossless_draft_verification_spec_amd import sv
+    xa, xb = dev_rows(za, dtype), dev_rows(zb, dtype, ld_pad_b)
+    oa, ob = sv.sv_build_support_pair(xa, xb, k, top_p, T, renorm, ws=ws)
+    torch.cuda.synchronize()
+    return ({n: v.cpu().numpy() for n, v in oa.items()}, {n: v.cpu().numpy() for n, v in ob.items()})
+
+
+def assert_same(g, h):
+    """Bit-for-bit equality of two support outputs (NaN payloads included)."""
+    for n in ("ids", "count", "flags"):
+        np.testing.assert_array_equal(g[n], h[n])
+    np.testing.assert_array_equal(g["probs"].view(np.uint32), h["probs"].view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("renorm", [True, False])
+def test_pair_small_against_oracle_and_single_calls(dtype, renorm):
+    za = zipf_rows(11, 9, 3001, dtype=dtype)
+    zb = zipf_rows(12, 5, 3001, sigma=1.0, dtype=dtype)
+    ga, gb = run_pair(za, zb, dtype, 50, 0.95, 1.0, renorm, ld_pad_b=37)
+    check(ga, oracle.build_support(za, dtype, 50, 0.95, 1.0, renorm=renorm), renorm)
+    check(gb, oracle.build_support(zb, dtype, 50, 0.95, 1.0, renorm=renorm), renorm)
+    assert_same(ga, run_support(za, dtype, 50, 0.95, 1.0, renorm))
+    assert_same(gb, run_support(zb, dtype, 50, 0.95, 1.0, renorm, ld_pad=37))
+
+
+@pytest.mark.parametrize("rows_a,rows_b", [(1026, 4), (700, 330), (1, 1029), (1029, 1), (2000, 113)])
+def test_pair_rows_past_a_resident_round(rows_a, rows_b):
+    """Sizes whose rows past the last full resident round (1024 workgroups on MI355X) are cut into segments, with
+    that tail inside the first set, inside the second, or across the two; faulted rows in both sets. Every row
+    matches the single-set calls bit for bit, and sampled rows of each set (the tail's among them) the oracle."""
+    V = 20000
+    za = zipf_rows(21, rows_a, V, dtype="bf16")
+    zb = zipf_rows(22, rows_b, V, sigma=2.0, dtype="bf16")
+    za[0, 5] = 0x7FC0                                        # NaN
+    zb[-1, :] = 0xFF80                                       # a row all -inf
+    ga, gb = run_pair(za, zb, "bf16", 50, 0.95, 1.0, True)
+    assert_same(ga, run_support(za, "bf16", 50, 0.95, 1.0, True))
+    assert_same(gb, run_support(zb, "bf16", 50, 0.95, 1.0, True))
+    rng = np.random.default_rng(rows_a * 7 + rows_b)
+    total = rows_a + rows_b
+    tail = np.arange(total - total % 1024, total)
+    for g, z, lo, n in ((ga, za, 0, rows_a), (gb, zb, rows_a, rows_b)):
+        mine = tail[(tail >= lo) & (tail < lo + n)] - lo
+        pick = np.unique(np.concatenate([rng.choice(n, min(n, 12), replace=False), mine[:6], mine[-6:], [0, n - 1]]))
+        check(g, oracle.build_support(z[pick], "bf16", 50, 0.95, 1.0), True, pick)
+    assert ga["flags"][0] != 0 and gb["flags"][-1] != 0
+
+
+def test_pair_of_one_set_twice():
+    """Both sets on the same logits: the two outputs are the one set's support."""
+    from lossless_draft_verification_spec_amd import sv
+    z = zipf_rows(31, 70, 151936, dtype="bf16")
+    x = t_logits(z, "bf16")
+    oa, ob = sv.sv_build_support_pair(x, x, 64, 0.9, 0.8, False)
+    torch.cuda.synchronize()
+    ga = {n: v.cpu().numpy() for n, v in oa.items()}
+    gb = {n: v.cpu().numpy() for n, v in ob.items()}
+    assert_same(ga, gb)
+    check(ga, oracle.build_support(z, "bf16", 64, 0.9, 0.8, renorm=False), False)
+
+
+def test_pair_headline_shaped_rows_sampled():
+    """The target rows (B x (gamma + 1) = 1088) and the draft rows (B x gamma = 1024) of the dense block workload
+    (V = 151936, bf16) in one launch, as the benchmark's chain runs them: every row bit for bit against the single-set
+    calls, 48 sampled rows of each set (the 64 rows past the second resident round among them) against the oracle."""
+    case = W.make("dense_block_B64_g16_V151936_bf16")
+    V = case["V"]
+    zt, zd = case["target"].reshape(-1, V), case["draft"].reshape(-1, V)
+    gt, gd = run_pair(zt, zd, "bf16", 50, 0.95, 1.0, True)
+    assert_same(gt, run_support(zt, "bf16", 50, 0.95, 1.0, True))
+    assert_same(gd, run_support(zd, "bf16", 50, 0.95, 1.0, True))
+    rng = np.random.default_rng(9)
+    rows_d = zd.shape[0]
+    tail_d = np.arange(rows_d - 64, rows_d)                  # global rows 2048 .. 2111: the draft set's last 64
+    for g, z, extra in ((gt, zt, np.array([], dtype=np.int64)), (gd, zd, tail_d)):
+        rows = np.unique(np.concatenate([rng.choice(z.shape[0], 40, replace=False), extra[::8]]))
+        check(g, oracle.build_support(z[rows], "bf16", 50, 0.95, 1.0), True, rows)
+        assert (g["flags"] == 0).all()
+
+
+def test_pair_and_single_calls_share_a_workspace():
+    from lossless_draft_verification_spec_amd import sv
+    V = 151936
+    za, zb = zipf_rows(41, 30, V, dtype="bf16"), zipf_rows(42, 12, V, dtype="bf16")
+    ws = sv._zeroed_workspace(sv.sv_support_workspace_bytes(42, V, 64), dev())
+    oa = oracle.build_support(za, "bf16", 64, 0.95, 1.0)
+    ob = oracle.build_support(zb, "bf16", 64, 0.95, 1.0)
+    for _ in range(2):
+        ga, gb = run_pair(za, zb, "bf16", 64, 0.95, 1.0, True, ws=ws)
+        check(ga, oa, True)
+        check(gb, ob, True)
+        check(run_support(za, "bf16", 64, 0.95, 1.0, True, ws=ws), oa, True)
+        ga, gb = run_pair(zb, za[:5], "bf16", 64, 0.95, 1.0, True, ws=ws)   # fewer rows through the same workspace
+        check(ga, ob, True)
+        check(gb, oracle.build_support(za[:5], "bf16", 64, 0.95, 1.0), True)
