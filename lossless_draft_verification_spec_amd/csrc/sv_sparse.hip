@@ -7,13 +7,16 @@
 // adds the first-rejection scan and the draw from the correction distribution at that slot (or a bonus draw from p's
 // support of row gamma), as the dense path does.
 //
-// One workgroup of 8 waves per sequence (three fit a compute unit); the slots go in batches whose correction weights
-// fit the LDS table (one batch for the usual sizes, e.g. 16 slots of 64-entry supports).
-//  1. a wave per slot (slots wave, wave + 8, ...), the slot's supports in its lanes (entry e in lane e % 64, register
-//     e / 64): the rows are checked; p_spec and q_spec come from a ballot of the entries whose id is the drafted one;
-//     the accept test; then each p entry's q probability, every lane comparing its p ids with one q entry at a time
-//     (q staged in LDS), and the weights max(p - q_on_p, 0) into the LDS table with their ids. With one batch, the
-//     checks of every row end before any output is written; with several, all rows are checked in a pass before.
+// One workgroup of 8 waves per sequence (four fit a compute unit for supports of up to 64 entries, so that a thousand
+// sequences run in one round); the slots go in batches whose correction weights fit the LDS table (one batch for the
+// usual sizes, e.g. 16 slots of 64-entry supports).
+//  1. a wave per slot (slots wave, wave + 8, ...; the next slot's rows requested before this one's are used), the
+//     slot's supports in its lanes (entry e in lane e % 64, register e / 64): the rows are checked; p_spec and q_spec
+//     come from a ballot of the entries whose id is the drafted one; the accept test; then each p entry's q
+//     probability, every lane comparing its p ids with one q entry at a time (read across lanes from the lane that
+//     holds it), and the weights max(p - q_on_p, 0) into the LDS table with their ids (p's probabilities when no
+//     weight is positive). With one batch, the checks of every row end before any output is written; with several,
+//     all rows are checked in a pass before.
 //  2. one thread per slot sums its weights in slot order (and keeps the running sums of the slot to be drawn from);
 //     the outputs and the normalised correction distribution are written by all threads.
 //  3. the draw, by one wave: a ballot over the stored running sums finds the first that exceeds t.
@@ -90,12 +93,19 @@ __device__ __forceinline__ double match_sum(const Row<kEnt>& r, int k, int32_t x
   return s;
 }
 
+// Buckets of a wave's index of q (an entry number each): four per entry of the widest q support, so that few
+// entries share a bucket.
+template <int kEnt> constexpr int kQBuckets = 256 * kEnt;
+template <int kEnt> constexpr int kQBucketBits = kEnt == 1 ? 8 : kEnt == 2 ? 9 : 10;
+
+// Sized for supports of up to 64 kEnt entries, so that the narrow layouts leave room for more workgroups.
+template <int kEnt>
 struct SpShared {
   double w[kTable];                    // weights of the batch's slots, row stride ldw
   int32_t pid[kTable];                 // their p ids
   double S[kBatchMax];                 // per slot of the batch: its normaliser
-  int2 q[kWaves][SV_MAX_K];            // per wave: the q support of its slot (id, probability bits)
-  double cum[SV_MAX_K];                // the drawn slot's running sums of its weights (slot order)
+  double cum[64 * kEnt];               // the drawn slot's running sums of its weights (slot order)
+  int32_t qb[kWaves][kQBuckets<kEnt>]; // per wave: the index of its slot's q support (entry per bucket)
   float ps[kBatchMax], qs[kBatchMax];  // per slot of the batch: p_spec, q_spec
   float us[kBatchMax];                 // per slot of the batch: its draw uniform
   uint8_t acc[SV_MAX_GAMMA];
@@ -104,17 +114,17 @@ struct SpShared {
   int32_t tok;
 };
 
-// Sum of n weights in slot order (one thread), their values requested four at a time; with cum, every running sum
+// Sum of n weights in slot order (one thread), their values requested eight at a time; with cum, every running sum
 // is stored too.
 __device__ __forceinline__ double seq_sum(const double* w, int n, double* cum) {
   double s = 0.0;
   int e = 0;
-  for (; e + 4 <= n; e += 4) {
-    double v[4];
+  for (; e + 8 <= n; e += 8) {
+    double v[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = w[e + i];
+    for (int i = 0; i < 8; ++i) v[i] = w[e + i];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
       s += v[i];
       if (cum) cum[e + i] = s;
     }
@@ -141,77 +151,131 @@ __device__ __forceinline__ int wave_draw(const double* w, const double* cum, int
   return -1;
 }
 
-// The correction weights max(p_e - q_on_p_e, 0) of one slot (by one wave) into w, and the p ids into ids: each p
-// entry's q probability is found by comparing every lane's p ids with one q entry at a time (q is staged in qs from
-// the lanes that hold it); when q repeats an id of p, that slot's matches are summed again in float64, in q's slot
-// order.
 template <int kEnt>
-__device__ __forceinline__ void slot_weights(const Row<kEnt>& P, const Row<kEnt>& Q, int kp, int kq, int2* qs,
+__device__ __forceinline__ uint32_t q_bucket(int32_t id) {
+  return (uint32_t(id) * 0x9E3779B1u) >> (32 - kQBucketBits<kEnt>);
+}
+
+// q entry e (taken mod 64 kEnt) for every lane: id and probability, read across lanes from the lane that holds it.
+template <int kEnt>
+__device__ __forceinline__ void q_entry(const Row<kEnt>& Q, int e, int32_t& id, float& pr) {
+  const int src = (e & 63) << 2;
+  id = -1;
+  pr = 0.f;
+#pragma unroll
+  for (int m = 0; m < kEnt; ++m) {
+    const int i = __builtin_amdgcn_ds_bpermute(src, Q.id[m]);
+    const int f = __builtin_amdgcn_ds_bpermute(src, __float_as_int(Q.pr[m]));
+    if (((e >> 6) & (kEnt - 1)) == m) {
+      id = i;
+      pr = __int_as_float(f);
+    }
+  }
+}
+
+// The correction weights max(p_e - q_on_p_e, 0) of one slot (by one wave) into w, and the p ids into ids. Each p
+// entry's q probability is found through the wave's index of q (qb, an entry number per bucket of the id's hash): every q
+// entry writes its index at its bucket, and an entry that reads back another's has lost the bucket; each p entry
+// reads its bucket and checks the id of the q entry named there (so the index needs no clearing: a stale or
+// uninitialised word names an entry whose id does not match, or one that does and is a true match); the q entries
+// that lost their bucket (a few) are then compared with every p entry one at a time. When q repeats an id, every
+// q_on_p is summed again in float64 in q's slot order instead, each q entry read across lanes. With no positive
+// weight (no leftover mass) the weights become p's probabilities and the result is true (the same for every lane).
+template <int kEnt>
+__device__ __forceinline__ bool slot_weights(const Row<kEnt>& P, const Row<kEnt>& Q, int kp, int kq, int32_t* qb,
                                              double* w, int32_t* ids) {
   const int lane = threadIdx.x & 63;
+  // lanes talk through the index, so every access is a relaxed atomic (never merged with this lane's own earlier
+  // write by the compiler); every write of the wave lands before its reads: the LDS executes one wave's operations
+  // in issue order
+  auto put = [&](int b, int v) { __hip_atomic_store(qb + b, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT); };
+  auto get = [&](int b) { return __hip_atomic_load(qb + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT); };
 #pragma unroll
   for (int m = 0; m < kEnt; ++m)
-    if (m * 64 + lane < kq) qs[m * 64 + lane] = make_int2(Q.id[m], __float_as_int(Q.pr[m]));
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (m * 64 + lane < kq) put(q_bucket<kEnt>(Q.id[m]), m * 64 + lane);
+  uint64_t lost[kEnt];
+#pragma unroll
+  for (int m = 0; m < kEnt; ++m) {
+    const int e = m * 64 + lane;
+    lost[m] = __ballot(e < kq && get(q_bucket<kEnt>(Q.id[m])) != e);
+  }
   float qm[kEnt];
   int nm[kEnt];
 #pragma unroll
-  for (int m = 0; m < kEnt; ++m) { qm[m] = 0.f; nm[m] = 0; }
-#pragma unroll 4
-  for (int l = 0; l < kq; ++l) {
-    const int2 qe = qs[l];
+  for (int m = 0; m < kEnt; ++m) {
+    const bool ok = m * 64 + lane < kp;
+    const int c = ok ? get(q_bucket<kEnt>(P.id[m])) : 0;
+    int32_t qid;
+    float qpr;
+    q_entry<kEnt>(Q, c, qid, qpr);
+    const bool hit = ok && c >= 0 && c < kq && qid == P.id[m];
+    qm[m] = hit ? qpr : 0.f;
+    nm[m] = hit ? 1 : 0;
+  }
 #pragma unroll
-    for (int m = 0; m < kEnt; ++m) {
-      if (m * 64 >= kp) break;
-      const bool hit = P.id[m] == qe.x;
-      qm[m] = hit ? __int_as_float(qe.y) : qm[m];
-      nm[m] += hit ? 1 : 0;
+  for (int mq = 0; mq < kEnt; ++mq) {
+    uint64_t left = lost[mq];
+    while (left) {
+      const int l = __builtin_ctzll(left);
+      left &= left - 1;
+      const int32_t qid = __builtin_amdgcn_readlane(Q.id[mq], l);
+      const float qpr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Q.pr[mq]), l));
+#pragma unroll
+      for (int m = 0; m < kEnt; ++m) {
+        const bool hit = m * 64 + lane < kp && P.id[m] == qid;
+        qm[m] = hit ? qpr : qm[m];
+        nm[m] += hit ? 1 : 0;
+      }
     }
   }
-  double qop[kEnt];
-#pragma unroll
-  for (int m = 0; m < kEnt; ++m) qop[m] = double(qm[m]);
   bool multi = false;
 #pragma unroll
   for (int m = 0; m < kEnt; ++m) multi |= nm[m] > 1;
+  double qop[kEnt];
+#pragma unroll
+  for (int m = 0; m < kEnt; ++m) qop[m] = double(qm[m]);
   if (__any(multi)) {
 #pragma unroll
     for (int m = 0; m < kEnt; ++m) qop[m] = 0.0;
-    for (int l = 0; l < kq; ++l) {
-      const int2 qe = qs[l];
 #pragma unroll
-      for (int m = 0; m < kEnt; ++m)
-        if (m * 64 < kp) qop[m] += (P.id[m] == qe.x) ? double(__int_as_float(qe.y)) : 0.0;
+    for (int mq = 0; mq < kEnt; ++mq) {
+      const int n = min(64, kq - 64 * mq);
+      for (int l = 0; l < n; ++l) {
+        const int32_t qid = __builtin_amdgcn_readlane(Q.id[mq], l);
+        const double qpr = double(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(Q.pr[mq]), l)));
+#pragma unroll
+        for (int m = 0; m < kEnt; ++m) qop[m] += (P.id[m] == qid) ? qpr : 0.0;
+      }
     }
   }
+  double r[kEnt];
+  bool pos = false;
 #pragma unroll
   for (int m = 0; m < kEnt; ++m) {
 #pragma clang fp contract(off)
+    const double d = double(P.pr[m]) - qop[m];
+    r[m] = d > 0.0 ? d : 0.0;
+    pos |= m * 64 + lane < kp && r[m] > 0.0;
+  }
+  const bool empty = !__any(pos);
+#pragma unroll
+  for (int m = 0; m < kEnt; ++m) {
     const int e = m * 64 + lane;
-    const double r = double(P.pr[m]) - qop[m];
     if (e < kp) {
-      w[e] = r > 0.0 ? r : 0.0;
+      w[e] = empty ? double(P.pr[m]) : r[m];
       ids[e] = P.id[m];
     }
   }
+  return empty;
 }
 
-// A slot's normaliser (one thread), with the running sums when cum is given; no leftover mass: the weights become p.
-__device__ __forceinline__ double slot_norm(double* w, const float* p_pr, int kp, double* cum, bool& empty) {
-  double S = seq_sum(w, kp, cum);
-  empty = !(S > 0.0);
-  if (empty) {
-    for (int e = 0; e < kp; ++e) w[e] = double(p_pr[e]);
-    S = seq_sum(w, kp, cum);
-  }
-  return S;
-}
+// Waves per SIMD asked of each layout: the narrowest (supports of up to 64 entries) fits four workgroups per compute
+// unit, so that a thousand sequences run in one round.
+template <int kEnt> constexpr int kSparseWpe = kEnt == 1 ? 8 : 1;
 
 template <int kEnt>
-__global__ __launch_bounds__(kBlock) void k_sparse(SparseArgs a) {
-  __shared__ SpShared sh;
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kSparseWpe<kEnt>))) void k_sparse(SparseArgs a) {
+  __shared__ SpShared<kEnt> sh;
 
   const int64_t b = blockIdx.x;
   const int G = a.G, kp = a.kp, kq = a.kq;
@@ -263,12 +327,24 @@ __global__ __launch_bounds__(kBlock) void k_sparse(SparseArgs a) {
   for (int j0 = 0; j0 < G; j0 += nb) {
     const int j1 = min(j0 + nb, G);
     // 1. a wave per slot: accept test and, when needed, the correction weights
+    // the next slot's rows and scalars are requested before this slot's are used (one load round per wave when
+    // every wave has at most two slots)
+    Row<kEnt> Pn, Qn;
+    int32_t xn = 0;
+    float un = 0.f, udn = 0.f;
+    auto fetch = [&](int j) {
+      Pn = load_row<kEnt>(P_ids + int64_t(j) * kp, P_pr + int64_t(j) * kp, kp, lane);
+      Qn = load_row<kEnt>(Q_ids + int64_t(j) * kq, Q_pr + int64_t(j) * kq, kq, lane);
+      xn = a.spec[b * G + j];
+      un = a.ua[b * G + j];
+      udn = a.us[b * (G + 1) + j];
+    };
+    if (j0 + wv < j1) fetch(j0 + wv);
     for (int j = j0 + wv; j < j1; j += kWaves) {
-      const Row<kEnt> P = load_row<kEnt>(P_ids + int64_t(j) * kp, P_pr + int64_t(j) * kp, kp, lane);
-      const Row<kEnt> Q = load_row<kEnt>(Q_ids + int64_t(j) * kq, Q_pr + int64_t(j) * kq, kq, lane);
-      const int32_t x = a.spec[b * G + j];
-      const float u = a.ua[b * G + j];
-      const float uds = a.us[b * (G + 1) + j];
+      const Row<kEnt> P = Pn, Q = Qn;
+      const int32_t x = xn;
+      const float u = un, uds = udn;
+      if (j + kWaves < j1) fetch(j + kWaves);
       if (single) {
         check_row(P, kp, a.vocab, bad_nf, bad_id);
         check_row(Q, kq, a.vocab, bad_nf, bad_id);
@@ -284,7 +360,10 @@ __global__ __launch_bounds__(kBlock) void k_sparse(SparseArgs a) {
         sh.qs[j - j0] = float(qs);
         sh.us[j - j0] = uds;
       }
-      if (weights) slot_weights(P, Q, kp, kq, sh.q[wv], sh.w + (j - j0) * ldw, sh.pid + (j - j0) * ldw);
+      if (weights) {
+        const bool em = slot_weights(P, Q, kp, kq, sh.qb[wv], sh.w + (j - j0) * ldw, sh.pid + (j - j0) * ldw);
+        if (lane == 0) sh.empty[j - j0] = em ? 1 : 0;
+      }
     }
     if (single) {
       bad_id = __syncthreads_or(bad_id);
@@ -307,11 +386,8 @@ __global__ __launch_bounds__(kBlock) void k_sparse(SparseArgs a) {
     const int k = sh.k;                              // known here only with a single batch
     // 2. normalisers, one thread per slot
     if (weights) {
-      for (int s = tid; s < j1 - j0; s += kBlock) {
-        bool empty;
-        sh.S[s] = slot_norm(sh.w + s * ldw, P_pr + int64_t(j0 + s) * kp, kp, j0 + s == k ? sh.cum : nullptr, empty);
-        sh.empty[s] = empty ? 1 : 0;
-      }
+      for (int s = tid; s < j1 - j0; s += kBlock)
+        sh.S[s] = seq_sum(sh.w + s * ldw, kp, j0 + s == k ? sh.cum : nullptr);
     }
     __syncthreads();
     // 3. the batch's outputs, then (single batch) the draw
@@ -350,19 +426,13 @@ __global__ __launch_bounds__(kBlock) void k_sparse(SparseArgs a) {
     if (k < G) {
       const Row<kEnt> P = load_row<kEnt>(P_ids + int64_t(k) * kp, P_pr + int64_t(k) * kp, kp, lane);
       const Row<kEnt> Q = load_row<kEnt>(Q_ids + int64_t(k) * kq, Q_pr + int64_t(k) * kq, kq, lane);
-      slot_weights(P, Q, kp, kq, sh.q[0], sh.w, sh.pid);
+      const bool empty = slot_weights(P, Q, kp, kq, sh.qb[0], sh.w, sh.pid);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       double S = 0.0;
-      int empty = 0;
-      if (lane == 0) {
-        bool em;
-        S = slot_norm(sh.w, P_pr + int64_t(k) * kp, kp, sh.cum, em);
-        empty = em;
-      }
+      if (lane == 0) S = seq_sum(sh.w, kp, sh.cum);
       S = __shfl(S, 0);
-      empty = __shfl(empty, 0);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");

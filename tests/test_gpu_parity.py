@@ -280,7 +280,8 @@ def check_sparse_exact(g, o, label):
         assert np.array_equal(g[k], want, equal_nan=True), f"{label}: {k}"
 
 
-@pytest.mark.parametrize("shape", [(8, 5, 64, 1000), (3, 16, 17, 200), (5, 2, 256, 100_000), (40, 1, 1, 10)])
+@pytest.mark.parametrize("shape", [(8, 5, 64, 1000), (3, 16, 17, 200), (5, 2, 256, 100_000), (40, 1, 1, 10),
+                                   (3, 30, 64, 5000), (2, 7, 256, 100_000), (2, 70, 128, 3000)])
 def test_sparse_shapes_bit_exact(shape):
     B, G, k, V = shape
     case = W.sparse_case(B, G, k, V, shared=max(1, k // 2), seed=31)
@@ -301,6 +302,49 @@ def test_sparse_faults_and_fallback():
     o = oracle.verify_sparse(case["p_ids"], case["p_probs"], case["q_ids"], case["q_probs"], case["spec_ids"],
                              case["u_accept"], case["u_sample"], bonus=1, vocab_size=50)
     check_sparse_exact(g, o, "sparse faults")
+
+
+def _one_bucket(n, bits, bucket, rng):
+    """n distinct ids in [0, 2^24) that the kernel's index of q (2^bits buckets of a multiplicative hash) sends to
+    one bucket, so that all but one of a support's entries lose it and take the kernel's slower matching."""
+    ids = np.arange(1 << 24, dtype=np.int64)
+    h = ((ids * 0x9E3779B1) & 0xFFFFFFFF) >> (32 - bits)
+    pool = ids[h == bucket]
+    assert pool.size >= n
+    return rng.choice(pool, size=n, replace=False).astype(np.int32)
+
+
+@pytest.mark.parametrize("k,bits", [(64, 8), (50, 8), (128, 9), (256, 10)])
+def test_sparse_colliding_repeated_and_unchecked_ids(k, bits):
+    """Supports whose ids all share one bucket of the kernel's index of q, q and p supports with repeated ids
+    (matches summed in slot order, as the routine's id-equality gathers do), and, with the vocabulary unchecked, ids
+    -1, 0 and the most negative int32. Bit-exact against the oracle."""
+    rng = np.random.default_rng(k)
+    case = W.sparse_case(6, 4, k, 1 << 24, shared=k // 2, seed=40 + k)
+    G = case["gamma"]
+    for b in range(6):
+        for j in range(G + 1):
+            ids = _one_bucket(2 * k, bits, (1 << bits) - 1, rng)
+            case["p_ids"][b, j] = ids[:k]
+            if j < G:
+                q = np.concatenate([rng.choice(ids[:k], k // 2, replace=False), ids[k:k + k - k // 2]])
+                case["q_ids"][b, j] = rng.permutation(q)
+    case["q_ids"][1, :, 1] = case["q_ids"][1, :, 0]   # q repeats an id (shared with p or not)
+    case["p_ids"][2, :, 2] = case["p_ids"][2, :, 0]   # p repeats an id
+    case["q_ids"][2, 0, 3] = case["p_ids"][2, 0, 0]
+    for c, v in ((3, -1), (4, 0), (5, np.iinfo(np.int32).min)):
+        case["p_ids"][c, :, 0] = v                    # unchecked ids when vocab_size = 0
+        case["q_ids"][c, :, 1] = v
+    slot = rng.integers(0, k, size=(6, G))
+    case["spec_ids"] = np.take_along_axis(case["q_ids"], slot[..., None], axis=-1)[..., 0].astype(np.int32)
+    for vocab in (0, 1 << 24):
+        if vocab:
+            for key in ("p_ids", "q_ids", "spec_ids"):
+                case[key] = np.where(case[key] < 0, 7, case[key]).astype(np.int32)
+        g = run_sparse(case, vocab_size=vocab)
+        o = oracle.verify_sparse(case["p_ids"], case["p_probs"], case["q_ids"], case["q_probs"], case["spec_ids"],
+                                 case["u_accept"], case["u_sample"], bonus=1, vocab_size=vocab)
+        check_sparse_exact(g, o, f"colliding ids k={k} vocab={vocab}")
 
 
 def test_sparse_workload_full_size_bit_exact():
