@@ -274,12 +274,17 @@ __device__ __forceinline__ bool slot_weights(const Row<kEnt>& P, const Row<kEnt>
 template <int kEnt> constexpr int kSparseWpe = kEnt == 1 ? 8 : 1;
 
 template <int kEnt>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kSparseWpe<kEnt>))) void k_sparse(SparseArgs a) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kSparseWpe<kEnt>))) void k_sparse(SparseArgs kargs) {
+  (void)kargs;
+  // the arguments are read in place from the argument segment, each when it is used, instead of being held in
+  // scalar registers for the whole kernel
+  const SparseArgs& a = *(const SparseArgs*)(__builtin_amdgcn_kernarg_segment_ptr());
   __shared__ SpShared<kEnt> sh;
 
   const int64_t b = blockIdx.x;
   const int G = a.G, kp = a.kp, kq = a.kq;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // the wave index in a scalar register: every slot index, row address and loop bound of a wave is then scalar
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rows_p = G + (a.bonus ? 1 : 0);
   const int32_t* P_ids = a.p_ids + b * int64_t(rows_p) * kp;
   const float* P_pr = a.p_probs + b * int64_t(rows_p) * kp;
