@@ -99,6 +99,8 @@ struct SupShared {
   float mval;
   int32_t ival;
   int32_t flag;
+  int32_t pool_n;                      // keys the waves have added to the pilot's pool in uni (whole rows)
+  int32_t pool_in;                     // waves that have added theirs
 };
 
 // The workgroup's shared state, at file scope so that functions that are not inlined address it as LDS too.
@@ -478,6 +480,37 @@ __device__ __forceinline__ void rank_keys(const uint64_t* a, int n, F f) {
 // wave takes it as its threshold. That is the k-th largest key of every element the workgroup has seen, a bound
 // each wave alone would only reach after seeing four times as many; the logits of the rows at hand (largest at low
 // ids) make it close to the segment's final k-th largest, so that later rounds rarely offer anything.
+// The same threshold for a whole row, without a barrier: each wave adds its candidates (at most SV_MAX_K, compacted
+// first if need be) to a pool in uni and counts itself in; the last wave to arrive selects the pool's k-th largest
+// and publishes it as its own threshold, which the others take at their next refresh, streaming on meanwhile. The
+// waves of a workgroup reach this point at different times (their loads return unevenly), and the barrier pair
+// would hold the early ones; a segment's few remaining rounds would mostly pass before the threshold arrived, so
+// segments keep the barrier form.
+__device__ __forceinline__ void pilot_async(int w, WaveCands& wc, int k) {
+  const int lane = threadIdx.x & 63;
+  if (wc.cnt > SV_MAX_K) compact(w, wc, k, SV_MAX_K);
+  int off = 0;
+  if (lane == 0)
+    off = __hip_atomic_fetch_add(&g_sup.pool_n, wc.cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  off = __builtin_amdgcn_readfirstlane(off);
+  for (int j = lane; j < wc.cnt; j += 64) g_sup.uni[off + j] = g_sup.buf[w * kWaveCap + j];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");      // the copies land before the wave counts itself in
+  int last = 0;
+  if (lane == 0)
+    last = __hip_atomic_fetch_add(&g_sup.pool_in, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == kSupWaves - 1;
+  if (!__builtin_amdgcn_readfirstlane(last)) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  const int n = __builtin_amdgcn_readfirstlane(
+      __hip_atomic_load(&g_sup.pool_n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+  if (n <= k) return;
+  // the wave's own histogram: other waves may be compacting with theirs meanwhile
+  const uint64_t t = uint64_t(uniform_i64(int64_t(wave_select(g_sup.uni, n, k, g_sup.hist[w]))));
+  if (t > wc.theta) {
+    set_theta(wc, t);
+    if (lane == 0) lds_store_u64(&g_sup.theta[w], t);
+  }
+}
+
 __device__ __forceinline__ void pilot(int w, WaveCands& wc, int k) {
   const int lane = threadIdx.x & 63;
   if (wc.cnt > SV_MAX_K) compact(w, wc, k, SV_MAX_K);
@@ -638,6 +671,10 @@ __device__ __forceinline__ void support_item(const SupportParams& p, int64_t row
   const int64_t V = p.V;
 
   if (lane == 0) lds_store_u64(&g_sup.theta[w], 0ull);
+  if (tid == 0) {
+    g_sup.pool_n = 0;
+    g_sup.pool_in = 0;
+  }
   WaveCands wc;
   set_theta(wc, 0ull);
   wc.cnt = 0;
@@ -706,7 +743,10 @@ __device__ __forceinline__ void support_item(const SupportParams& p, int64_t row
     load_round(ga, r + 2 < nround ? r + 2 : r + 1);  // the next pair's first round, or the first round left over
     __builtin_amdgcn_sched_barrier(0);
     take_round<T, SUM, false>(w, wc, st, nan, k, p.c, gb, id_v + uint32_t(r + 1) * kIdStep, nullptr);
-    if (r == 0 && npair > 1) pilot(w, wc, k);
+    if (r == 0 && npair > 1) {
+      if (nseg == 1) pilot_async(w, wc, k);
+      else pilot(w, wc, k);
+    }
   }
   // at most two rounds left (a full one and the partial one); the first is already in ga
   for (int64_t r = 2 * npair; r < nround; ++r) {
