@@ -343,7 +343,7 @@ int sv_verify_tree(const void* target_logits, int64_t t_seq, int64_t t_row, int 
   for (const void* p : ptrs)
     if (p && !aligned(p, 4)) return SV_ERR_ALIGN;
   const sv::TreePlan plan = sv::make_tree_plan(B, N, V, dtype, sv::tree_resident_workgroups(dtype));
-  if (double(plan.items) + double(B) * double(plan.ntask) > double(kMaxI32)) return SV_ERR_SHAPE;
+  if (double(plan.items) + double(plan.tasks) > double(kMaxI32)) return SV_ERR_SHAPE;
   const int st = check_workspace(workspace, workspace_bytes, plan.total);
   if (st != SV_OK) return st;
   sv::TreeArgs a{target_logits, t_seq, t_row, dtype, parent, token, u_accept, u_sample, temperature, accept,

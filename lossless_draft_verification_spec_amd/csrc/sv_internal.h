@@ -168,8 +168,12 @@ struct TreePlan {
   int32_t nseg = 1;         // pieces of every later row (1: those rows are whole too)
   int64_t items = 0;        // row items (workgroups before the draw tasks in the launch)
   int64_t nch = 0;          // 512-element chunks per row in the draw
-  int32_t ntask = 1;        // draw tasks per sequence
+  int32_t ntask = 1;        // draw tasks per sequence (all but the last tailq sequences)
   int32_t task_chunks = 16; // chunks per draw task
+  int32_t tailq = 0;        // the last sequences, whose rows finish last: smaller draw tasks
+  int32_t ntask2 = 1;       // draw tasks of each of them
+  int32_t task_chunks2 = 8; // chunks per such task
+  int64_t tasks = 0;        // draw tasks of the launch
   size_t off_ctr1 = 0;      // int32 per sequence: rows finished, N + 1 once the walk published the job; back to 0
                             // after the pick
   size_t off_ctr2 = 0;      // int32 per sequence: draw tasks finished, back to 0 after the pick
@@ -193,6 +197,35 @@ __host__ __device__ inline void tree_item(int64_t item, int64_t head_rows, int32
     *r = head_rows + j / nseg;
     *seg = int32_t(j % nseg);
   }
+}
+
+// Draw task j of the tree launch: sequence b, its task t of nt, chunks [c0, c1). The first B - tailq sequences have
+// ntask tasks of task_chunks chunks, the last tailq have ntask2 of task_chunks2, in sequence order.
+struct TreeTask {
+  int64_t b;
+  int32_t t, nt;
+  int64_t c0, c1;
+};
+__host__ __device__ inline TreeTask tree_task(int64_t j, int64_t B, int32_t tailq, int32_t ntask, int32_t ntask2,
+                                              int32_t task_chunks, int32_t task_chunks2, int64_t nch) {
+  const int64_t head = (B - tailq) * int64_t(ntask);
+  TreeTask k;
+  int64_t per;
+  if (j < head) {
+    k.b = j / ntask;
+    k.t = int32_t(j % ntask);
+    k.nt = ntask;
+    per = task_chunks;
+  } else {
+    const int64_t j2 = j - head;
+    k.b = B - tailq + j2 / ntask2;
+    k.t = int32_t(j2 % ntask2);
+    k.nt = ntask2;
+    per = task_chunks2;
+  }
+  k.c0 = int64_t(k.t) * per;
+  k.c1 = k.c0 + per < nch ? k.c0 + per : nch;
+  return k;
 }
 
 // resident: workgroups of the tree launch resident on the device at once (it sets which rows are cut into pieces;

@@ -49,6 +49,8 @@ constexpr int kTWaves = kTBlock / 64;
 constexpr int kTU = 4;                 // 16-byte vectors per thread per group of the row stream
 constexpr int kHits = 8;               // masked elements one thread keeps in its list (more: the exact slow path)
 constexpr int kTChunk = 512;           // elements per chunk of the draw (8 per lane of a wave)
+constexpr int64_t kTTailChunks = 8;    // chunks per draw task of the sequences that walk last
+constexpr int64_t kTTailPerSlot = 3;   // their chunks in all, per resident workgroup
 constexpr int kTPer = kTChunk / 64;
 constexpr int kTMaxSeg = 64;           // pieces of one row at most (one lane each in the merge)
 constexpr int64_t kTMinSegVec = 512;   // 16-byte vectors of one piece at least (2 per thread)
@@ -72,8 +74,9 @@ struct TreeParams {
   TreeJob* jobs;                       // per b: where the walk stopped
   double* chunk;                       // per (b, chunk): float64 weight of the chunk of the stop row
   int64_t nch;                         // chunks per row
-  int32_t ntask;                       // draw tasks per sequence
+  int32_t ntask;                       // draw tasks per sequence (all but the last tailq)
   int32_t task_chunks;                 // chunks per draw task
+  int32_t tailq, ntask2, task_chunks2; // the last sequences' smaller tasks
   int64_t row_items;                   // workgroups of the row pass (the draw tasks follow them)
 };
 
@@ -764,8 +767,8 @@ template <typename T>
 __device__ void tree_draw_item(const TreeParams& p, int64_t j) {
   TreeShared& sh = g_tree;
   const int tid = threadIdx.x, wave = tid >> 6;
-  const int64_t b = j / p.ntask;
-  const int task = int(j % p.ntask);
+  const TreeTask tk = tree_task(j, p.B, p.tailq, p.ntask, p.ntask2, p.task_chunks, p.task_chunks2, p.nch);
+  const int64_t b = tk.b;
   const int N = p.N;
   const bool seen = ws_seen_clean(p.ws, p.sig);
   for (int i = tid; i < N; i += kTBlock) {
@@ -811,7 +814,7 @@ __device__ void tree_draw_item(const TreeParams& p, int64_t j) {
   const bool vec = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
   const double c2 = p.c2, nm = -(double(job.m) * c2);
   if (live) {
-    const int64_t c0 = int64_t(task) * p.task_chunks, c1 = std::min<int64_t>(c0 + p.task_chunks, p.nch);
+    const int64_t c0 = tk.c0, c1 = tk.c1;
     // the wave's chunks c0 + wave + 4k, kTBatch of them in flight at a time
     constexpr int kTBatch = 4;
     for (int64_t cb = c0 + wave; cb < c1; cb += int64_t(kTBatch) * kTWaves) {
@@ -837,7 +840,7 @@ __device__ void tree_draw_item(const TreeParams& p, int64_t j) {
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tid == 0) sh.flag = ctr_add(p.ctr2 + b) == p.ntask - 1;
+  if (tid == 0) sh.flag = ctr_add(p.ctr2 + b) == tk.nt - 1;
   __syncthreads();
   if (!sh.flag) return;
   // the last task of the sequence: the pick (wave 0), and the sequence's outputs that the walk left to it (one writer
@@ -904,6 +907,14 @@ TreePlan make_tree_plan(int64_t B, int32_t N, int64_t V, int dtype, int64_t resi
   int64_t tc = std::max<int64_t>(4, (pl.nch + want - 1) / want);
   pl.task_chunks = int32_t(std::min<int64_t>(tc, std::max<int64_t>(pl.nch, 1)));
   pl.ntask = int32_t((pl.nch + pl.task_chunks - 1) / pl.task_chunks);
+  // the sequences whose rows finish last (the walks come last) take tasks of kTTailChunks chunks: about
+  // kTTailPerSlot chunks per resident workgroup in all, so the end of the launch is many short tasks
+  pl.task_chunks2 = int32_t(std::min<int64_t>(kTTailChunks, std::max<int64_t>(pl.nch, 1)));
+  pl.ntask2 = int32_t((pl.nch + pl.task_chunks2 - 1) / pl.task_chunks2);
+  pl.tailq = pl.ntask2 > pl.ntask
+      ? int32_t(std::min<int64_t>(B, (kTTailPerSlot * W + pl.nch - 1) / std::max<int64_t>(pl.nch, 1)))
+      : 0;
+  pl.tasks = (B - pl.tailq) * int64_t(pl.ntask) + int64_t(pl.tailq) * pl.ntask2;
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t ncut = size_t(std::min<int64_t>(R, kTPieceCap / 2));      // cut rows at most (2 pieces or more each)
   const size_t npiece = size_t(std::min<int64_t>(R * kTMaxSeg, kTPieceCap));
@@ -961,8 +972,9 @@ hipError_t launch_tree(const TreePlan& plan, const TreeArgs& a, hipStream_t stre
   p.jobs = reinterpret_cast<TreeJob*>(a.ws + plan.off_jobs);
   p.chunk = reinterpret_cast<double*>(a.ws + plan.off_chunk);
   p.nch = plan.nch; p.ntask = plan.ntask; p.task_chunks = plan.task_chunks;
+  p.tailq = plan.tailq; p.ntask2 = plan.ntask2; p.task_chunks2 = plan.task_chunks2;
   p.row_items = plan.items;
-  const unsigned grid = unsigned(plan.items + plan.B * plan.ntask);
+  const unsigned grid = unsigned(plan.items + plan.tasks);
   if (a.dtype == SV_BF16)
     hipLaunchKernelGGL(k_tree<uint16_t>, dim3(grid), dim3(kTBlock), 0, stream, p);
   else

@@ -154,6 +154,30 @@ static void check_tree_plans() {
               }
             }
             for (int64_t r = 0; r < R; ++r) CHECK(seen[size_t(r)] == (r < pl.head_rows ? 1 : pl.nseg));
+            // draw tasks: every chunk of every sequence's row in exactly one task, the tasks of a sequence in order
+            CHECK(pl.tailq >= 0 && pl.tailq <= B && pl.ntask >= 1 && pl.ntask2 >= 1);
+            CHECK(pl.tasks == (B - pl.tailq) * int64_t(pl.ntask) + int64_t(pl.tailq) * pl.ntask2);
+            if (pl.tasks <= 2000000) {
+              int64_t prev_b = -1, next_c = 0;
+              int32_t next_t = 0;
+              for (int64_t j = 0; j < pl.tasks; ++j) {
+                const sv::TreeTask k = sv::tree_task(j, B, pl.tailq, pl.ntask, pl.ntask2, pl.task_chunks,
+                                                     pl.task_chunks2, pl.nch);
+                if (k.b != prev_b) {
+                  if (prev_b >= 0) CHECK(next_c == pl.nch);
+                  CHECK(k.b == prev_b + 1);
+                  prev_b = k.b;
+                  next_c = 0;
+                  next_t = 0;
+                }
+                CHECK(k.t == next_t && k.t < k.nt);
+                CHECK(k.nt == (k.b < B - pl.tailq ? pl.ntask : pl.ntask2));
+                CHECK(k.c0 == next_c && k.c1 > k.c0 && k.c1 <= pl.nch);
+                next_c = k.c1;
+                ++next_t;
+              }
+              CHECK(prev_b == B - 1 && next_c == pl.nch);
+            }
           }
       }
   CHECK(cut_plans > 100);
