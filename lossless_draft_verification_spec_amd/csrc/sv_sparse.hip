@@ -10,13 +10,12 @@
 // One workgroup of 8 waves per sequence (four fit a compute unit for supports of up to 64 entries, so that a thousand
 // sequences run in one round); the slots go in batches whose correction weights fit the LDS table (one batch for the
 // usual sizes, e.g. 16 slots of 64-entry supports).
-//  1. a wave per slot (slots wave, wave + 8, ...; the next slot's rows requested before this one's are used), the
-//     slot's supports in its lanes (entry e in lane e % 64, register e / 64): the rows are checked; p_spec and q_spec
-//     come from a ballot of the entries whose id is the drafted one; the accept test; then each p entry's q
-//     probability, every lane comparing its p ids with one q entry at a time (read across lanes from the lane that
-//     holds it), and the weights max(p - q_on_p, 0) into the LDS table with their ids (p's probabilities when no
-//     weight is positive). With one batch, the checks of every row end before any output is written; with several,
-//     all rows are checked in a pass before.
+//  1. a wave per slot (slots wave, wave + 8, ...), the slot's supports in its lanes (entry e in lane e % 64,
+//     register e / 64): the rows are checked; p_spec and q_spec come from a ballot of the entries whose id is the
+//     drafted one; the accept test; then each p entry's q probability through the wave's bucket index of q (see
+//     slot_weights), and the weights max(p - q_on_p, 0) into the LDS table with their ids (p's probabilities when no
+//     weight is positive). With one batch, the checks of every row end before any output is written; with several, all
+//     rows are checked in a pass before.
 //  2. one thread per slot sums its weights in slot order (and keeps the running sums of the slot to be drawn from);
 //     the outputs and the normalised correction distribution are written by all threads.
 //  3. the draw, by one wave: a ballot over the stored running sums finds the first that exceeds t.
@@ -174,13 +173,13 @@ __device__ __forceinline__ void q_entry(const Row<kEnt>& Q, int e, int32_t& id, 
 }
 
 // The correction weights max(p_e - q_on_p_e, 0) of one slot (by one wave) into w, and the p ids into ids. Each p
-// entry's q probability is found through the wave's index of q (qb, an entry number per bucket of the id's hash): every q
-// entry writes its index at its bucket, and an entry that reads back another's has lost the bucket; each p entry
+// entry's q probability is found through the wave's index of q (qb, an entry number per bucket of the id's hash): every
+// q entry writes its index at its bucket, and an entry that reads back another's has lost the bucket; each p entry
 // reads its bucket and checks the id of the q entry named there (so the index needs no clearing: a stale or
-// uninitialised word names an entry whose id does not match, or one that does and is a true match); the q entries
-// that lost their bucket (a few) are then compared with every p entry one at a time. When q repeats an id, every
-// q_on_p is summed again in float64 in q's slot order instead, each q entry read across lanes. With no positive
-// weight (no leftover mass) the weights become p's probabilities and the result is true (the same for every lane).
+// uninitialised word names an entry whose id does not match, or one that does and is a true match); the q entries that
+// lost their bucket (a few) are then compared with every p entry one at a time. When q repeats an id, every q_on_p is
+// summed again in float64 in q's slot order instead, each q entry read across lanes. With no positive weight (no
+// leftover mass) the weights become p's probabilities and the result is true (the same for every lane).
 template <int kEnt>
 __device__ __forceinline__ bool slot_weights(const Row<kEnt>& P, const Row<kEnt>& Q, int kp, int kq, int32_t* qb,
                                              double* w, int32_t* ids) {
@@ -274,7 +273,8 @@ __device__ __forceinline__ bool slot_weights(const Row<kEnt>& P, const Row<kEnt>
 template <int kEnt> constexpr int kSparseWpe = kEnt == 1 ? 8 : 1;
 
 template <int kEnt>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kSparseWpe<kEnt>))) void k_sparse(SparseArgs kargs) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kSparseWpe<kEnt>)))
+void k_sparse(SparseArgs kargs) {
   (void)kargs;
   // the arguments are read in place from the argument segment, each when it is used, instead of being held in
   // scalar registers for the whole kernel
@@ -332,24 +332,12 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kSparseW
   for (int j0 = 0; j0 < G; j0 += nb) {
     const int j1 = min(j0 + nb, G);
     // 1. a wave per slot: accept test and, when needed, the correction weights
-    // the next slot's rows and scalars are requested before this slot's are used (one load round per wave when
-    // every wave has at most two slots)
-    Row<kEnt> Pn, Qn;
-    int32_t xn = 0;
-    float un = 0.f, udn = 0.f;
-    auto fetch = [&](int j) {
-      Pn = load_row<kEnt>(P_ids + int64_t(j) * kp, P_pr + int64_t(j) * kp, kp, lane);
-      Qn = load_row<kEnt>(Q_ids + int64_t(j) * kq, Q_pr + int64_t(j) * kq, kq, lane);
-      xn = a.spec[b * G + j];
-      un = a.ua[b * G + j];
-      udn = a.us[b * (G + 1) + j];
-    };
-    if (j0 + wv < j1) fetch(j0 + wv);
     for (int j = j0 + wv; j < j1; j += kWaves) {
-      const Row<kEnt> P = Pn, Q = Qn;
-      const int32_t x = xn;
-      const float u = un, uds = udn;
-      if (j + kWaves < j1) fetch(j + kWaves);
+      const Row<kEnt> P = load_row<kEnt>(P_ids + int64_t(j) * kp, P_pr + int64_t(j) * kp, kp, lane);
+      const Row<kEnt> Q = load_row<kEnt>(Q_ids + int64_t(j) * kq, Q_pr + int64_t(j) * kq, kq, lane);
+      const int32_t x = a.spec[b * G + j];
+      const float u = a.ua[b * G + j];
+      const float uds = a.us[b * (G + 1) + j];
       if (single) {
         check_row(P, kp, a.vocab, bad_nf, bad_id);
         check_row(Q, kq, a.vocab, bad_nf, bad_id);
