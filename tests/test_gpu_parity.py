@@ -190,6 +190,53 @@ def test_dense_rows_longer_than_one_pick_tile():
     assert g["n_accepted"][0] == G and (g["n_accepted"][1:] < G).any()
 
 
+def _side_by_side(*cases):
+    """Cases of one shape and dtype as one batch (sequence order kept)."""
+    out = dict(cases[0])
+    for key in ("target", "draft", "draft_ids", "u_accept", "u_sample"):
+        if out.get(key) is not None:
+            out[key] = np.concatenate([c[key] for c in cases])
+    out["B"] = sum(c["B"] for c in cases)
+    return out
+
+
+@pytest.mark.parametrize("dt,V", [("f32", 257), ("bf16", 1_031)])
+def test_dense_at_the_largest_gamma(dt, V):
+    """gamma = SV_MAX_GAMMA = 1024: 2048 statistics items per sequence and a scan over 1024 slots. Sequence 0's draft
+    is the target up to a tiny perturbation (a long run of acceptances), sequence 1's differs (an early rejection);
+    then the same batch along random orders from starts 0 and 700 (a 1024-slot permutation check)."""
+    from lossless_draft_verification_spec_amd import sv
+    G = sv.SV_MAX_GAMMA
+    case = _side_by_side(W.dense_case(1, G, V, dtype=dt, sigma_t=1.0, sigma_d=1e-3, seed=71),
+                         W.dense_case(1, G, V, dtype=dt, sigma_t=1.0, sigma_d=1.0, seed=72))
+    g, o = check_dense(case, f"dense gamma={G} {dt}")
+    log(f"  n_accepted {g['n_accepted'].tolist()}")
+    assert o["n_accepted"][0] > 200 and o["n_accepted"][1] < 50
+    rng = np.random.default_rng(73)
+    order = np.stack([rng.permutation(G) for _ in range(2)]).astype(np.int32)
+    g, o = check_dense(case, f"dense gamma={G} {dt} ordered", start=np.array([0, 700], np.int32), order=order)
+    log(f"  n_accepted {g['n_accepted'].tolist()}, starts out {g['start_out'].tolist()}")
+
+
+def test_onehot_at_the_largest_gamma():
+    """One-hot drafts at gamma = 1024 whose drafted ids carry nearly all of the target's mass: sequence 0 accepts
+    every slot and draws the bonus after 1024 rows; sequence 1 has one ordinary slot (600) with a uniform near 1, so
+    it rejects there and draws from that row's residual."""
+    from lossless_draft_verification_spec_amd import sv
+    G = sv.SV_MAX_GAMMA
+    case = W.onehot_case(2, G, 513, dtype="f32", temperature=0.7, seed=74)
+    spike = np.ones((2, G), bool)
+    spike[1, 600] = False
+    b, j = np.nonzero(spike)
+    case["target"][b, j, case["draft_ids"][b, j]] += np.float32(30.0)
+    case["u_accept"][1, 600] = np.float32(0.99999)
+    g = run_onehot(case)
+    o = oracle_dense(case, onehot=True)
+    log(f"onehot gamma={G}: {compare_decisions(g, o, f'onehot gamma={G}')}, n {g['n_accepted'].tolist()}")
+    compare_probs(g, o, "p_draft", "f32")
+    assert o["n_accepted"].tolist() == [G, 600]
+
+
 def test_dense_is_deterministic():
     case = W.dense_case(4, 6, 40_000, dtype="bf16", seed=15)
     a, b = run_dense(case), run_dense(case)
@@ -289,6 +336,24 @@ def test_sparse_shapes_bit_exact(shape):
     o = oracle.verify_sparse(case["p_ids"], case["p_probs"], case["q_ids"], case["q_probs"], case["spec_ids"],
                              case["u_accept"], case["u_sample"], bonus=1, vocab_size=V)
     check_sparse_exact(g, o, f"sparse {shape}")
+
+
+@pytest.mark.parametrize("k", [16, 256])
+def test_sparse_at_the_largest_gamma(k):
+    """gamma = SV_MAX_GAMMA = 1024 slots (several batches of correction weights in LDS). Sequence 0's draft support is
+    its target support (q = p at every slot: every draft is accepted and the bonus is drawn after 1024 slots);
+    sequence 1 is random (an early rejection)."""
+    from lossless_draft_verification_spec_amd import sv
+    G, V = sv.SV_MAX_GAMMA, 50_000
+    case = W.sparse_case(2, G, k, V, shared=max(1, k // 2), seed=75)
+    case["q_ids"][0] = case["p_ids"][0, :G]
+    case["q_probs"][0] = case["p_probs"][0, :G]
+    case["spec_ids"][0] = case["q_ids"][0, :, 0]
+    g = run_sparse(case, vocab_size=V)
+    o = oracle.verify_sparse(case["p_ids"], case["p_probs"], case["q_ids"], case["q_probs"], case["spec_ids"],
+                             case["u_accept"], case["u_sample"], bonus=1, vocab_size=V)
+    check_sparse_exact(g, o, f"sparse gamma={G} k={k}")
+    assert o["n_accepted"][0] == G and o["n_accepted"][1] < G
 
 
 def test_sparse_faults_and_fallback():

@@ -123,6 +123,35 @@ def test_tree_sizes_at_the_walk_boundary(N):
     assert r["tests"] > 4 * (N - 1) // 2                      # most siblings were tested
 
 
+@pytest.mark.parametrize("shape", ["chain", "random", "star"])
+def test_tree_at_the_largest_size(shape):
+    """Trees of SV_MAX_TREE_NODES = 1024 nodes: a single chain (the walk descends up to 1023 levels), a random
+    recursive tree, and a root with 1023 children (1023 masked tokens in the root's row, siblings tested in chunks of
+    64 with first-holder checks across chunks)."""
+    from lossless_draft_verification_spec_amd import sv
+    N = sv.SV_MAX_TREE_NODES
+    case = W.tree_case(2, N, 3_000, dtype="bf16", seed=311)
+    if shape == "chain":
+        case["parent"] = W.random_tree_parents(np.random.default_rng(312), 2, N, p_chain=1.0)
+        case["u_accept"][0] = np.float32(0.0)                  # every test passes: down to the leaf
+    elif shape == "random":
+        case["parent"] = W.random_tree_parents(np.random.default_rng(313), 2, N, p_chain=0.0)
+    else:
+        case["parent"][:] = 0
+        case["parent"][:, 0] = -1
+    case = _retoken(case)
+    if shape == "star":
+        case["token"][:, 1:] = case["token"][:, 1:][:, ::-1]   # the root's top candidate on its last child
+        case["u_accept"][:] = np.float32(0.97)
+    o = run_oracle(case)
+    r = compare_tree(run_tree(case), o, "bf16", f"N={N} {shape}")
+    print(f"tree N={N} {shape}: {r}", flush=True)
+    if shape == "chain":
+        assert o["n_accepted"][0] == N - 1
+    if shape == "star":
+        assert r["tests"] == 2 * (N - 1)
+
+
 def _retoken(case):
     """Children tokens for a new parent array: the top candidates of each node's row, in decreasing order."""
     z = oracle.widen(case["target"], case["dtype"])
