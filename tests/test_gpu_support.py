@@ -99,6 +99,19 @@ def test_segmented_rows_merge(dtype, renorm):
     check(g, o, renorm)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("k", [50, 256])
+def test_long_rows_many_segments(dtype, k):
+    """Three rows of V = 1,000,003: each row is cut into the most segments the merge area allows (16 at k = 50, 12
+    at k = 256), the vocabulary's odd length leaves a ragged tail on the last segment, and the merge ranks up to
+    12 x 256 keys."""
+    z = zipf_rows(7 + k, 3, 1_000_003, dtype=dtype)
+    for renorm in (True, False):
+        g = run_support(z, dtype, k, 0.95, 1.0, renorm)
+        o = oracle.build_support(z, dtype, k, 0.95, 1.0, renorm=renorm)
+        check(g, o, renorm)
+
+
 @pytest.mark.parametrize("k", [1, 50, 256])
 def test_ties_and_degenerate_rows(k):
     V = 70001
