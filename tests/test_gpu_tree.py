@@ -123,6 +123,15 @@ def test_tree_sizes_at_the_walk_boundary(N):
     assert r["tests"] > 4 * (N - 1) // 2                      # most siblings were tested
 
 
+@pytest.mark.parametrize("B,N,dt", [(2, 9, "bf16"), (2, 5, "f32")])
+def test_tree_rows_cut_into_many_pieces(B, N, dt):
+    """A few rows of V = 600,001: the launch cuts every row into as many pieces as fill a resident round (56 pieces
+    of the 18 bf16 rows, the most the merge takes, 64, of the 10 float32 rows), merged one lane per piece."""
+    case = W.tree_case(B, N, 600_001, dtype=dt, seed=321 + N)
+    r = compare_tree(run_tree(case), run_oracle(case), dt, f"pieces B={B} N={N} {dt}")
+    print(f"tree pieces B={B} N={N} {dt}: {r}", flush=True)
+
+
 @pytest.mark.parametrize("shape", ["chain", "random", "star"])
 def test_tree_at_the_largest_size(shape):
     """Trees of SV_MAX_TREE_NODES = 1024 nodes: a single chain (the walk descends up to 1023 levels), a random
