@@ -160,6 +160,28 @@ def test_dense_data_faults():
     assert g["flags"][7] & oracle.FLAG_ID_RANGE
 
 
+def test_dense_faults_inside_later_segments():
+    """Rows of 600,001 float32 logits are read as three statistics segments: a NaN in the last segment of a target
+    row and a +inf in the middle segment of a draft row make their sequences non-finite once the segments' partials
+    are merged; a draft row that is -inf past its first 1000 elements has q = 0 at its drafted id (Q_ZERO, the
+    draft rejected) while its finite head still normalises the row."""
+    B, G, V = 4, 2, 600_001
+    case = W.dense_case(B, G, V, dtype="f32", seed=18)
+    zt, zd = case["target"], case["draft"]
+    zt[0, 1, V - 5] = np.nan
+    zd[1, 0, V // 2] = np.inf
+    zd[2, 1, 1000:] = -np.inf
+    g = run_dense(case)
+    o = oracle_dense(case)
+    s = compare_decisions(g, o, "faults in later segments")
+    compare_probs(g, o, "p_draft", "f32", "faults in later segments")
+    assert g["flags"][0] & oracle.FLAG_NONFINITE and g["n_accepted"][0] == -1
+    assert g["flags"][1] & oracle.FLAG_NONFINITE and g["n_accepted"][1] == -1
+    assert g["flags"][2] & oracle.FLAG_Q_ZERO and g["n_accepted"][2] == o["n_accepted"][2]
+    assert g["flags"][3] == o["flags"][3]
+    log(f"faults in later segments: {s}, flags {g['flags'].tolist()}, n {g['n_accepted'].tolist()}")
+
+
 @pytest.mark.parametrize("V", [30_000, 600_001])
 def test_dense_near_equal_distributions(V):
     """Draft = target + tiny noise: the residual's sign is undecided for most elements, so the pick recomputes most
