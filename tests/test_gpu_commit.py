@@ -139,6 +139,21 @@ def test_faults_and_ties():
         np.testing.assert_array_equal(g["token"], o["token"])
 
 
+def test_faults_inside_later_segments():
+    """Rows of 600,001 float32 logits read in segments: a NaN in the last segment of a masked slot and a +inf in the
+    middle of another masked slot void their blocks; a +inf in an unmasked slot is never read."""
+    print("commit faults in segments", flush=True)
+    c = W.commit_case(3, 3, 600_001, dtype="f32", seed=332)
+    z, m = c["logits"], c["masked"]                  # masked: [[1, 1, 1], [1, 0, 1], [1, 0, 1]]
+    z[0, 2, 600_001 - 3] = np.nan
+    z[1, 1, 300_000] = np.inf
+    z[2, 0, 300_000] = np.inf
+    o = with_argmax(oracle.confidence_commit(z, "f32", 0.8, m), z, "f32")
+    g = run_commit(z, "f32", 0.8, m)
+    check(g, o, 0.8, "faults in segments")
+    assert g["n_commit"].tolist()[0] == -1 and g["n_commit"].tolist()[2] == -1 and g["n_commit"].tolist()[1] >= 1
+
+
 def test_block_workload_and_shared_workspace():
     """B = 256 blocks of W = 4 masked slots over V = 151936 (bf16), the benchmark's configuration, on a workspace
     that a greedy verification uses in between."""

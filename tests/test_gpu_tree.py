@@ -132,6 +132,20 @@ def test_tree_rows_cut_into_many_pieces(B, N, dt):
     print(f"tree pieces B={B} N={N} {dt}: {r}", flush=True)
 
 
+def test_tree_faults_inside_pieces():
+    """Rows of 600,001 float32 logits cut into pieces: a NaN in the root row's last piece and a +inf in a middle
+    piece of a row on the walk's path make those sequences non-finite once the pieces are merged; the third tree
+    is clean."""
+    case = W.tree_case(3, 5, 600_001, dtype="f32", seed=331)
+    case["target"][0, 0, 600_001 - 3] = np.nan
+    case["target"][1, 1, 300_000] = np.inf
+    g, o = run_tree(case), run_oracle(case)
+    r = compare_tree(g, o, "f32", "faults inside pieces")
+    assert (g["flags"][:2] & oracle.FLAG_NONFINITE).all() and (g["n_accepted"][:2] == -1).all()
+    assert g["flags"][2] == o["flags"][2] == 0
+    print(f"tree faults inside pieces: {r}, flags {g['flags'].tolist()}", flush=True)
+
+
 @pytest.mark.parametrize("shape", ["chain", "random", "star"])
 def test_tree_at_the_largest_size(shape):
     """Trees of SV_MAX_TREE_NODES = 1024 nodes: a single chain (the walk descends up to 1023 levels), a random
