@@ -152,6 +152,23 @@ def test_faults_and_bad_arguments():
     assert (o2["flags"] == oracle.FLAG_NONFINITE).all() and (o2["n_accepted"] == G).all()
 
 
+def test_faults_inside_later_segments():
+    """Rows of 600,001 float32 logits read as many segments: a NaN in the last segment of a verified row and a +inf
+    in a middle segment of another are fatal for their sequences once the segments' keys are merged; a row with
+    nothing above -inf but its first segment's range stays valid."""
+    print("greedy faults in segments", flush=True)
+    B, G, V = 4, 2, 600_001
+    c = W.greedy_case(B, G, V, dtype="f32", sigma_t=2.0, zipf=0.0, agree=1.0, seed=7)
+    z, ids = c["target"].copy(), c["draft_ids"].copy()
+    z[0, 1, V - 3] = np.nan
+    z[1, 0, V // 2] = np.inf
+    z[2, 1, 1000:] = -np.inf
+    o = oracle.verify_greedy(z, ids, dtype="f32")
+    g = run_greedy(z, "f32", ids)
+    check(g, o)
+    assert o["flags"][0] == o["flags"][1] == oracle.FLAG_NONFINITE and o["flags"][2] == 0
+
+
 def test_long_blocks():
     """gamma = SV_MAX_GAMMA = 1024: the merge walks 1025 rows and a 1024-bit permutation check."""
     print("greedy long blocks", flush=True)
