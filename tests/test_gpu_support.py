@@ -112,6 +112,23 @@ def test_long_rows_many_segments(dtype, k):
         check(g, o, renorm)
 
 
+def test_faults_inside_later_segments():
+    """Rows of 600,001 logits cut into segments: a NaN in the last segment and a +inf in a middle one are reported
+    for their rows once the segments are merged; a row -inf past its first 1000 elements keeps its head's support."""
+    z = zipf_rows(11, 4, 600_001)
+    z[0, 600_001 - 3] = np.nan
+    z[1, 300_000] = np.inf
+    z[2, 1000:] = -np.inf
+    for dtype in ("f32", "bf16"):
+        zz = W.f32_to_bf16_bits(z) if dtype == "bf16" else z
+        for renorm in (True, False):
+            g = run_support(zz, dtype, 50, 0.95, 1.0, renorm)
+            o = oracle.build_support(zz, dtype, 50, 0.95, 1.0, renorm=renorm)
+            check(g, o, renorm)
+            assert (g["flags"][:2] == o["flags"][:2]).all() and (o["flags"][:2] != 0).all()
+            assert g["flags"][2] == 0 and g["flags"][3] == 0
+
+
 @pytest.mark.parametrize("k", [1, 50, 256])
 def test_ties_and_degenerate_rows(k):
     V = 70001
