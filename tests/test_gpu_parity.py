@@ -391,6 +391,30 @@ def test_sparse_faults_and_fallback():
     check_sparse_exact(g, o, "sparse faults")
 
 
+def test_sparse_faults_across_batches():
+    """gamma = 1024 slots in batches of correction weights (96 slots a batch at k = 16): a NaN probability and an
+    out-of-vocabulary id in late batches, q = 0 at every drafted id, a bad bonus row after 1024 accepted slots, and an
+    empty residual at slot 800 after 800 accepted ones; the kernel checks the rows batch by batch here, not all at
+    once."""
+    from lossless_draft_verification_spec_amd import sv
+    G, k, V = sv.SV_MAX_GAMMA, 16, 5000
+    case = W.sparse_case(6, G, k, V, seed=33)
+    pi, pp, qi, qp, sp, ua = (case[x] for x in ("p_ids", "p_probs", "q_ids", "q_probs", "spec_ids", "u_accept"))
+    pp[0, 900, 3] = np.nan
+    qi[1, 700, 0] = V
+    qp[2] = 0.0
+    for b in (3, 4):                                   # q = p: every draft accepted
+        qi[b], qp[b] = pi[b, :G], pp[b, :G]
+        sp[b] = qi[b, :, 0]
+    pp[3, G, 5] = np.nan                               # the bonus row
+    qp[4, 800] = 2.0 * pp[4, 800]                      # q dominates p at slot 800, which then rejects
+    ua[4, 800] = np.float32(0.9)
+    g = run_sparse(case, vocab_size=V)
+    o = oracle.verify_sparse(pi, pp, qi, qp, sp, ua, case["u_sample"], bonus=1, vocab_size=V)
+    check_sparse_exact(g, o, "sparse faults across batches")
+    log(f"sparse faults across batches: flags {g['flags'].tolist()}, n {g['n_accepted'].tolist()}")
+
+
 def _one_bucket(n, bits, bucket, rng):
     """n distinct ids in [0, 2^24) that the kernel's index of q (2^bits buckets of a multiplicative hash) sends to
     one bucket, so that all but one of a support's entries lose it and take the kernel's slower matching."""
