@@ -1,7 +1,7 @@
-"""Calls captured in a HIP graph: the library records kernel launches only (no allocation, no memset, no host
-synchronisation), so a captured call replays correctly. Workspaces and outputs are allocated before the capture;
-every replay is checked against the eager result, with the program's own eager work and synchronisations between the
-replays."""
+"""Calls captured in a HIP graph, the no-allocation dense variant among them: the library records kernel launches only
+(no allocation, no memset, no host synchronisation), so a captured call replays correctly. Workspaces and outputs
+are allocated before the capture; every replay is checked against the eager result, with the program's own eager
+work and synchronisations between the replays."""
 import numpy as np
 import pytest
 import torch
@@ -35,15 +35,17 @@ def test_calls_replayed_from_a_captured_graph():
     ws_d = sv.workspace(sv.SV_KIND_DENSE, B, G, V, d)
     ws_s = sv.support_workspace(B * (G + 1) + B * G, V, 50, d)
     ws_t = sv.workspace(sv.SV_KIND_TREE, tc["B"], tc["N"], V, d)
-    o_d, o_a, o_b, o_s, o_t = {}, {}, {}, {}, {}
+    o_d, o_a, o_b, o_s, o_t, o_n = {}, {}, {}, {}, {}, {}
 
     def calls():
         sv.sv_verify_dense(tgt, dft, ids, ua, us, T, bonus=1, out=o_d, ws=ws_d)
         sv.sv_build_support_pair(tgt.view(-1, V), dft.view(-1, V), 50, 0.95, T, True, out_a=o_a, out_b=o_b, ws=ws_s)
         sv.sv_verify_sparse(*sp, bonus=1, vocab_size=sc["V"], out=o_s)
         sv.sv_verify_tree(tt, tp, tk, tua, tus, tc["temperature"], out=o_t, ws=ws_t)
+        # the no-allocation variant on the library's static scratch (calls in one graph run in order: no overlap)
+        sv.sv_verify_dense_noalloc(tgt, dft, ids, ua, us, T, bonus=1, out=o_n)
 
-    outs = (o_d, o_a, o_b, o_s, o_t)
+    outs = (o_d, o_a, o_b, o_s, o_t, o_n)
     calls()                                              # eager: allocates every output once
     torch.cuda.synchronize()
     want = [{k: v.cpu().numpy().copy() for k, v in o.items()} for o in outs]
