@@ -227,12 +227,13 @@ __device__ __forceinline__ uint32_t wave_code_floor(const uint64_t* a, int n, in
 }
 
 // The k-th largest of the n distinct keys a[0..n), n > k >= 1, by a most-significant-digit-first radix select with
-// 8-bit digits over a 256-bin histogram in LDS; the k largest keys are then moved to a[0..k), in no particular
-// order. One wave, all 64 lanes active, no barrier: the LDS executes one wave's operations in issue order. The keys
-// of a buffer lie close together and share their high bits, so the digits start at the highest bit where the
-// smallest and the largest key differ: the first histogram spreads over its bins instead of piling every key into
-// one (whose atomic adds would serialise).
-__device__ __forceinline__ uint64_t wave_select(uint64_t* a, int n, int k, uint32_t* hist) {
+// 8-bit digits over a 256-bin histogram in LDS; with `move`, the k largest keys are then moved to a[0..k), in no
+// particular order (the pilots, which only need the threshold, leave the keys where they are). One wave, all 64
+// lanes active, no barrier: the LDS executes one wave's operations in issue order. The keys of a buffer lie close
+// together and share their high bits, so the digits start at the highest bit where the smallest and the largest key
+// differ: the first histogram spreads over its bins instead of piling every key into one (whose atomic adds would
+// serialise).
+__device__ __forceinline__ uint64_t wave_select(uint64_t* a, int n, int k, uint32_t* hist, bool move = true) {
   const int lane = threadIdx.x & 63;
   uint64_t lo = ~0ull, hi_key = 0ull;
   for (int j = lane; j < n; j += 64) {
@@ -293,7 +294,7 @@ __device__ __forceinline__ uint64_t wave_select(uint64_t* a, int n, int k, uint3
     }
   }
   if (!found) theta = prefix;                       // only with repeated keys, which callers never pass
-  keep_from(a, n, theta);                          // exactly k keys
+  if (move) keep_from(a, n, theta);                // exactly k keys
   return theta;
 }
 
@@ -504,7 +505,7 @@ __device__ __forceinline__ void pilot_async(int w, WaveCands& wc, int k) {
       __hip_atomic_load(&g_sup.pool_n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
   if (n <= k) return;
   // the wave's own histogram: other waves may be compacting with theirs meanwhile
-  const uint64_t t = uint64_t(uniform_i64(int64_t(wave_select(g_sup.uni, n, k, g_sup.hist[w]))));
+  const uint64_t t = uint64_t(uniform_i64(int64_t(wave_select(g_sup.uni, n, k, g_sup.hist[w], false))));
   if (t > wc.theta) {
     set_theta(wc, t);
     if (lane == 0) lds_store_u64(&g_sup.theta[w], t);
@@ -526,7 +527,7 @@ __device__ __forceinline__ void pilot(int w, WaveCands& wc, int k) {
   for (int j = lane; j < wc.cnt; j += 64) g_sup.uni[off + j] = g_sup.buf[w * kWaveCap + j];
   __syncthreads();
   if (w == 0 && n > k) {
-    const uint64_t t = wave_select(g_sup.uni, n, k, g_sup.hist[0]);
+    const uint64_t t = wave_select(g_sup.uni, n, k, g_sup.hist[0], false);
     if (lane == 0) lds_store_u64(&g_sup.theta[0], t > wc.theta ? t : wc.theta);
   }
   __syncthreads();
